@@ -1,0 +1,386 @@
+"""Pins of the float64 oracle against facts fixed outside itself (no GPU needed).
+
+Each test checks the oracle against something it does not compute itself: a library decoder,
+exact rational arithmetic, a brute-force output-MSE evaluation, a closed-form identity, an
+invariance of the method, or hand-derived golden cases.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import lh_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+GRID_F = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+          Fraction(4), Fraction(6)]
+
+
+def rng(*k):
+    return np.random.default_rng(list(k))
+
+
+# ------------------------------------------------------------------ P1: the E4M3 candidate ladder
+def test_e4m3_ladder_matches_library_decoder():
+    torch = pytest.importorskip("torch")
+    allb = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    pos = [(b, v) for b, v in enumerate(allb) if np.isfinite(v) and v > 0]
+    assert len(pos) == 126                                  # "126 candidate scales"
+    assert [b for b, _ in pos] == list(range(1, 127))
+    lad = oracle.e4m3_ladder()
+    np.testing.assert_array_equal(lad, np.array([v for _, v in pos]))
+    assert lad[0] == 2.0 ** -9 and lad[-1] == 448.0        # 448-normalized NVFP4 scaling
+    assert np.all(np.diff(lad) > 0)
+
+
+def test_global_and_candidate_scales_are_fp32_roundings():
+    amax = np.float32(0.0871234)
+    g = oracle.global_scale(amax)
+    assert g == np.float64(np.float32(Fraction(float(amax)) / 2688))  # correctly rounded quotient
+    s = oracle.candidate_scales(g)
+    for k in (0, 7, 63, 125):
+        exact = Fraction(float(O.e4m3_ladder()[k])) * Fraction(float(g))
+        assert s[k] == float(np.float32(float(exact)))
+    # candidate 126 restores the block amax: 6 * s_126 ~= amax (448 * 6 = 2688)
+    assert abs(6 * s[-1] - float(amax)) <= 2 * 6 * np.spacing(np.float32(s[-1]))
+
+
+# ------------------------------------------------------------------ P2: E2M1 rounding
+def _exact_index(w: float, s: float) -> int:
+    if s == 0:
+        return 0
+    r = abs(Fraction(w)) / Fraction(s)
+    d = [abs(r - v) for v in GRID_F]
+    best = min(d)
+    cands = [i for i, x in enumerate(d) if x == best]
+    even = [i for i in cands if i % 2 == 0]
+    return even[0] if even else cands[0]
+
+
+def test_e2m1_golden_cases():
+    rows = []
+    with open(os.path.join(GOLDEN, "e2m1_cases.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                w, s, nib = line.split()[:3]
+                rows.append((float(w), float(s), int(nib, 16)))
+    assert len(rows) >= 20
+    for w, s, nib in rows:
+        got, _, _ = oracle.fake_quant(np.array([w]), np.array([s]))
+        assert int(got[0]) == nib, (w, s, nib, int(got[0]))
+
+
+def test_e2m1_rounding_matches_exact_rationals_on_midpoints_and_neighbours():
+    r = rng(2)
+    cases_w, cases_s = [], []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    # scales with short mantissas make m*s exactly representable: genuine ties
+    for s in [1.0, 0.5, 2.0 ** -7, 0.75, 1.5 * 2.0 ** -9, 0.625]:
+        for m in mids:
+            w = np.float32(m * s)
+            for v in (w, np.nextafter(w, np.float32(np.inf)), np.nextafter(w, np.float32(0))):
+                cases_w.append(float(v)); cases_s.append(s)
+    # random fp32 scales: nearest fp32 neighbours of the (inexact) midpoints
+    for _ in range(300):
+        s = float(np.float32(r.uniform(1e-4, 1.0)))
+        m = mids[r.integers(len(mids))]
+        w = np.float32(m * s)
+        for v in (w, np.nextafter(w, np.float32(np.inf)), np.nextafter(w, np.float32(0))):
+            cases_w.append(float(v)); cases_s.append(s)
+    # bf16 weights against candidate scales from the real ladder
+    g = float(oracle.global_scale(0.09))
+    sc = oracle.candidate_scales(g)
+    wb = synth.f32_from_bf16_bits(synth.bf16_bits_from_f32(r.normal(0, 0.02, 400).astype(np.float32)))
+    for w in wb:
+        for s in sc[r.integers(0, 126, 4)]:
+            cases_w.append(float(w)); cases_s.append(float(s))
+    w = np.array(cases_w); s = np.array(cases_s)
+    nib, wq, e = oracle.fake_quant(w, s)
+    exp = np.array([_exact_index(a, b) for a, b in zip(cases_w, cases_s)])
+    np.testing.assert_array_equal(nib & 7, exp)
+    np.testing.assert_array_equal(nib >> 3, (w < 0).astype(np.uint8))
+    # e is exact: compare with rationals
+    for i in range(0, len(w), 97):
+        q = GRID_F[exp[i]] * Fraction(s[i]) * (-1 if w[i] < 0 else 1)
+        assert Fraction(e[i]) == q - Fraction(w[i])
+
+
+def test_pack_nibbles_low_first():
+    nib = np.array([[1, 2, 3, 4, 0xf, 0]], dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.pack_nibbles(nib), [[0x21, 0x43, 0x0f]])
+
+
+# ------------------------------------------------------------------ accumulation identities
+def test_hessian_quadratic_form_and_importance_identities():
+    r = rng(3)
+    T, cin = 53, 48
+    X = r.standard_normal((T, cin))
+    off = np.array([0, T])
+    H, imp = oracle.accumulate(X, off, want_imp=True)
+    for n in range(cin // 16):
+        v = r.standard_normal(16)
+        q = X[:, 16 * n:16 * n + 16] @ v
+        assert np.isclose(v @ H[0, n] @ v, q @ q / T, rtol=1e-12)
+        np.testing.assert_allclose(np.diag(H[0, n]) * T, imp[0, 16 * n:16 * n + 16], rtol=1e-12)
+        assert np.allclose(H[0, n], H[0, n].T)
+    assert np.isclose(imp.sum(), (X * X).sum(), rtol=1e-12)
+
+
+def test_cross_matrix_bilinear_identity_and_beta():
+    r = rng(4)
+    T, cin = 41, 32
+    X = r.standard_normal((T, cin))
+    Xq = X + 0.1 * r.standard_normal((T, cin))
+    off = np.array([0, T])
+    H, P = oracle.accumulate_act_aware(X, Xq, off)
+    u, v = r.standard_normal(16), r.standard_normal(16)
+    for n in range(2):
+        sl = slice(16 * n, 16 * n + 16)
+        assert np.isclose(u @ P[0, n] @ v, (Xq[:, sl] @ u) @ ((Xq - X)[:, sl] @ v) / T, rtol=1e-12)
+        assert np.isclose(u @ H[0, n] @ u, np.sum((Xq[:, sl] @ u) ** 2) / T, rtol=1e-12)
+    H2, P2 = oracle.accumulate_act_aware(X, Xq, off, beta=0.5, H_prev=H, P_prev=P)
+    np.testing.assert_allclose(H2, 1.5 * H, rtol=1e-14)
+    np.testing.assert_allclose(P2, 1.5 * P, rtol=1e-14)
+    Hx, Px = oracle.accumulate_act_aware(X, X, off)
+    assert np.all(Px == 0)                                   # X_q = X => P = 0
+
+
+def test_empty_group_gives_zero_sums():
+    X = rng(5).standard_normal((10, 16))
+    H, imp = oracle.accumulate(X, np.array([0, 0, 10, 10]), want_imp=True)
+    assert np.all(H[0] == 0) and np.all(H[2] == 0) and np.all(imp[0] == 0)
+    assert np.any(H[1] != 0)
+
+
+# ------------------------------------------------------------------ P3: expanded output-MSE identity
+@pytest.mark.parametrize("cin,act", [(16, False), (16, True), (48, False), (48, True)])
+def test_objective_equals_output_mse_minus_constant(cin, act):
+    r = rng(6, cin, int(act))
+    T, cout = 37, 5
+    X = r.standard_normal((T, cin))
+    Xq = (X + 0.15 * r.standard_normal((T, cin))) if act else X.copy()
+    W = r.normal(0, 0.02, (1, cout, cin))
+    amax = oracle.absmax(W)
+    g = oracle.global_scale(amax)[0]
+    if act:
+        H, P = oracle.accumulate_act_aware(X, Xq, np.array([0, T]))
+    else:
+        H, _ = oracle.accumulate(X, np.array([0, T]))
+        P = None
+    s = oracle.candidate_scales(g)
+    saw_negative = False
+    for c in range(cout):
+        for n in range(cin // 16):
+            sl = slice(16 * n, 16 * n + 16)
+            w0 = W[0, c, sl]
+            L, Q, C = oracle.candidate_losses(w0[None], [g], H[0, n][None],
+                                              None if P is None else P[0, n][None])
+            direct = np.empty(126)
+            for k in range(126):
+                _, wq, _ = oracle.fake_quant(w0, s[k])
+                y = Xq[:, sl] @ wq - X[:, sl] @ w0
+                direct[k] = y @ y / T
+            const = np.sum(((Xq - X)[:, sl] @ w0) ** 2) / T
+            np.testing.assert_allclose(L[0] + const, direct, rtol=1e-10, atol=1e-14)
+            saw_negative |= bool(np.any(L[0] < 0))
+            res = oracle.sweep_blocks(w0[None], [g], H[0, n][None], None if P is None else P[0, n][None])
+            kd = int(np.argmin(direct))
+            if abs(np.sort(direct)[1] - direct[kd]) > 1e-9 * abs(direct[kd]):
+                assert res["code"][0] == kd + 1
+    if act:
+        assert saw_negative, "the activation-aware objective should go negative on some candidate"
+
+
+# ------------------------------------------------------------------ P4: diagonal equivalence
+def test_diagonal_hessian_equals_wmse_form():
+    r = rng(7)
+    G, cout, cin = 2, 12, 64
+    W = r.normal(0, 0.02, (G, cout, cin))
+    imp = r.uniform(0.1, 50.0, (G, cin))
+    imp[1, :16] = 0.0                                       # a dead block: both sides use 1
+    H = np.zeros((G, cin // 16, 16, 16))
+    for gi in range(G):
+        for n in range(cin // 16):
+            H[gi, n] = np.diag(imp[gi, 16 * n:16 * n + 16])
+    amax = oracle.absmax(W)
+    a = oracle.sweep(W, amax, H)
+    b = oracle.sweep_diag(W, amax, imp)
+    np.testing.assert_array_equal(a["code"], b["code"])
+    np.testing.assert_array_equal(a["fp4"], b["fp4"])
+    np.testing.assert_allclose(a["loss"], b["loss"], rtol=1e-12)
+
+
+def test_diag_of_hessian_scales_by_token_count():
+    r = rng(8)
+    T, cin, cout = 29, 32, 6
+    X = r.standard_normal((T, cin))
+    W = r.normal(0, 0.02, (1, cout, cin))
+    H, imp = oracle.accumulate(X, np.array([0, T]), want_imp=True)
+    Hd = np.zeros_like(H)
+    for n in range(cin // 16):
+        Hd[0, n] = np.diag(np.diag(H[0, n]))
+    amax = oracle.absmax(W)
+    a = oracle.sweep(W, amax, Hd)
+    b = oracle.sweep_diag(W, amax, imp)
+    np.testing.assert_array_equal(a["code"], b["code"])
+    np.testing.assert_allclose(b["loss"], T * a["loss"], rtol=1e-12)
+
+
+# ------------------------------------------------------------------ P5: H = I is the plain MSE search
+def _scalar_quant(w, s):
+    """Independent scalar E2M1 rounding through the midpoint thresholds."""
+    if s == 0:
+        return 0.0
+    a = abs(w)
+    mids_down = [(0.25, 0), (1.25, 2), (2.5, 4), (5.0, 6)]      # ties go to the lower (even) index
+    mids_up = [(0.75, 2), (1.75, 4), (3.5, 6)]                  # ties go to the upper (even) index
+    c = 0
+    for m, _ in mids_down:
+        c += Fraction(a) > Fraction(m) * Fraction(s)
+    for m, _ in mids_up:
+        c += Fraction(a) >= Fraction(m) * Fraction(s)
+    v = [0, 0.5, 1, 1.5, 2, 3, 4, 6][c] * s
+    return -v if w < 0 else v
+
+
+def test_identity_hessian_is_plain_weight_mse():
+    r = rng(9)
+    cout, cin = 6, 32
+    W = r.normal(0, 0.02, (1, cout, cin))
+    H = np.broadcast_to(np.eye(16), (1, cin // 16, 16, 16)).copy()
+    res = oracle.sweep(W, oracle.absmax(W), H)
+    g = float(oracle.global_scale(oracle.absmax(W))[0])
+    s = oracle.candidate_scales(g)
+    for c in range(cout):
+        for n in range(cin // 16):
+            w = W[0, c, 16 * n:16 * n + 16]
+            best, bk = np.inf, -1
+            for k in range(126):
+                err = sum((_scalar_quant(x, s[k]) - x) ** 2 for x in w)
+                if err < best:
+                    best, bk = err, k
+            assert res["code"][0, c, n] == bk + 1
+            assert np.isclose(res["loss"][0, c, n], best, rtol=1e-12)
+
+
+# ------------------------------------------------------------------ P6: invariances
+def test_invariances():
+    r = rng(10)
+    T, cout, cin = 64, 10, 48
+    X = r.standard_normal((T, cin))
+    Xq = X + 0.1 * r.standard_normal((T, cin))
+    W = r.normal(0, 0.02, (1, cout, cin))
+    off = np.array([0, T])
+    H, P = oracle.accumulate_act_aware(X, Xq, off)
+    amax = oracle.absmax(W)
+    base = oracle.sweep(W, amax, H, P)
+    # common positive scale of H and P
+    a = oracle.sweep(W, amax, 3.7 * H, 3.7 * P)
+    np.testing.assert_array_equal(a["code"], base["code"])
+    # X scaled by 2^j
+    H2, P2 = oracle.accumulate_act_aware(4 * X, 4 * Xq, off)
+    np.testing.assert_array_equal(oracle.sweep(W, amax, H2, P2)["code"], base["code"])
+    # W scaled by 2^j: the global scale, candidates and quotients scale exactly
+    b = oracle.sweep(8 * W, oracle.absmax(8 * W), H, P)
+    np.testing.assert_array_equal(b["code"], base["code"])
+    np.testing.assert_array_equal(b["fp4"], base["fp4"])
+    np.testing.assert_allclose(b["loss"], 64 * base["loss"], rtol=1e-12)
+    # output-row permutation
+    perm = r.permutation(cout)
+    c = oracle.sweep(W[:, perm], amax, H, P)
+    np.testing.assert_array_equal(c["code"], base["code"][:, perm])
+    # X_q = X makes the act-aware search the plain one
+    Hx, Px = oracle.accumulate_act_aware(X, X, off)
+    Hp, _ = oracle.accumulate(X, off)
+    np.testing.assert_array_equal(oracle.sweep(W, amax, Hx, Px)["code"], oracle.sweep(W, amax, Hp)["code"])
+
+
+# ------------------------------------------------------------------ P7: grouped == per-group
+def test_grouped_equals_per_group():
+    wl = synth.make("c5", n_groups=6, cout=8, cin=32, tokens=60, topk=2)
+    X, off = wl.X_f64(), wl.offsets
+    W = wl.W_f64()
+    H, imp = oracle.accumulate(X, off, want_imp=True)
+    res = oracle.sweep(W, oracle.absmax(W), H)
+    for g in range(wl.n_groups):
+        Xg = X[off[g]:off[g + 1]]
+        Hg, ig = oracle.accumulate(Xg, np.array([0, len(Xg)]), want_imp=True)
+        np.testing.assert_array_equal(Hg[0], H[g])
+        np.testing.assert_array_equal(ig[0], imp[g])
+        rg = oracle.sweep(W[g:g + 1], oracle.absmax(W[g:g + 1]), Hg)
+        np.testing.assert_array_equal(rg["code"][0], res["code"][g])
+        np.testing.assert_array_equal(rg["fp4"][0], res["fp4"][g])
+
+
+# ------------------------------------------------------------------ P8: non-vacuity
+def test_hessian_changes_codes_against_plain_mse():
+    wl = synth.make("c2", cout=64, cin=256, rows=512)
+    X, W = wl.X_f64(), wl.W_f64()
+    H, _ = oracle.accumulate(X, wl.offsets)
+    amax = oracle.absmax(W)
+    a = oracle.sweep(W, amax, H)["code"]
+    eye = np.broadcast_to(np.eye(16), H.shape).copy()
+    b = oracle.sweep(W, amax, eye)["code"]
+    frac = np.mean(a != b)
+    assert frac > 0.05, frac
+
+
+# ------------------------------------------------------------------ P9: optimality re-check
+def test_winner_is_optimal_on_independent_reevaluation():
+    r = rng(11)
+    B = 40
+    w = r.normal(0, 0.02, (B, 16))
+    g = oracle.global_scale(np.full(B, 0.1))
+    A = r.standard_normal((B, 16, 16))
+    H = np.einsum("bij,bkj->bik", A, A) / 16
+    P = 0.1 * r.standard_normal((B, 16, 16))
+    res = oracle.sweep_blocks(w, g, H, P)
+    for b in range(B):
+        s = oracle.candidate_scales(g[b])
+        bias = P[b] @ w[b]
+        Ls = []
+        for k in range(126):
+            e = np.array([_scalar_quant(x, s[k]) for x in w[b]]) - w[b]
+            Ls.append(float(e @ H[b] @ e + 2 * e @ bias))
+        kbest = int(np.argmin(Ls))
+        assert res["code"][b] == kbest + 1
+        assert np.isclose(res["loss"][b], Ls[kbest], rtol=1e-10, atol=1e-18)
+
+
+# ------------------------------------------------------------------ degenerate blocks
+def test_degenerate_blocks():
+    w = np.zeros((3, 16))
+    w[1] = np.linspace(-0.05, 0.05, 16)
+    g = oracle.global_scale(np.array([0.1, 0.1, 0.0]))
+    H = np.zeros((3, 16, 16))                                 # zero trace: plain MSE
+    res = oracle.sweep_blocks(w, g, H)
+    # all-zero block: every candidate scores 0, first (lowest) code wins, nibbles 0
+    assert res["code"][0] == 1 and np.all(res["nib"][0] == 0) and res["loss"][0] == 0
+    eye = np.broadcast_to(np.eye(16), (1, 16, 16))
+    ref = oracle.sweep_blocks(w[1:2], g[1:2], eye)
+    assert res["code"][1] == ref["code"][0]
+    # zero global scale (all-zero matrix): all scales 0 -> everything quantizes to 0, code 1
+    assert res["code"][2] == 1 and np.all(res["nib"][2] == 0)
+
+
+def test_exemption_rule_flags_true_ties_only():
+    res = dict(L1=np.array([1.0, 1.0, -1e-3]), L2=np.array([1.0 + 5e-7, 1.1, -1e-3 + 1e-10]),
+               Q1=np.array([1.0, 1.0, 0.5]), C1=np.array([0.0, 0.0, -0.501]),
+               Q2=np.array([1.0, 1.1, 0.5]), C2=np.array([0.0, 0.0, -0.501]))
+    np.testing.assert_array_equal(oracle.exempt_mask(res), [True, False, True])
+
+
+# ------------------------------------------------------------------ input generator determinism
+def test_generator_is_deterministic_and_shaped():
+    a = synth.make("c1")
+    b = synth.make("c1")
+    assert a.sha256() == b.sha256()
+    assert a.W.shape == (1, 64, 128) and a.X.shape == (256, 128) and a.W.dtype == np.float32
+    with open(os.path.join(GOLDEN, "synth_sha256.txt")) as f:
+        want = dict(line.split() for line in f if line.strip() and not line.startswith("#"))
+    assert a.sha256()["W"] == want["c1.W"] and a.sha256()["X"] == want["c1.X"]
+    c = synth.make("c5", n_groups=8, cout=4, cin=32, tokens=100, topk=3)
+    assert c.offsets[-1] == 300 and np.all(np.diff(c.offsets) >= 0)
