@@ -1,0 +1,217 @@
+"""Benchmark of the whole calibration path on one MI355X.
+
+One step = one pass of the hot path over one synthetic layer: max calibration of W (global amax),
+Hessian / importance / cross-matrix accumulation over the layer's tokens, and the 126-candidate
+E4M3 scale sweep over every weight block.  Inputs are resident in HBM before timing starts; X and W
+rotate over enough copies (>= 1 GiB) that every step streams them from HBM rather than from the
+256 MB Infinity Cache.
+
+Prints ONE JSON line.  `value` is weight blocks scored per second for the whole step.  `roofline`
+describes the dominant kernel (the sweep), timed with HIP events on the stream it runs on;
+`accumulate` gives the accumulation's algorithmic HBM rate.  `cpu_baseline` is the float64 oracle
+timed on this host (see --help for the sample).
+
+Default workload: the dense 2048x2048 layer (bf16 W, 8192 tokens with 1% outlier channels).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "16-elem blocks scored/sec (126 scales each) + Hessian accum GB/s, % roofline"
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, GB/s
+FP32_PEAK_TFLOPS = 157.3           # MI355X dense fp32 matrix (MFMA) peak
+VALU_FP32_TFLOPS = 78.6            # fp32 vector FMA without packed math: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+# algorithmic flops per block (126 candidates): fake-quant 2/elem, H e 512, e^T(He) 32 (+ 2 e^T b 32)
+FLOPS_FULL = 126 * (32 + 512 + 32)
+FLOPS_COUPLED = 126 * (32 + 512 + 32 + 32) + 512
+FLOPS_DIAG = 126 * (32 + 48)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="c2", choices=list(synth.CONFIGS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-blocks", type=int, default=24576,
+                   help="blocks of the oracle's sweep timed for the CPU baseline")
+    p.add_argument("--rotate-gib", type=float, default=1.0)
+    return p.parse_args()
+
+
+def to_dev(torch, a, dtype, dev):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(dev)
+
+
+def cpu_baseline(wl, sample_blocks):
+    """The float64 oracle, single-threaded: full absmax and accumulation, sweep on a seeded sample
+    of blocks; returns the projected whole-step blocks/s."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    if wl.n_groups != 1:
+        raise RuntimeError("the CPU baseline is defined for the dense workloads")
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        Wo = wl.W_f64()
+        amax = oracle.absmax(Wo)
+        t_abs = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        if wl.mode == "act":
+            H, P = oracle.accumulate_act_aware(wl.X_f64(), wl.Xq_f64(), wl.offsets)
+        elif wl.mode == "diag":
+            H, P = None, None
+            _, imp = oracle.accumulate(wl.X_f64(), wl.offsets, want_h=False, want_imp=True)
+        else:
+            H, P = oracle.accumulate(wl.X_f64(), wl.offsets)[0], None
+        t_acc = time.perf_counter() - t0
+        rng = np.random.default_rng(12345)
+        nb = wl.n_blocks
+        B = min(sample_blocks, wl.cout * nb)
+        flat = rng.choice(wl.cout * nb, size=B, replace=False)
+        c, n = flat // nb, flat % nb
+        w = Wo[0].reshape(wl.cout, nb, 16)[c, n]
+        g = np.repeat(oracle.global_scale(amax)[0], B)
+        t0 = time.perf_counter()
+        if wl.mode == "diag":
+            oracle.sweep_blocks_diag(w, g, imp[0].reshape(nb, 16)[n])
+        else:
+            oracle.sweep_blocks(w, g, H[0], None if P is None else P[0], hidx=n)
+        t_sw = time.perf_counter() - t0
+    blocks = wl.weight_blocks
+    step = t_abs + t_acc + t_sw / B * blocks
+    return {"value": blocks / step, "unit": "blocks/s", "cores": 1, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle, 1 thread: absmax and accumulation over the whole layer "
+                       f"({t_abs + t_acc:.2f} s), sweep over {B} seeded random blocks ({t_sw:.2f} s); "
+                       f"whole-step time projected per block to all {blocks} blocks")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import nvfp4_scale_calibration_lh_amd as lh
+
+    dev = torch.device("cuda:0")
+    wl = synth.make(args.config)
+    G, cout, cin, rows = wl.n_groups, wl.cout, wl.cin, wl.rows
+    nb = cin // 16
+    blocks = wl.weight_blocks
+    esz = 2 if wl.dtype == "bf16" else 4
+    x_bytes = rows * cin * esz * (2 if wl.mode == "act" else 1)
+    w_bytes = G * cout * cin * esz
+    copies = max(1, min(64, int(np.ceil(args.rotate_gib * 2 ** 30 / max(1, x_bytes + w_bytes)))))
+    free = torch.cuda.mem_get_info(dev)[0]
+    copies = max(1, min(copies, int(0.5 * free // max(1, x_bytes + w_bytes))))
+
+    W0 = to_dev(torch, wl.W, wl.dtype, dev)
+    X0 = to_dev(torch, wl.X, wl.dtype, dev)
+    Xq0 = to_dev(torch, wl.Xq, wl.dtype, dev) if wl.Xq is not None else None
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
+    Xqs = ([Xq0] + [Xq0.clone() for _ in range(copies - 1)]) if Xq0 is not None else None
+    off = torch.from_numpy(wl.offsets).to(dev) if G > 1 else None
+
+    amax = torch.empty(G, dtype=torch.float32, device=dev)
+    H = torch.empty((G, nb, 16, 16), dtype=torch.float32, device=dev)
+    P = torch.empty_like(H) if wl.mode == "act" else None
+    imp = torch.empty((G, cin), dtype=torch.float32, device=dev)
+    code = torch.empty((G, cout, nb), dtype=torch.uint8, device=dev)
+    fp4 = torch.empty((G, cout, cin // 2), dtype=torch.uint8, device=dev)
+    loss = torch.empty((G, cout, nb), dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        j = i % copies
+        W, X = Ws[j], Xs[j]
+        if ev: ev[0].record()
+        lh.lh_absmax(W, amax)
+        if ev: ev[1].record()
+        if wl.mode == "act":
+            lh.lh_accumulate_act_aware(X, Xqs[j], H=H, P=P, offsets=off)
+        elif wl.mode == "diag":
+            lh.lh_accumulate(X, H=None, imp=imp, offsets=off, want_h=False, want_imp=True)
+        else:
+            lh.lh_accumulate(X, H=H, offsets=off)
+        if ev: ev[2].record()
+        if wl.mode == "diag":
+            lh.lh_scale_sweep_diag(W, amax, imp, code, fp4, loss)
+        else:
+            lh.lh_scale_sweep(W, amax, H, P, code, fp4, loss)
+        if ev: ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_abs = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_acc = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_sw = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms_step = wall / args.steps * 1e3
+
+    flops_blk = FLOPS_DIAG if wl.mode == "diag" else (FLOPS_COUPLED if wl.mode == "act" else FLOPS_FULL)
+    sweep_tflops = flops_blk * blocks / (ms_sw * 1e-3) / 1e12
+    acc_bytes = x_bytes + (G * cin * 4 if wl.mode == "diag" else G * nb * 1024 * (2 if wl.mode == "act" else 1))
+    acc_gbs = acc_bytes / (ms_acc * 1e-3) / 1e9
+    abs_gbs = w_bytes / (ms_abs * 1e-3) / 1e9
+    if wl.mode == "diag":
+        roof = {"bound": "alu", "achieved": sweep_tflops, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
+                "frac": sweep_tflops / VALU_FP32_TFLOPS, "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": sweep_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": sweep_tflops / FP32_PEAK_TFLOPS, "traffic": None}
+    roof.update({"kernel": "sweep", "flops_per_block": flops_blk, "blocks_per_launch": blocks,
+                 "avg_launch_ms": ms_sw})
+
+    out = {
+        "metric": METRIC,
+        "value": blocks / (ms_step * 1e-3),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.description, "name": args.config, "n_groups": G, "cout": cout,
+                   "cin": cin, "rows": rows, "blocks": blocks, "input_dtype": wl.dtype,
+                   "mode": wl.mode, "rotating_copies": copies},
+        "roofline": roof,
+        "accumulate": {"avg_launch_ms": ms_acc, "algorithmic_bytes": acc_bytes, "achieved_gbs": acc_gbs,
+                       "peak_gbs": HBM_PEAK_GBS, "frac": acc_gbs / HBM_PEAK_GBS},
+        "absmax": {"avg_launch_ms": ms_abs, "achieved_gbs": abs_gbs, "frac": abs_gbs / HBM_PEAK_GBS},
+        "sweep": {"avg_launch_ms": ms_sw, "blocks_per_s": blocks / (ms_sw * 1e-3), "tflops": sweep_tflops},
+    }
+    if not args.no_cpu_baseline and G == 1:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_blocks)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * lh.h -- C ABI of the MI355X (gfx950) local-Hessian NVFP4 weight-scale calibration library.
+ *
+ * The library computes, on one GPU, the two parts of local-Hessian-weighted NVFP4 weight-scale
+ * calibration:
+ *   1. per 16-wide input-channel block n, the local Hessian H_n = X[:,n]^T X[:,n] / B, the
+ *      activation-aware cross matrix P_n = X_q^T (X_q - X) / B and the importance vector
+ *      Imp_i = ||X[:,i]||^2;
+ *   2. for every 16-element weight block, the exhaustive search over the 126 positive finite
+ *      E4M3 block scales, scoring the E2M1 fake-quantization error e = quant(w) - w by
+ *      e^T H_n e + 2 e^T (P_n w) (or sum_i Imp_i e_i^2) and keeping the argmin.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers, row-major and densely packed, owned by the caller.
+ *     Inputs are never modified.  Outputs are fully overwritten (H, P and imp are read first
+ *     only when beta != 0).
+ *   - X is [rows, cin] (tokens x input channels, as a linear layer sees its input); W is
+ *     [n_groups, cout, cin]; blocks run along cin in 16s (block n = channels 16n..16n+15).
+ *   - Groups are MoE experts: rows [off[g], off[g+1]) of X belong to group g.  group_offsets is a
+ *     device int64 array of n_groups+1 entries; pass NULL with n_groups == 1 for a dense layer
+ *     (all rows).  Offsets must be non-decreasing with off[0] = 0 and off[n_groups] = rows; this is
+ *     a caller contract (checking it would need a device read) and is not verified.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null stream of
+ *     the pointers' device).  The library never synchronizes the host, launches on the device that
+ *     owns the pointers and restores the caller's current device.
+ *   - Scratch memory, when an entry point needs it, is taken with hipMallocAsync on `stream` and
+ *     released with hipFreeAsync on the same stream before the call returns.
+ *   - Return: LH_OK, or an error code with a message available from lh_last_error().  Argument
+ *     checks run before any launch.  Faults inside kernels surface at the caller's next
+ *     synchronization, as usual in HIP.  NaN or Inf in any input gives undefined results.
+ *
+ * Numerics
+ *   - Accumulation reads bf16 or fp32 values exactly, multiplies them exactly (bf16) or in fp32
+ *     (fp32 inputs), and sums in fp32 in a fixed order: results are bit-reproducible run to run.
+ *   - The sweep returns the scale code and FP4 codes of the exact argmin of the float64 objective:
+ *     a float32 pass scores every candidate with a rigorous error bound and any block whose
+ *     winner is not certain is re-scored in float64 with exact quantization.
+ *
+ * Citations are to the pages this library follows: "Add activation-aware local Hessian scale
+ * calibration" (PR #1976), "add local hessian calibration" (PR #788), "Add WMSE weight scale
+ * search calibration" (PR #2283) and "Add composable scale calibration to GPTQ" (PR #2004).
+ */
+#ifndef LH_H_
+#define LH_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LH_VERSION 1
+
+typedef enum {
+  LH_OK = 0,
+  LH_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, host or foreign-device pointer */
+  LH_ERR_UNSUPPORTED = 2,      /* unknown dtype or no gfx950 device */
+  LH_ERR_HIP = 3               /* a HIP runtime call or launch failed */
+} lh_status;
+
+typedef enum { LH_DTYPE_F32 = 0, LH_DTYPE_BF16 = 1 } lh_dtype;
+
+/*
+ * Per-block local Hessian and importance (PR #788, Overview / Changes: per-block Hessians
+ * collected by forward hooks; PR #2283, How: the diagonal path accumulates x.square().sum(-1)).
+ *
+ *   H[g][n]   = beta * H[g][n]   + (1/T_g) * sum_{t in g} x_t[n] x_t[n]^T     (if H != NULL)
+ *   imp[g][i] = beta * imp[g][i] + sum_{t in g} X[t,i]^2                      (if imp != NULL)
+ *
+ * X        [rows, cin], dtype x_dtype.
+ * H        [n_groups, cin/16, 16, 16] fp32 or NULL.      imp  [n_groups, cin] fp32 or NULL.
+ * At least one of H, imp must be non-NULL.  T_g = off[g+1]-off[g]; T_g == 0 makes the sum term 0.
+ * beta lets a caller stream token batches (beta = 1 with sums, or a running mean).
+ * Errors: INVALID_ARGUMENT for rows < 0, cin <= 0 or cin % 16, n_groups < 1, NULL X with rows > 0,
+ * both outputs NULL, offsets NULL with n_groups > 1, non-device or mixed-device pointers.
+ */
+lh_status lh_accumulate(const void* X, lh_dtype x_dtype, int64_t rows, int64_t cin,
+                        const int64_t* group_offsets, int64_t n_groups, float beta,
+                        float* H, float* imp, void* stream);
+
+/*
+ * Activation-aware Hessian and cross matrix (PR #1976, What does this PR do?):
+ *   H[g][n] = beta*H[g][n] + X_q^T X_q / T_g,   P[g][n] = beta*P[g][n] + X_q^T (X_q - X) / T_g
+ * per 16-channel block, over the rows of group g.  X and Xq are [rows, cin] of the same dtype.
+ * P is formed from the difference D = X_q - X (exact in fp32 for bf16 inputs), never as the
+ * difference of two products.  H and P are both required.  Errors as lh_accumulate.
+ */
+lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype, int64_t rows,
+                                  int64_t cin, const int64_t* group_offsets, int64_t n_groups,
+                                  float beta, float* H, float* P, void* stream);
+
+/*
+ * Exhaustive FP8 block-scale sweep with the local-Hessian objective (PR #788, review: block loss
+ * cnb,nbd,cnd->cn; PR #1976, review: dw = quant(w) - w, coupling term 2 dw^T (P W0) with
+ * P.W0 = nbd,cnd->cnb, best_loss = inf so negative losses are handled; PR #2283, How: the 126
+ * candidate scales; PR #2004: NVFP4 scaling is 448-normalized).
+ *
+ * For every block (g, c, n) with weights w = W[g][c][16n..16n+15]:
+ *   g_g  = fp32(global_amax[g] / (6*448))
+ *   s_k  = fp32(v_k * g_g), v_k the E4M3 value of byte k, k = 0x01..0x7E (126 candidates)
+ *   q_k  = E2M1 fake-quant of w with scale s_k: each |w_i|/s_k (exact quotient) is rounded to the
+ *          nearest of {0,0.5,1,1.5,2,3,4,6}, ties to the even grid index, saturating at 6
+ *   e_k  = q_k - w,  L_k = e_k^T H_n e_k + 2 e_k^T (P_n w)      (P == NULL: no cross term)
+ *   k*   = argmin_k L_k, lowest code on ties.
+ * A block whose H_n has zero trace (no activation energy) is scored with H = I and no cross term.
+ *
+ * W           [n_groups, cout, cin] dtype w_dtype.
+ * global_amax [n_groups] fp32 device, >= 0 and finite (normally max |W_g|, see lh_absmax).
+ * H, P        [n_groups, cin/16, 16, 16] fp32 (P may be NULL).
+ * scale_code  [n_groups, cout, cin/16] uint8: the E4M3 byte k* (0x01..0x7E).
+ * fp4         [n_groups, cout, cin/2] uint8 or NULL: nibble = (w < 0) << 3 | grid index,
+ *             element 2j in the low nibble of byte j.
+ * best_loss   [n_groups, cout, cin/16] fp32 or NULL: L_{k*} (may be negative with P).
+ * Errors: INVALID_ARGUMENT for n_groups < 1, cout < 0, cin <= 0 or cin % 16, NULL required
+ * pointers, non-device or mixed-device pointers.
+ */
+lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                         int64_t cin, const float* global_amax, const float* H, const float* P,
+                         uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream);
+
+/*
+ * Same sweep scored by the importance-weighted error L_k = sum_i imp[g][16n+i] * e_{k,i}^2
+ * (PR #2283, What / How: H replaced by diag(Imp), einsum cnb,nb->cn, no diag_embed and no
+ * matmul on the hot path).  A block whose importance sums to zero uses Imp = 1.
+ * imp [n_groups, cin] fp32.  Other arguments and errors as lh_scale_sweep.
+ */
+lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                              int64_t cin, const float* global_amax, const float* imp,
+                              uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream);
+
+/*
+ * Per-group absolute maximum amax_out[g] = max |W_g| over elems_per_group elements: the max
+ * calibration that fixes the weight's global amax before the search (PR #788, Sequence diagram:
+ * initial max_calibrate).  W is [n_groups, elems_per_group]; an empty group gives 0.
+ * Errors: INVALID_ARGUMENT for n_groups < 1, elems_per_group < 0, NULL pointers, non-device or
+ * mixed-device pointers.
+ */
+lh_status lh_absmax(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t elems_per_group,
+                    float* amax_out, void* stream);
+
+/* Message of the last error on the calling thread ("" if none); valid until its next call. */
+const char* lh_last_error(void);
+
+/* LH_VERSION of the built library. */
+int lh_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LH_H_ */

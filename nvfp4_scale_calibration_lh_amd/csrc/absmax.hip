@@ -1,0 +1,112 @@
+// Per-group max |W| (the max calibration that fixes each weight matrix's global amax before the
+// scale search; "add local hessian calibration", Sequence diagram: initial max_calibrate).
+//
+// HBM-bound streaming reduction.  |x| is compared on raw bit patterns with the sign bit cleared
+// (for finite values the unsigned order of those bits is the order of the magnitudes), so the
+// bf16 path never converts to float and the result is exact and order-independent.  Workgroups
+// combine with an unsigned atomicMax on the output word, which an init kernel sets to 0 first.
+#include "lh_internal.hpp"
+
+namespace lh {
+namespace {
+
+constexpr int kThreads = 256;
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+__global__ void k_absmax_init(unsigned* out, int64_t n) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) out[i] = 0u;
+}
+
+__device__ inline unsigned wave_max(unsigned v) {
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// Vector path: each thread reads 16 bytes per step (8 bf16 or 4 fp32).  Requires the group's
+// base to be 16-byte aligned and elems to be a multiple of the vector width.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_absmax_vec(const v4u* __restrict__ W,
+                                                         int64_t vec_per_group, unsigned* out) {
+  const int g = blockIdx.y;
+  const v4u* base = W + (int64_t)g * vec_per_group;
+  unsigned m = 0;
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < vec_per_group;
+       i += (int64_t)gridDim.x * kThreads) {
+    const v4u v = __builtin_nontemporal_load(base + i);
+    if (BF16) {
+      unsigned a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+      unsigned b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+      m = max(m, max(a, b) << 16);
+    } else {
+      m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+    }
+  }
+  __shared__ unsigned red[kThreads / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned r = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+    if (r) atomicMax(out + g, r);
+  }
+}
+
+// Scalar path for unaligned or ragged groups.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_absmax_scalar(const void* __restrict__ W,
+                                                            int64_t elems, unsigned* out) {
+  const int g = blockIdx.y;
+  unsigned m = 0;
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < elems;
+       i += (int64_t)gridDim.x * kThreads) {
+    if (BF16) {
+      unsigned short b = ((const unsigned short*)W)[(int64_t)g * elems + i];
+      m = max(m, ((unsigned)b & 0x7FFFu) << 16);
+    } else {
+      m = max(m, ((const unsigned*)W)[(int64_t)g * elems + i] & 0x7FFFFFFFu);
+    }
+  }
+  __shared__ unsigned red[kThreads / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned r = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+    if (r) atomicMax(out + g, r);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_absmax(const void* W, bool bf16, int64_t n_groups, int64_t elems, float* amax,
+                         hipStream_t stream) {
+  unsigned* out = reinterpret_cast<unsigned*>(amax);
+  hipLaunchKernelGGL(k_absmax_init, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, stream,
+                     out, n_groups);
+  if (elems == 0) return hipGetLastError();
+  const int vec = bf16 ? 8 : 4;
+  const bool aligned = (reinterpret_cast<uintptr_t>(W) % 16 == 0) && (elems % vec == 0);
+  const int64_t units = aligned ? elems / vec : elems;
+  // about 8 units per thread, at most 256 workgroups per group
+  int64_t bx = (units + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
+  if (bx < 1) bx = 1;
+  if (bx > 256) bx = 256;
+  dim3 grid((unsigned)bx, (unsigned)n_groups);
+  if (aligned) {
+    if (bf16)
+      hipLaunchKernelGGL(k_absmax_vec<true>, grid, dim3(kThreads), 0, stream, (const v4u*)W, units, out);
+    else
+      hipLaunchKernelGGL(k_absmax_vec<false>, grid, dim3(kThreads), 0, stream, (const v4u*)W, units, out);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL(k_absmax_scalar<true>, grid, dim3(kThreads), 0, stream, W, elems, out);
+    else
+      hipLaunchKernelGGL(k_absmax_scalar<false>, grid, dim3(kThreads), 0, stream, W, elems, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lh

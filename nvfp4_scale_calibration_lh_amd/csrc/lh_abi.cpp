@@ -1,0 +1,282 @@
+// C ABI of the calibration library (declarations and contracts in include/lh.h).
+//
+// This file validates arguments before anything is launched, selects the device that owns the
+// pointers (restoring the caller's current device), takes accumulation scratch memory from a
+// library-owned stream-ordered pool, and launches the kernels on the caller's stream.  It keeps
+// no state besides the per-device pool and a thread-local error message.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/lh.h"
+#include "lh_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lh_status fail(lh_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+lh_status ok() {
+  g_last_error.clear();
+  return LH_OK;
+}
+
+lh_status hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();  // clear the sticky launch error so the caller's next call is clean
+  return fail(LH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int d) { return d == LH_DTYPE_F32 || d == LH_DTYPE_BF16; }
+
+// Device that owns `p`, or -1 (with the error message set) if p is not device memory.
+int device_of(const void* p, const char* name) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    fail(LH_ERR_INVALID_ARGUMENT, "%s is not a device pointer (%s)", name, hipGetErrorString(e));
+    return -1;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) {
+    fail(LH_ERR_INVALID_ARGUMENT, "%s is not device memory", name);
+    return -1;
+  }
+  return attr.device;
+}
+
+struct PtrCheck {
+  const void* p;
+  const char* name;
+};
+
+// All non-null pointers must be device memory of one device, 16-byte aligned where required.
+lh_status check_pointers(std::initializer_list<PtrCheck> ptrs, int* dev_out) {
+  int dev = -1;
+  for (const PtrCheck& c : ptrs) {
+    if (!c.p) continue;
+    int d = device_of(c.p, c.name);
+    if (d < 0) return LH_ERR_INVALID_ARGUMENT;
+    if (dev >= 0 && d != dev) return fail(LH_ERR_INVALID_ARGUMENT, "%s is on device %d, other pointers on device %d", c.name, d, dev);
+    dev = d;
+  }
+  if (dev < 0) return fail(LH_ERR_INVALID_ARGUMENT, "no device pointer given");
+  *dev_out = dev;
+  return LH_OK;
+}
+
+lh_status check_aligned(const void* p, const char* name) {
+  if (p && (reinterpret_cast<uintptr_t>(p) % 16) != 0)
+    return fail(LH_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  return LH_OK;
+}
+
+// Switches to `dev` for the lifetime of the guard and checks that it is a gfx950 device.
+class DeviceGuard {
+ public:
+  lh_status enter(int dev) {
+    hipError_t e = hipGetDevice(&prev_);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (prev_ != dev) {
+      e = hipSetDevice(dev);
+      if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+      switched_ = true;
+    }
+    static std::mutex mu;
+    static std::vector<int> arch_ok(64, -1);
+    std::lock_guard<std::mutex> lk(mu);
+    if (dev < 0 || dev >= (int)arch_ok.size()) return fail(LH_ERR_UNSUPPORTED, "device %d out of range", dev);
+    if (arch_ok[dev] < 0) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+      arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    }
+    if (!arch_ok[dev]) return fail(LH_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+    return LH_OK;
+  }
+  ~DeviceGuard() {
+    if (switched_) (void)hipSetDevice(prev_);
+  }
+
+ private:
+  int prev_ = 0;
+  bool switched_ = false;
+};
+
+// One stream-ordered pool per device; its release threshold keeps freed scratch for reuse.
+hipError_t scratch_pool(int dev, hipMemPool_t* pool) {
+  static std::mutex mu;
+  static std::vector<hipMemPool_t> pools(64, nullptr);
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 0 || dev >= (int)pools.size()) return hipErrorInvalidDevice;
+  if (!pools[dev]) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p;
+    hipError_t e = hipMemPoolCreate(&p, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = ~0ull;
+    e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    pools[dev] = p;
+  }
+  *pool = pools[dev];
+  return hipSuccess;
+}
+
+lh_status check_shapes_x(int64_t rows, int64_t cin, const int64_t* offsets, int64_t n_groups) {
+  if (rows < 0) return fail(LH_ERR_INVALID_ARGUMENT, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (cin <= 0 || cin % 16) return fail(LH_ERR_INVALID_ARGUMENT, "cin must be a positive multiple of 16 (got %lld)", (long long)cin);
+  if (cin / 16 > 4LL * 65535) return fail(LH_ERR_INVALID_ARGUMENT, "cin too large");
+  if (n_groups < 1 || n_groups > 2147483647LL) return fail(LH_ERR_INVALID_ARGUMENT, "n_groups must be >= 1 (got %lld)", (long long)n_groups);
+  if (!offsets && n_groups != 1) return fail(LH_ERR_INVALID_ARGUMENT, "group_offsets is required when n_groups > 1");
+  return LH_OK;
+}
+
+lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t rows, int64_t cin,
+                         const int64_t* offsets, int64_t n_groups, float beta, float* H, float* P,
+                         float* imp, void* stream) {
+  int dev = -1;
+  lh_status st = check_pointers({{X, "X"}, {Xq, "Xq"}, {offsets, "group_offsets"}, {H, "H"}, {P, "P"}, {imp, "imp"}}, &dev);
+  if (st != LH_OK) return st;
+  if ((st = check_aligned(X, "X")) != LH_OK) return st;
+  if ((st = check_aligned(Xq, "Xq")) != LH_OK) return st;
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nb = cin / 16;
+  const bool act = Xq != nullptr;
+  const size_t floats = lh::accumulate_scratch_floats(rows, nb, act);
+  hipMemPool_t pool;
+  hipError_t e = scratch_pool(dev, &pool);
+  if (e != hipSuccess) return hip_fail(e, "scratch pool");
+  void* scratch = nullptr;
+  if (floats) {
+    e = hipMallocFromPoolAsync(&scratch, floats * sizeof(float), pool, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocFromPoolAsync");
+  }
+  const int64_t* off = offsets;   // NULL: dense layer, handled inside the kernels
+  e = lh::launch_accumulate(X, Xq, dt == LH_DTYPE_BF16, rows, cin, off, n_groups, beta, H, P, imp,
+                            static_cast<float*>(scratch), s);
+  hipError_t e2 = scratch ? hipFreeAsync(scratch, s) : hipSuccess;
+  if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFreeAsync");
+  return ok();
+}
+
+lh_status check_sweep_shapes(int64_t n_groups, int64_t cout, int64_t cin) {
+  if (n_groups < 1 || n_groups > 65535) return fail(LH_ERR_INVALID_ARGUMENT, "n_groups must be in [1, 65535] (got %lld)", (long long)n_groups);
+  if (cout < 0 || cout > 65535LL * 64) return fail(LH_ERR_INVALID_ARGUMENT, "cout out of range (got %lld)", (long long)cout);
+  if (cin <= 0 || cin % 16) return fail(LH_ERR_INVALID_ARGUMENT, "cin must be a positive multiple of 16 (got %lld)", (long long)cin);
+  return LH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lh_status lh_accumulate(const void* X, lh_dtype x_dtype, int64_t rows, int64_t cin,
+                        const int64_t* group_offsets, int64_t n_groups, float beta, float* H,
+                        float* imp, void* stream) {
+  if (!dtype_ok(x_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)x_dtype);
+  lh_status st = check_shapes_x(rows, cin, group_offsets, n_groups);
+  if (st != LH_OK) return st;
+  if (!H && !imp) return fail(LH_ERR_INVALID_ARGUMENT, "at least one of H, imp must be given");
+  if (!X && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X is NULL");
+  return run_accumulate(X, nullptr, x_dtype, rows, cin, group_offsets, n_groups, beta, H, nullptr, imp, stream);
+}
+
+lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype, int64_t rows,
+                                  int64_t cin, const int64_t* group_offsets, int64_t n_groups,
+                                  float beta, float* H, float* P, void* stream) {
+  if (!dtype_ok(dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  lh_status st = check_shapes_x(rows, cin, group_offsets, n_groups);
+  if (st != LH_OK) return st;
+  if (!H || !P) return fail(LH_ERR_INVALID_ARGUMENT, "H and P are both required");
+  if ((!X || !Xq) && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X and Xq are required");
+  if (rows == 0) {
+    // nothing to read: only the beta term remains; run the generic path with an alias for Xq
+    return run_accumulate(X ? X : H, Xq ? Xq : H, dtype, 0, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
+  }
+  return run_accumulate(X, Xq, dtype, rows, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
+}
+
+lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                         int64_t cin, const float* global_amax, const float* H, const float* P,
+                         uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {
+  if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);
+  lh_status st = check_sweep_shapes(n_groups, cout, cin);
+  if (st != LH_OK) return st;
+  if (!global_amax || !H || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax, H and scale_code are required");
+  if (!W && cout > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
+  int dev = -1;
+  st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {H, "H"}, {P, "P"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
+  if (st != LH_OK) return st;
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipError_t e = lh::launch_sweep(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, H, P,
+                                  scale_code, fp4, best_loss, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sweep launch");
+  return ok();
+}
+
+lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                              int64_t cin, const float* global_amax, const float* imp,
+                              uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {
+  if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);
+  lh_status st = check_sweep_shapes(n_groups, cout, cin);
+  if (st != LH_OK) return st;
+  if (!global_amax || !imp || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax, imp and scale_code are required");
+  if (!W && cout > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
+  int dev = -1;
+  st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {imp, "imp"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
+  if (st != LH_OK) return st;
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipError_t e = lh::launch_sweep_diag(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, imp,
+                                       scale_code, fp4, best_loss, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "diagonal sweep launch");
+  return ok();
+}
+
+lh_status lh_absmax(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t elems_per_group,
+                    float* amax_out, void* stream) {
+  if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);
+  if (n_groups < 1 || n_groups > 65535) return fail(LH_ERR_INVALID_ARGUMENT, "n_groups must be in [1, 65535] (got %lld)", (long long)n_groups);
+  if (elems_per_group < 0) return fail(LH_ERR_INVALID_ARGUMENT, "elems_per_group must be >= 0");
+  if (!amax_out) return fail(LH_ERR_INVALID_ARGUMENT, "amax_out is required");
+  if (!W && elems_per_group > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
+  int dev = -1;
+  lh_status st = check_pointers({{W, "W"}, {amax_out, "amax_out"}}, &dev);
+  if (st != LH_OK) return st;
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipError_t e = lh::launch_absmax(W, w_dtype == LH_DTYPE_BF16, n_groups, elems_per_group, amax_out,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "absmax launch");
+  return ok();
+}
+
+const char* lh_last_error(void) { return g_last_error.c_str(); }
+
+int lh_version(void) { return LH_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+"""The C ABI library loads, exports every entry point of include/lh.h, and rejects bad arguments
+before touching a device (no compute calls here: this suite runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lh.h")
+
+lh = pytest.importorskip("nvfp4_scale_calibration_lh_amd")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lh_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_scale_sweep", "lh_scale_sweep_diag",
+              "lh_absmax", "lh_last_error", "lh_version"):
+        assert n in names
+    assert set(names) == set(lh.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lh.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert lh.lh_version() == 1
+
+
+VP = ctypes.c_void_p
+FAKE = VP(0x1000)        # a non-null address that is not device memory
+
+
+def _err(code):
+    return code, lh.lh_last_error()
+
+
+def test_validation_errors_without_device():
+    L = lh.lib()
+    # unknown dtype
+    c, m = _err(L.lh_accumulate(FAKE, 7, 10, 32, None, 1, 0.0, FAKE, None, None))
+    assert c == lh.LH_ERR_UNSUPPORTED and "dtype" in m
+    # cin not a multiple of 16
+    c, m = _err(L.lh_accumulate(FAKE, lh.LH_DTYPE_BF16, 10, 40, None, 1, 0.0, FAKE, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "cin" in m
+    # negative rows, n_groups < 1, missing offsets for several groups
+    assert L.lh_accumulate(FAKE, 1, -1, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_accumulate(FAKE, 1, 10, 32, None, 0, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    c, m = _err(L.lh_accumulate(FAKE, 1, 10, 32, None, 3, 0.0, FAKE, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "group_offsets" in m
+    # no outputs, NULL input
+    assert L.lh_accumulate(FAKE, 1, 10, 32, None, 1, 0.0, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_accumulate(None, 1, 10, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    # act-aware needs both outputs
+    assert L.lh_accumulate_act_aware(FAKE, FAKE, 1, 10, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    # sweep
+    assert L.lh_scale_sweep(FAKE, 1, 0, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep(FAKE, 1, 1, 4, 33, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep(FAKE, 1, 1, 4, 32, None, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep(FAKE, 9, 1, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_UNSUPPORTED
+    assert L.lh_scale_sweep_diag(FAKE, 1, 1, 4, 32, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_absmax(FAKE, 1, 0, 10, FAKE, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_absmax(FAKE, 1, 1, -1, FAKE, None) == lh.LH_ERR_INVALID_ARGUMENT
+
+
+def test_host_pointer_is_rejected_not_dereferenced():
+    L = lh.lib()
+    buf = (ctypes.c_float * 64)()
+    out = (ctypes.c_float * 4)()
+    c, m = _err(L.lh_absmax(ctypes.cast(buf, VP), lh.LH_DTYPE_F32, 1, 64, ctypes.cast(out, VP), None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT, (c, m)
+    assert "W" in m
+    c, m = _err(L.lh_accumulate(ctypes.cast(buf, VP), lh.LH_DTYPE_F32, 4, 16, None, 1, 0.0,
+                                ctypes.cast(out, VP), None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT
+
+
+def test_binding_checks_shapes_before_calling():
+    import torch
+    with pytest.raises(ValueError):
+        lh.lh_accumulate(torch.zeros((4, 16)))          # CPU tensor
+    with pytest.raises(TypeError):
+        lh._dtype_code(torch.zeros(2, dtype=torch.float16))

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP library (called through its C ABI) against the float64 oracle.
+
+Sizes are small enough for the oracle to finish in seconds but span several accumulation tiles
+(256 rows), several sweep workgroups (64 rows x 4 block columns), partial tiles and ragged tails.
+Every case prints its name, seed and shapes before it touches the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import (assert_h_close, assert_imp_close, assert_p_close, assert_sweep_match,
+                         cross_gram)
+
+pytestmark = pytest.mark.gpu
+
+lh = pytest.importorskip("nvfp4_scale_calibration_lh_amd")
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def to_dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(DEV)
+
+
+def upload(wl):
+    W = to_dev(wl.W, wl.dtype)
+    X = to_dev(wl.X, wl.dtype)
+    Xq = to_dev(wl.Xq, wl.dtype) if wl.Xq is not None else None
+    off = torch.from_numpy(wl.offsets).to(DEV) if wl.n_groups > 1 else None
+    return W, X, Xq, off
+
+
+SMALL = {
+    "c1": dict(),
+    "c2": dict(cout=150, cin=80, rows=600),
+    "c3": dict(cout=70, cin=96, rows=530),
+    "c4": dict(cout=130, cin=112, rows=300),
+    "c5": dict(n_groups=12, cout=40, cin=64, tokens=400, topk=3),
+}
+
+
+# ------------------------------------------------------------------------------------ absmax
+@pytest.mark.parametrize("name", list(SMALL))
+def test_absmax_bit_exact(name):
+    wl = synth.make(name, **SMALL[name])
+    note(f"absmax {name} W{wl.W.shape}")
+    W, _, _, _ = upload(wl)
+    got = lh.lh_absmax(W).cpu().numpy()
+    ref = oracle.absmax(wl.W_f64()).astype(np.float32)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_absmax_ragged_and_unaligned():
+    r = np.random.default_rng(1)
+    a = r.normal(0, 1, 3 * 1001).astype(np.float32)
+    a[1500] = -77.0
+    note("absmax ragged fp32 3x1001")
+    t = torch.from_numpy(a).to(DEV).view(3, 1, 1001)          # 3 groups of 1001 elements
+    np.testing.assert_array_equal(lh.lh_absmax(t).cpu().numpy(), np.abs(a.reshape(3, 1001)).max(1))
+    b = synth.bf16_bits_from_f32(r.normal(0, 1, 2 * 37).astype(np.float32))
+    tb = torch.from_numpy(b).view(torch.bfloat16).to(DEV).view(2, 1, 37)
+    ref = np.abs(synth.f32_from_bf16_bits(b).reshape(2, 37)).max(1)
+    np.testing.assert_array_equal(lh.lh_absmax(tb).cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------------------------ accumulation
+@pytest.mark.parametrize("name", ["c1", "c2", "c4", "c5"])
+def test_accumulate_h_and_imp(name):
+    wl = synth.make(name, **SMALL[name])
+    note(f"accumulate {name} X{wl.X.shape} groups={wl.n_groups}")
+    _, X, _, off = upload(wl)
+    H, imp = lh.lh_accumulate(X, offsets=off, want_imp=True)
+    H_ref, imp_ref = oracle.accumulate(wl.X_f64(), wl.offsets, want_imp=True)
+    assert_h_close(H.cpu().numpy(), H_ref)
+    assert_imp_close(imp.cpu().numpy(), imp_ref)
+
+
+def test_accumulate_deterministic_and_only_imp():
+    wl = synth.make("c2", cout=16, cin=128, rows=1000)
+    note("accumulate determinism c2 rows=1000")
+    _, X, _, _ = upload(wl)
+    H1, i1 = lh.lh_accumulate(X, want_imp=True)
+    H2, i2 = lh.lh_accumulate(X, want_imp=True)
+    _, i3 = lh.lh_accumulate(X, want_h=False, want_imp=True)
+    assert torch.equal(H1, H2) and torch.equal(i1, i2) and torch.equal(i1, i3)
+
+
+def test_accumulate_empty_groups_and_beta():
+    r = np.random.default_rng(5)
+    rows, cin = 700, 48
+    X = synth.bf16_bits_from_f32(r.normal(0, 1, (rows, cin)).astype(np.float32))
+    off = np.array([0, 0, 5, 5, 300, 301, 700, 700], dtype=np.int64)   # empty, tiny, spans tiles
+    note("accumulate groups with empty/one-row/tile-spanning members, beta streaming")
+    Xd = torch.from_numpy(X).view(torch.bfloat16).to(DEV)
+    offd = torch.from_numpy(off).to(DEV)
+    Xf = synth.f32_from_bf16_bits(X).astype(np.float64)
+    H_ref, imp_ref = oracle.accumulate(Xf, off, want_imp=True)
+    H, imp = lh.lh_accumulate(Xd, offsets=offd, want_imp=True)
+    assert_h_close(H.cpu().numpy(), H_ref)
+    assert_imp_close(imp.cpu().numpy(), imp_ref)
+    # streaming: second call with beta = 0.5 on the same data
+    lh.lh_accumulate(Xd, H=H, imp=imp, offsets=offd, beta=0.5)
+    H2_ref, imp2_ref = oracle.accumulate(Xf, off, beta=0.5, H_prev=H_ref, imp_prev=imp_ref, want_imp=True)
+    assert_h_close(H.cpu().numpy(), H2_ref)
+    assert_imp_close(imp.cpu().numpy(), imp2_ref)
+
+
+def test_accumulate_zero_rows():
+    note("accumulate rows=0")
+    X = torch.empty((0, 32), dtype=torch.bfloat16, device=DEV)
+    H, imp = lh.lh_accumulate(X, want_imp=True)
+    assert torch.count_nonzero(H) == 0 and torch.count_nonzero(imp) == 0
+
+
+@pytest.mark.parametrize("name", ["c3", "c1"])
+def test_accumulate_act_aware(name):
+    if name == "c1":      # fp32 act-aware: X_q from a perturbation of X
+        wl = synth.make("c1")
+        r = np.random.default_rng(7)
+        Xq = (wl.X + 0.05 * r.standard_normal(wl.X.shape)).astype(np.float32)
+        wl.Xq = Xq
+    else:
+        wl = synth.make(name, **SMALL[name])
+    note(f"act-aware accumulate {name} X{wl.X.shape}")
+    _, X, Xq, off = upload(wl)
+    H, P = lh.lh_accumulate_act_aware(X, Xq, offsets=off)
+    H_ref, P_ref = oracle.accumulate_act_aware(wl.X_f64(), wl.Xq_f64(), wl.offsets)
+    R_ref = cross_gram(wl.X_f64(), wl.Xq_f64(), wl.offsets)
+    assert_h_close(H.cpu().numpy(), H_ref)
+    assert_p_close(P.cpu().numpy(), P_ref, H_ref, R_ref)
+
+
+# ------------------------------------------------------------------------------------ sweep
+def _oracle_h32(wl):
+    """fp32 Hessians computed by the oracle: the identical input both sweeps receive."""
+    if wl.mode == "act":
+        H, P = oracle.accumulate_act_aware(wl.X_f64(), wl.Xq_f64(), wl.offsets)
+        return H.astype(np.float32), P.astype(np.float32)
+    H, _ = oracle.accumulate(wl.X_f64(), wl.offsets)
+    return H.astype(np.float32), None
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_sweep_full_parity(name):
+    wl = synth.make(name, **SMALL[name])
+    note(f"sweep {name} W{wl.W.shape} mode={wl.mode}")
+    W, _, _, _ = upload(wl)
+    H32, P32 = _oracle_h32(wl)
+    amax = oracle.absmax(wl.W_f64()).astype(np.float32)
+    code, fp4, loss = lh.lh_scale_sweep(W, torch.from_numpy(amax).to(DEV), torch.from_numpy(H32).to(DEV),
+                                        None if P32 is None else torch.from_numpy(P32).to(DEV))
+    res = oracle.sweep(wl.W_f64(), amax, H32, P32)
+    n_ex = assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+    note(f"  exempt near-ties: {n_ex} of {code.numel()}")
+
+
+def test_sweep_diag_parity():
+    wl = synth.make("c4", **SMALL["c4"])
+    note(f"diag sweep c4 W{wl.W.shape}")
+    W, _, _, _ = upload(wl)
+    _, imp = oracle.accumulate(wl.X_f64(), wl.offsets, want_h=False, want_imp=True)
+    imp32 = imp.astype(np.float32)
+    amax = oracle.absmax(wl.W_f64()).astype(np.float32)
+    code, fp4, loss = lh.lh_scale_sweep_diag(W, torch.from_numpy(amax).to(DEV), torch.from_numpy(imp32).to(DEV))
+    res = oracle.sweep_diag(wl.W_f64(), amax, imp32)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
+def test_sweep_degenerate_blocks():
+    """All-zero blocks, zero-trace Hessians, an all-zero matrix (amax 0), ragged shapes."""
+    r = np.random.default_rng(3)
+    G, cout, cin = 3, 21, 48
+    W = r.normal(0, 0.02, (G, cout, cin)).astype(np.float32)
+    W[0, 3, 16:32] = 0.0                      # zero block
+    W[1, :, :] *= 1e3                         # large weights
+    W[2] = 0.0                                # amax 0 group
+    W[0, 5, 0] = -0.0
+    A = r.standard_normal((G, cin // 16, 16, 16)).astype(np.float32)
+    H = np.einsum("gnij,gnkj->gnik", A, A).astype(np.float32) / 16
+    H[0, 1] = 0.0                             # zero trace: plain MSE
+    P = (0.1 * r.standard_normal(H.shape)).astype(np.float32)
+    amax = oracle.absmax(W).astype(np.float32)
+    note("sweep degenerate cases fp32 G=3 cout=21 cin=48")
+    args = [torch.from_numpy(x).to(DEV) for x in (W, amax, H)]
+    for with_p in (False, True):
+        code, fp4, loss = lh.lh_scale_sweep(*args, torch.from_numpy(P).to(DEV) if with_p else None)
+        res = oracle.sweep(W.astype(np.float64), amax, H, P if with_p else None)
+        assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+        assert np.all(code.cpu().numpy()[2] == 1) and np.all(fp4.cpu().numpy()[2] == 0)
+    imp = np.abs(r.standard_normal((G, cin))).astype(np.float32)
+    imp[1, 16:32] = 0.0
+    code, fp4, loss = lh.lh_scale_sweep_diag(args[0], args[1], torch.from_numpy(imp).to(DEV))
+    res = oracle.sweep_diag(W.astype(np.float64), amax, imp)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
+def test_sweep_exact_midpoint_ties():
+    """Weights placed exactly on E2M1 midpoints of some candidate scale must round like the oracle."""
+    r = np.random.default_rng(4)
+    cout, cin = 64, 32
+    amax = np.float32(0.0875)
+    g = oracle.global_scale(amax)
+    s = oracle.candidate_scales(g)
+    W = r.normal(0, 0.02, (1, cout, cin)).astype(np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for c in range(cout):
+        for j in range(0, cin, 3):
+            k = r.integers(90, 126)
+            v = np.float32(mids[r.integers(7)] * s[k])      # nearest fp32 to the midpoint
+            W[0, c, j] = v if r.random() < 0.5 else np.nextafter(v, np.float32(1))
+    W[0, 0, 0] = amax
+    H = np.broadcast_to(np.eye(16, dtype=np.float32) * 2.0, (1, cin // 16, 16, 16)).copy()
+    note("sweep exact midpoint ties")
+    code, fp4, loss = lh.lh_scale_sweep(torch.from_numpy(W).to(DEV), torch.from_numpy(np.array([amax])).to(DEV),
+                                        torch.from_numpy(H).to(DEV))
+    res = oracle.sweep(W.astype(np.float64), np.array([amax]), H)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
+def test_sweep_deterministic():
+    wl = synth.make("c2", cout=100, cin=64, rows=300)
+    note("sweep determinism")
+    W, X, _, _ = upload(wl)
+    amax = lh.lh_absmax(W)
+    H, _ = lh.lh_accumulate(X)
+    a = lh.lh_scale_sweep(W, amax, H)
+    b = lh.lh_scale_sweep(W, amax, H)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
+                           y.view(torch.uint8) if y.dtype != torch.uint8 else y)
+
+
+# ------------------------------------------------------------------------------------ end to end
+@pytest.mark.parametrize("name", list(SMALL))
+def test_end_to_end(name):
+    """absmax -> accumulate -> sweep entirely on the GPU, against the oracle's own float64 path."""
+    wl = synth.make(name, **SMALL[name])
+    note(f"end-to-end {name}")
+    W, X, Xq, off = upload(wl)
+    amax = lh.lh_absmax(W)
+    Wo = wl.W_f64()
+    a_ref = oracle.absmax(Wo)
+    if wl.mode == "diag":
+        _, imp = lh.lh_accumulate(X, offsets=off, want_h=False, want_imp=True)
+        code, fp4, loss = lh.lh_scale_sweep_diag(W, amax, imp)
+        _, imp_ref = oracle.accumulate(wl.X_f64(), wl.offsets, want_h=False, want_imp=True)
+        res = oracle.sweep_diag(Wo, a_ref, imp_ref)
+    elif wl.mode == "act":
+        H, P = lh.lh_accumulate_act_aware(X, Xq, offsets=off)
+        code, fp4, loss = lh.lh_scale_sweep(W, amax, H, P)
+        H_ref, P_ref = oracle.accumulate_act_aware(wl.X_f64(), wl.Xq_f64(), wl.offsets)
+        res = oracle.sweep(Wo, a_ref, H_ref, P_ref)
+    else:
+        H, _ = lh.lh_accumulate(X, offsets=off)
+        code, fp4, loss = lh.lh_scale_sweep(W, amax, H)
+        H_ref, _ = oracle.accumulate(wl.X_f64(), wl.offsets)
+        res = oracle.sweep(Wo, a_ref, H_ref)
+    # each side used its own Hessian; near-ties within 1e-6 are exempt as everywhere
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), None, res)
