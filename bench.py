@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--cpu-sample-blocks", type=int, default=24576,
                    help="blocks of the oracle's sweep timed for the CPU baseline")
     p.add_argument("--rotate-gib", type=float, default=1.0)
+    p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                   help="only run a plain elementwise copy (torch.neg) of MIB MiB, 5 times, for "
+                        "calibrating HBM byte counters, and exit")
     return p.parse_args()
 
 
@@ -110,6 +113,15 @@ def main():
     import nvfp4_scale_calibration_lh_amd as lh
 
     dev = torch.device("cuda:0")
+    if args.copy_calib:
+        n = args.copy_calib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4, "launches": 5}))
+        return
     wl = synth.make(args.config)
     G, cout, cin, rows = wl.n_groups, wl.cout, wl.cin, wl.rows
     nb = cin // 16

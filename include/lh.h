@@ -12,6 +12,7 @@
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers, row-major and densely packed, owned by the caller.
+ *     X, Xq and W must be 16-byte aligned (PyTorch allocations are); fp4 2-byte aligned.
  *     Inputs are never modified.  Outputs are fully overwritten (H, P and imp are read first
  *     only when beta != 0).
  *   - X is [rows, cin] (tokens x input channels, as a linear layer sees its input); W is

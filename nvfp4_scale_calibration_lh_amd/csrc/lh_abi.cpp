@@ -230,6 +230,8 @@ lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int6
   int dev = -1;
   st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {H, "H"}, {P, "P"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
   if (st != LH_OK) return st;
+  if ((st = check_aligned(W, "W")) != LH_OK) return st;
+  if (fp4 && (reinterpret_cast<uintptr_t>(fp4) % 2) != 0) return fail(LH_ERR_INVALID_ARGUMENT, "fp4 must be 2-byte aligned");
   DeviceGuard guard;
   if ((st = guard.enter(dev)) != LH_OK) return st;
   hipError_t e = lh::launch_sweep(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, H, P,
@@ -249,6 +251,7 @@ lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups,
   int dev = -1;
   st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {imp, "imp"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
   if (st != LH_OK) return st;
+  if ((st = check_aligned(W, "W")) != LH_OK) return st;
   DeviceGuard guard;
   if ((st = guard.enter(dev)) != LH_OK) return st;
   hipError_t e = lh::launch_sweep_diag(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, imp,

@@ -11,24 +11,29 @@
 // and the block keeps the argmin (lowest code on ties).
 //
 // MI355X design
-//  * Full form: one wave per block, 16 candidates per MFMA tile (8 tiles = 128 lanes-candidates,
-//    126 used).  Lane l owns candidate l%16 of the tile and elements 4*(l/16)..+3.  The lane
-//    quantizes its 4 elements (r = w * (1/s) in fp32, then the gfx950 FP4 convert, which rounds
-//    to nearest-even on the E2M1 grid and saturates at 6, and the FP4->fp32 convert back), forms
+//  * Full form: one wave per block, 16 candidates per MFMA tile (8 tiles cover the 126 codes).
+//    Lane l owns candidate l%16 of the tile and elements 4*(l/16)..+3.  The lane quantizes its 4
+//    elements (r = w * (1/s) in fp32, then the gfx950 FP4 convert, which rounds to nearest-even
+//    on the E2M1 grid and saturates at 6, and the FP4->fp32 convert back), forms
 //    e = fma(q, s, -w), and four chained v_mfma_f32_16x16x4_f32 compute H e + 2b for the 16
-//    candidates (H_n is the A operand, resident in registers for the whole column; the K index is
-//    permuted so that each lane's output rows are exactly its own 4 elements).  The quadratic
-//    form and an error bound are reduced across the 4 lane groups with two permlane swaps.
-//    b = P_n w and |P_n||w| come from the same MFMA once per 16-row tile.
-//  * Diagonal form: VALU only (no contraction to map onto MFMA); lane l scores candidates l+1 and
-//    l+65 over all 16 elements, so no cross-lane reduction is needed until the argmin.
+//    candidates (H_n is the A operand, resident in registers for the whole column; the K index
+//    is permuted so that each lane's output rows are exactly its own 4 elements).  The quadratic
+//    form and an error bound are reduced across the 4 lane groups with permlane swaps; the
+//    argmin over the 16 candidate lanes uses DPP row rotations.  Quantization of the next tile
+//    is issued before the current tile's MFMA result is consumed.  b = P_n w and |P_n||w| come
+//    from the same MFMA shape once per 16-row tile.
+//  * Diagonal form: VALU only (there is no contraction to map onto MFMA); lane l scores
+//    candidates l+1 and l+65 over all 16 elements, whose weights are wave-uniform.
 //  * Exactness.  The float32 pass is a filter: each candidate carries a rigorous bound c*A_k on
 //    its rounding error (A_k = (sum|e_i| dmax_i)^2 + 2|e|^T(|P||w|), dmax_i^2 = max_j |H_ij|, or
 //    L_k itself in the diagonal form).  If exactly one candidate can be the minimum, it is the
-//    exact argmin.  Otherwise -- or when some |w_i|/s_k lies within a few ulps of an E2M1 rounding
-//    midpoint, where the fp32 quotient could round the other way (detected once per block by
-//    testing whether |w_i|/(m_j g) is near an E4M3 value) -- the block is re-scored in float64
-//    with exact quotient rounding.  The result is the argmin of the float64 objective.
+//    exact argmin; otherwise the block's code is left at 0 and a second kernel re-scores it in
+//    float64 with exact quotient rounding.  The fp32 quotient w*(1/s) can fall on the wrong side
+//    of an E2M1 rounding midpoint m only when |w|/s_k is within a few ulps of m, i.e. when
+//    |w|/(m g) is within a few ulps of an E4M3 value; once per block every (element, midpoint)
+//    pair is tested, and for a flagged pair the one affected candidate gets the exact decision
+//    (the sign of fma(m, s_k, -|w|)) in place of its fp32 quotient.  The result is the argmin of
+//    the float64 objective.
 #include "lh_internal.hpp"
 
 namespace lh {
@@ -38,7 +43,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per workgroup; wave w takes block column 4*bx + w
-constexpr int kRowsPerWave = 64;     // rows (blocks of one column) per wave
+constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
 constexpr float kErrC = 0x1p-17f;    // filter error bound factor (about 3x the derived bound)
 constexpr int kNearUlps = 16;        // midpoint proximity test, in ulps of |w|/(m g)
 
@@ -53,8 +58,13 @@ __device__ inline double e4m3_value(int k) {
 
 __device__ inline float global_scale(float amax) { return (float)((double)amax / 2688.0); }
 __device__ inline float cand_scale(int k, float g) { return (float)(e4m3_value(k) * (double)g); }
+__device__ inline float inv_scale(float s) { return s > 0.0f ? (float)(1.0 / (double)s) : 0.0f; }
+// The float32 filter is used only where scales and quotients stay normal and finite.
+__device__ inline bool filter_ok(float g) { return g >= 0x1p-116f && g <= 0x1p+100f; }
 
 // Exact E2M1 grid index of the quotient r = |w|/s given as float64 (ties to the even index).
+// |w| and m*s have at most 27 significant bits, so a float64 quotient is on the same side of
+// every midpoint m as the exact one, and equal to it only when the exact quotient is.
 __device__ inline int e2m1_index_exact(double r) {
   return (int)(r > 0.25) + (int)(r >= 0.75) + (int)(r > 1.25) + (int)(r >= 1.75) + (int)(r > 2.5) +
          (int)(r >= 3.5) + (int)(r > 5.0);
@@ -73,7 +83,8 @@ __device__ inline double exact_err(float wf, float s, int* nib) {
   return (wf < 0.0f ? -mag : mag) - w;
 }
 
-// True when |w|/s_k may lie within a few ulps of an E2M1 midpoint for some candidate k.
+// True when |w|/s_k may lie within a few ulps of an E2M1 midpoint m for some candidate k:
+// |w|/(m g) is then within a few ulps of an E4M3 value (3 significant bits).
 __device__ inline bool near_midpoint(float aw, float inv_mg) {
   const float z = aw * inv_mg;
   if (!(z >= 0x1p-10f && z <= 480.0f)) return false;
@@ -81,32 +92,162 @@ __device__ inline bool near_midpoint(float aw, float inv_mg) {
   return t < ((unsigned)(2 * kNearUlps) << 12);
 }
 
+// For a flagged (element, midpoint m) pair with z = |w|/(m g): the candidate k whose scale puts
+// |w|/s_k next to m (0 if there is none), i.e. the E4M3 value nearest z.
+__device__ inline int near_candidate(float z) {
+  if (z < 0x1p-6f) {
+    const int m = (int)rintf(z * 512.0f);             // subnormal E4M3: m * 2^-9 (m = 8 is 2^-6)
+    return (m >= 1 && m <= 8) ? m : 0;
+  }
+  const unsigned b = (__float_as_uint(z) + 0x80000u) & 0xFFF00000u;   // round to 3 mantissa bits
+  const int e = (int)(b >> 23) - 127, mant = (int)((b >> 20) & 7u);
+  const int k = ((e + 7) << 3) | mant;
+  return (k >= 8 && k <= 126) ? k : 0;
+}
+
+// Quotient to hand the FP4 convert for |w| near m*s: it lands on the side of the midpoint where
+// the exact quotient |w|/s lies (sign of the exactly rounded fma), or exactly on m for a true tie,
+// which the convert then rounds to the even grid index like the exact rule.
+__device__ inline float exact_side(float w, float m, float s) {
+  const float aw = fabsf(w);
+  const float d = fmaf(m, s, -aw);
+  const float r = d < 0.0f ? m * 1.0009765625f : (d > 0.0f ? m * 0.9990234375f : m);
+  return w < 0.0f ? -r : r;
+}
+
+// Per-lane description of this lane's flagged pair p (element p/7, midpoint p%7): the affected
+// candidate (0 if none) and the quotient to use for it.
+__device__ inline void pair_override(bool near, int p, float w_el, float gsc, int* kv, float* rv) {
+  *kv = 0;
+  *rv = 0.0f;
+  if (!near) return;
+  const float m = kMid[p % 7];
+  const float z = fabsf(w_el) * (float)(1.0 / ((double)m * (double)gsc));
+  const int k = near_candidate(z);
+  if (k == 0) return;
+  *kv = k;
+  *rv = exact_side(w_el, m, cand_scale(k, gsc));
+}
+
+// Apply the overrides of one ballot mask (pairs pbase + bit) to the quotients r[0..3] of a lane
+// that holds candidate (16*tau + i + 1) and elements 4*gg..4*gg+3; with tau < 0 the lane's
+// candidate is kmatch instead.
+__device__ inline void apply_overrides(unsigned long long m, int pbase, int kv, float rv, int tau,
+                                       int kmatch, int i, int gg, float r[4]) {
+  while (m) {
+    const int b = __builtin_ctzll(m);
+    m &= m - 1;
+    const int k = __builtin_amdgcn_readlane(kv, b);
+    if (k == 0) continue;
+    if (tau >= 0 ? (((k - 1) >> 4) != tau) : (k != kmatch)) continue;
+    const int el = (b + pbase) / 7;
+    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), b));
+    const bool me = (gg == (el >> 2)) && (tau < 0 || i == ((k - 1) & 15));
+    const int t = el & 3;
+    r[0] = (me && t == 0) ? v : r[0];
+    r[1] = (me && t == 1) ? v : r[1];
+    r[2] = (me && t == 2) ? v : r[2];
+    r[3] = (me && t == 3) ? v : r[3];
+  }
+}
+
+// Overrides for element el of candidate kmatch (used when emitting the winner's codes).
+__device__ inline float override_for(unsigned long long m, int pbase, int kv, float rv, int kmatch,
+                                     int el, float r) {
+  while (m) {
+    const int b = __builtin_ctzll(m);
+    m &= m - 1;
+    const int k = __builtin_amdgcn_readlane(kv, b);
+    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), b));
+    if (k != 0 && k == kmatch && (b + pbase) / 7 == el) r = v;
+  }
+  return r;
+}
+
 __device__ inline float load_w(const void* W, bool bf16, int64_t idx) {
   if (bf16) return __uint_as_float((unsigned)((const unsigned short*)W)[idx] << 16);
   return ((const float*)W)[idx];
 }
 
+template <int CTRL>
+__device__ inline float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// Minimum over the 16 lanes of each DPP row (row_ror by 8, 4, 2, 1); every lane gets the result.
+__device__ inline float row_min(float v) {
+  v = fminf(v, dppf<0x128>(v));
+  v = fminf(v, dppf<0x124>(v));
+  v = fminf(v, dppf<0x122>(v));
+  v = fminf(v, dppf<0x121>(v));
+  return v;
+}
+__device__ inline int row_min_i(int v) {
+  v = min(v, dppi<0x128>(v));
+  v = min(v, dppi<0x124>(v));
+  v = min(v, dppi<0x122>(v));
+  v = min(v, dppi<0x121>(v));
+  return v;
+}
+// Minimum over all 64 lanes.
+__device__ inline float wave_min(float v) {
+  v = row_min(v);
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline int wave_min_i(int v) {
+  v = row_min_i(v);
+  auto a = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = min((int)a[0], (int)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return min((int)b[0], (int)b[1]);
+}
+
+// Lowest (loss, code) over the wave in float64 (exact re-scoring).
+__device__ inline void wave_argmin_d(double& L, int& k) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const double oL = __shfl_xor(L, o, 64);
+    const int oK = __shfl_xor(k, o, 64);
+    if (oL < L || (oL == L && oK < k)) { L = oL; k = oK; }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
-// Full-Hessian sweep
+// Full-Hessian sweep: float32 filter
 // ------------------------------------------------------------------------------------------
-struct WaveLds {
+struct FullLds {
   float H[256];
   float P[256];
   float w[16][16];     // current 16-row tile: w[row][elem]
   float b2[16][16];    // 2 * (P w)[row][elem]
   float pw2[16][16];   // 2 * (|P| |w|)[row][elem]
-  double wide[16];     // exact-path exchange
-  int nib[16];
 };
+
+// Quantization error of the lane's 4 elements for scale s, from the quotients r = w / s.
+__device__ inline void quant4(const float w[4], const float r[4], float s, float e[4]) {
+  unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
+  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, r[2], r[3], 1.0f, 1);
+  const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
+  const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 1);
+  e[0] = fmaf(q01[0], s, -w[0]);
+  e[1] = fmaf(q01[1], s, -w[1]);
+  e[2] = fmaf(q23[0], s, -w[2]);
+  e[3] = fmaf(q23[1], s, -w[3]);
+}
 
 template <bool BF16, bool COUPLED>
 __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
     uint8_t* __restrict__ fp4, float* __restrict__ loss) {
-  __shared__ WaveLds lds_all[kWaves];
+  __shared__ FullLds lds_all[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  WaveLds& L = lds_all[wave];
+  FullLds& L = lds_all[wave];
   const int i = lane & 15, gg = lane >> 4;
   const int64_t nb = cin / 16;
   const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
@@ -115,7 +256,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
   if (n >= nb || c_begin >= cout) return;          // whole wave leaves; no workgroup barriers below
   const int64_t c_end = min(cout, c_begin + kRowsPerWave);
 
-  // ---- column set-up: H_n (and P_n) into LDS and registers
+  // ---- column set-up: H_n (and P_n) through LDS into registers
   const float* Hn = Hg + (g * nb + n) * 256;
   for (int q = 0; q < 4; ++q) L.H[lane * 4 + q] = Hn[lane * 4 + q];
   if (COUPLED) {
@@ -133,32 +274,31 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
   for (int t = 0; t < 4; ++t) {
     const int col = 4 * gg + t;
     a[t] = dead ? (i == col ? 1.0f : 0.0f) : L.H[i * 16 + col];
-    float mx = 0.0f;
-    if (dead) mx = 1.0f;
-    else
+    float mx = 1.0f;
+    if (!dead) {
+      mx = 0.0f;
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(fabsf(L.H[col * 16 + j]), fabsf(L.H[j * 16 + col])));
-    dm[t] = sqrtf(mx) * 1.0000002f;               // sqrt rounding margin
+    }
+    dm[t] = sqrtf(mx) * 1.0000002f;               // |H_ij| <= dm_i dm_j, with sqrt rounding margin
     pv[t] = coupled ? L.P[i * 16 + col] : 0.0f;
     pa[t] = fabsf(pv[t]);
   }
 
-  // ---- candidate scales for this lane's 8 tiles
+  // ---- candidate scales for this lane's 8 tiles (codes 127, 128 repeat 126 and are masked)
   const float gsc = global_scale(amax[g]);
-  const bool force_exact = !(gsc >= 0x1p-116f) || !(gsc <= 0x1p+100f);
+  const bool fast = filter_ok(gsc);
   float s[8], is[8];
-  bool valid[8];
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau) {
-    int k = 16 * tau + i + 1;
-    valid[tau] = k <= 126;
-    if (!valid[tau]) k = 126;
+    const int k = min(16 * tau + i + 1, 126);
     s[tau] = cand_scale(k, gsc);
-    is[tau] = s[tau] > 0.0f ? (float)(1.0 / (double)s[tau]) : 0.0f;
+    is[tau] = inv_scale(s[tau]);
   }
-  // midpoint proximity constants: this lane tests pairs p = lane and lane + 64 of (elem, midpoint)
+  // midpoint proximity: this lane tests pairs p = lane and lane + 64 of (element, midpoint)
   const int p0 = lane, p1 = lane + 64;
-  const float img0 = (float)(1.0 / ((double)kMid[p0 % 7] * (double)gsc));
-  const float img1 = p1 < 112 ? (float)(1.0 / ((double)kMid[p1 % 7] * (double)gsc)) : 0.0f;
+  const float img0 = fast ? (float)(1.0 / ((double)kMid[p0 % 7] * (double)gsc)) : 0.0f;
+  const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)kMid[p1 % 7] * (double)gsc)) : 0.0f;
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
     // ---- 16-row tile: w, b = P w and |P||w| (MFMA, K index = element 4*gg + t)
@@ -168,7 +308,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       wt[t] = row_on ? load_w(W, BF16, (g * cout + crow) * cin + n * 16 + 4 * gg + t) : 0.0f;
-    v4f bt = {0.f, 0.f, 0.f, 0.f}, pwt = {0.f, 0.f, 0.f, 0.f};
+    v4f bt = zero4, pwt = zero4;
     if (coupled) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -180,8 +320,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       L.w[i][4 * gg + t] = wt[t];
-      L.b2[i][4 * gg + t] = 2.0f * bt[t];          // lane holds rows 4gg+t of column (row) i
-      L.pw2[i][4 * gg + t] = 2.0f * pwt[t];
+      if (COUPLED) {
+        L.b2[i][4 * gg + t] = 2.0f * bt[t];          // lane holds elements 4gg+t of row i
+        L.pw2[i][4 * gg + t] = 2.0f * pwt[t];
+      }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -189,145 +331,125 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
     const int rows_here = (int)min((int64_t)16, c_end - c0);
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
-      float w[4], twob[4], pw2[4];
+      const int64_t oblk = (g * cout + c) * nb + n;
+      float w[4], pw2[4];
+      v4f cinit = zero4;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         w[t] = L.w[rr][4 * gg + t];
-        twob[t] = L.b2[rr][4 * gg + t];
-        pw2[t] = L.pw2[rr][4 * gg + t];
+        if (COUPLED) {
+          cinit[t] = coupled ? L.b2[rr][4 * gg + t] : 0.0f;
+          pw2[t] = coupled ? L.pw2[rr][4 * gg + t] : 0.0f;
+        }
       }
-      // midpoint proximity (exact-path trigger)
-      bool near = near_midpoint(fabsf(L.w[rr][p0 / 7]), img0);
-      if (p1 < 112) near = near || near_midpoint(fabsf(L.w[rr][p1 / 7]), img1);
-      const bool flag = __ballot(near) != 0ull || force_exact;
-
-      float bestL = __builtin_inff(), minUB = __builtin_inff(), LB[8];
-      int bestK = 127;
-      if (!flag) {
-        const v4f cinit = {twob[0], twob[1], twob[2], twob[3]};
-#pragma unroll
-        for (int tau = 0; tau < 8; ++tau) {
-          const float r0 = w[0] * is[tau], r1 = w[1] * is[tau], r2 = w[2] * is[tau], r3 = w[3] * is[tau];
-          unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r0, r1, 1.0f, 0);
-          pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, r2, r3, 1.0f, 1);
-          const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
-          const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 1);
-          const float e0 = fmaf(q01[0], s[tau], -w[0]);
-          const float e1 = fmaf(q01[1], s[tau], -w[1]);
-          const float e2 = fmaf(q23[0], s[tau], -w[2]);
-          const float e3 = fmaf(q23[1], s[tau], -w[3]);
-          v4f D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], e0, cinit, 0, 0, 0);
-          D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], e1, D, 0, 0, 0);
-          D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], e2, D, 0, 0, 0);
-          D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], e3, D, 0, 0, 0);
-          float lp = e0 * D[0];
-          lp = fmaf(e1, D[1], lp);
-          lp = fmaf(e2, D[2], lp);
-          lp = fmaf(e3, D[3], lp);
-          float sp = fabsf(e0) * dm[0];
-          sp = fmaf(fabsf(e1), dm[1], sp);
-          sp = fmaf(fabsf(e2), dm[2], sp);
-          sp = fmaf(fabsf(e3), dm[3], sp);
-          float ap = 4.0f * sp * sp;
-          if (coupled) {
-            float bp = fabsf(e0) * pw2[0];
-            bp = fmaf(fabsf(e1), pw2[1], bp);
-            bp = fmaf(fabsf(e2), pw2[2], bp);
-            bp = fmaf(fabsf(e3), pw2[3], bp);
-            ap += bp;
-          }
-          // reduce lp and ap over the 4 lane groups: lanes 0-31 end with L, 32-63 with A
-          auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(ap), false, false);
-          float z = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-          auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
-          z = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-          auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
-          const float Lk = __uint_as_float(u[0]);
-          const float Ak = __uint_as_float(u[1]);
-          if (valid[tau]) {
-            LB[tau] = fmaf(-kErrC, Ak, Lk);
-            minUB = fminf(minUB, fmaf(kErrC, Ak, Lk));
-            if (Lk < bestL) { bestL = Lk; bestK = 16 * tau + i + 1; }
-          } else {
-            LB[tau] = __builtin_inff();
-          }
-        }
-        // argmin and min upper bound over the 16 candidate lanes of a row
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float oL = __shfl_xor(bestL, o, 64);
-          const int oK = __shfl_xor(bestK, o, 64);
-          if (oL < bestL || (oL == bestL && oK < bestK)) { bestL = oL; bestK = oK; }
-          minUB = fminf(minUB, __shfl_xor(minUB, o, 64));
-        }
-        int cnt = 0;
-#pragma unroll
-        for (int tau = 0; tau < 8; ++tau) cnt += __popcll(__ballot(LB[tau] <= minUB) & 0xFFFFull);
-        if (cnt != 1) bestK = -1;
-      } else {
-        bestK = -1;
+      // quotients within a few ulps of an E2M1 midpoint are decided exactly (fma sign test)
+      const float wp0 = L.w[rr][p0 / 7], wp1 = L.w[rr][(p1 < 112 ? p1 : 0) / 7];
+      const bool near0 = near_midpoint(fabsf(wp0), img0);
+      const bool near1 = p1 < 112 && near_midpoint(fabsf(wp1), img1);
+      const unsigned long long m0 = __ballot(near0), m1 = __ballot(near1);
+      if (!fast) {
+        if (lane == 0) code[oblk] = 0;              // resolved by the float64 pass
+        continue;
       }
+      const bool has_ovr = (m0 | m1) != 0ull;
+      int kv0 = 0, kv1 = 0;
+      float rv0 = 0.0f, rv1 = 0.0f;
+      if (has_ovr) {
+        pair_override(near0, p0, wp0, gsc, &kv0, &rv0);
+        pair_override(near1, p1, wp1, gsc, &kv1, &rv1);
+      }
+      auto quotients = [&](int tau, float r[4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) r[t] = w[t] * is[tau];
+        if (has_ovr) {
+          apply_overrides(m0, 0, kv0, rv0, tau, 0, i, gg, r);
+          apply_overrides(m1, 64, kv1, rv1, tau, 0, i, gg, r);
+        }
+      };
 
-      const int64_t oblk = (g * cout + c) * nb + n;
-      if (bestK > 0) {
-        // unique float32 winner: emit its codes
-        const float sw = cand_scale(bestK, gsc);
-        const float iw = (float)(1.0 / (double)sw);
-        unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, w[0] * iw, w[1] * iw, 1.0f, 0);
-        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, w[2] * iw, w[3] * iw, 1.0f, 1);
-        unsigned nb4 = pk & 0x7777u;                                   // magnitudes
-        nb4 |= (w[0] < 0.0f ? 0x8u : 0u) | (w[1] < 0.0f ? 0x80u : 0u) |
-               (w[2] < 0.0f ? 0x800u : 0u) | (w[3] < 0.0f ? 0x8000u : 0u);
-        if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
-        if (lane == 0) {
-          code[oblk] = (uint8_t)bestK;
-          if (loss) loss[oblk] = bestL;
+      float Lk[8], Ak[8];
+      float e[4], en[4], rq[4];
+      quotients(0, rq);
+      quant4(w, rq, s[0], e);
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) {
+        v4f D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], e[0], cinit, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], e[1], D, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], e[2], D, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], e[3], D, 0, 0, 0);
+        if (tau < 7) {                                            // overlaps the MFMA chain
+          quotients(tau + 1, rq);
+          quant4(w, rq, s[tau + 1], en);
         }
-      } else {
-        // exact float64 re-scoring of all 126 candidates
-        double wd[16], bd[16];
-        for (int j = 0; j < 16; ++j) wd[j] = (double)L.w[rr][j];
-        for (int r2 = 0; r2 < 16; ++r2) {
-          double acc = 0.0;
-          if (coupled)
-            for (int j = 0; j < 16; ++j) acc += (double)L.P[r2 * 16 + j] * wd[j];
-          bd[r2] = acc;
+        float sp = fabsf(e[0]) * dm[0];
+        sp = fmaf(fabsf(e[1]), dm[1], sp);
+        sp = fmaf(fabsf(e[2]), dm[2], sp);
+        sp = fmaf(fabsf(e[3]), dm[3], sp);
+        float ap = 4.0f * sp * sp;
+        if (COUPLED) {
+          float bp = fabsf(e[0]) * pw2[0];
+          bp = fmaf(fabsf(e[1]), pw2[1], bp);
+          bp = fmaf(fabsf(e[2]), pw2[2], bp);
+          bp = fmaf(fabsf(e[3]), pw2[3], bp);
+          ap += bp;
         }
-        double bestD = __builtin_inf();
-        int bestKD = 127;
-        for (int h = 0; h < 2; ++h) {
-          const int k = lane + 1 + 64 * h;
-          if (k > 126) continue;
-          const float sk = cand_scale(k, gsc);
-          double e[16];
-          int dummy;
-          for (int j = 0; j < 16; ++j) e[j] = exact_err(L.w[rr][j], sk, &dummy);
-          double Lsum = 0.0;
-          for (int r2 = 0; r2 < 16; ++r2) {
-            double y = 0.0;
-            if (dead) y = e[r2];
-            else
-              for (int j = 0; j < 16; ++j) y += (double)L.H[r2 * 16 + j] * e[j];
-            Lsum += e[r2] * (y + 2.0 * bd[r2]);
-          }
-          if (Lsum < bestD) { bestD = Lsum; bestKD = k; }
+        float lp = e[0] * D[0];
+        lp = fmaf(e[1], D[1], lp);
+        lp = fmaf(e[2], D[2], lp);
+        lp = fmaf(e[3], D[3], lp);
+        // reduce lp and ap over the 4 lane groups: lanes 0-31 end with L, 32-63 with A; then
+        // spread both over the wave
+        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(ap), false, false);
+        float z = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+        z = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+        auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+        Lk[tau] = __uint_as_float(u[0]);
+        Ak[tau] = __uint_as_float(u[1]);
+        if (tau < 7) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) e[t] = en[t];
         }
-        for (int o = 1; o < 64; o <<= 1) {
-          const double oL = __shfl_xor(bestD, o, 64);
-          const int oK = __shfl_xor(bestKD, o, 64);
-          if (oL < bestD || (oL == bestD && oK < bestKD)) { bestD = oL; bestKD = oK; }
-        }
-        const float sw = cand_scale(bestKD, gsc);
-        if (lane < 8) {
-          int n0, n1;
-          exact_err(L.w[rr][2 * lane], sw, &n0);
-          exact_err(L.w[rr][2 * lane + 1], sw, &n1);
-          if (fp4) fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(n0 | (n1 << 4));
-        }
-        if (lane == 0) {
-          code[oblk] = (uint8_t)bestKD;
-          if (loss) loss[oblk] = (float)bestD;
-        }
+      }
+      if (i >= 14) Lk[7] = __builtin_inff();        // codes 127 and 128 do not exist
+
+      float bestL = __builtin_inff(), ub = __builtin_inff();
+      int bestK = 1 << 20;
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) {
+        ub = fminf(ub, fmaf(kErrC, Ak[tau], Lk[tau]));
+        if (Lk[tau] < bestL) { bestL = Lk[tau]; bestK = 16 * tau + i + 1; }
+      }
+      const float U = row_min(ub);
+      const float mL = row_min(bestL);
+      const int k_best = row_min_i(bestL == mL ? bestK : (1 << 20));
+      int cnt = 0;
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau)
+        cnt += __popcll(__ballot(fmaf(-kErrC, Ak[tau], Lk[tau]) <= U) & 0xFFFFull);
+      if (cnt != 1) {
+        if (lane == 0) code[oblk] = 0;              // several candidates can win: float64 pass
+        continue;
+      }
+      // unique winner: emit its codes
+      const float sw = cand_scale(k_best, gsc);
+      const float iw = inv_scale(sw);
+      float rw[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rw[t] = w[t] * iw;
+      if (has_ovr) {
+        apply_overrides(m0, 0, kv0, rv0, -1, k_best, i, gg, rw);
+        apply_overrides(m1, 64, kv1, rv1, -1, k_best, i, gg, rw);
+      }
+      unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, rw[0], rw[1], 1.0f, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, rw[2], rw[3], 1.0f, 1);
+      unsigned nb4 = pk & 0x7777u;                                   // magnitudes
+      nb4 |= (w[0] < 0.0f ? 0x8u : 0u) | (w[1] < 0.0f ? 0x80u : 0u) |
+             (w[2] < 0.0f ? 0x800u : 0u) | (w[3] < 0.0f ? 0x8000u : 0u);
+      if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
+      if (lane == 0) {
+        code[oblk] = (uint8_t)k_best;
+        if (loss) loss[oblk] = mL;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -335,8 +457,124 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
 }
 
 // ------------------------------------------------------------------------------------------
-// Diagonal (importance-weighted) sweep
+// Full-Hessian sweep: float64 re-scoring of the blocks the filter left at code 0
 // ------------------------------------------------------------------------------------------
+struct ExactLds {
+  float H[256];
+  float P[256];
+  float w[16];
+  double b[16];
+};
+
+template <bool BF16, bool COUPLED>
+__global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
+    const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
+    const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
+    uint8_t* __restrict__ fp4, float* __restrict__ loss) {
+  __shared__ ExactLds lds_all[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  ExactLds& L = lds_all[wave];
+  const int64_t nb = cin / 16;
+  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t g = blockIdx.z;
+  const int64_t c_begin = (int64_t)blockIdx.y * kRowsPerWave;
+  if (n >= nb || c_begin >= cout) return;
+  const int64_t c_end = min(cout, c_begin + kRowsPerWave);
+  // which of this wave's rows are pending (one row per lane)
+  const int64_t myc = c_begin + lane;
+  const bool pend = lane < kRowsPerWave && myc < c_end && code[(g * cout + myc) * nb + n] == 0;
+  unsigned long long todo = __ballot(pend);
+  if (!todo) return;
+
+  const float* Hn = Hg + (g * nb + n) * 256;
+  for (int q = 0; q < 4; ++q) L.H[lane * 4 + q] = Hn[lane * 4 + q];
+  if (COUPLED) {
+    const float* Pn = Pg + (g * nb + n) * 256;
+    for (int q = 0; q < 4; ++q) L.P[lane * 4 + q] = Pn[lane * 4 + q];
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  double tr = 0.0;
+  for (int j = 0; j < 16; ++j) tr += (double)L.H[j * 17];
+  const bool dead = (tr == 0.0);
+  const bool coupled = COUPLED && !dead;
+  const float gsc = global_scale(amax[g]);
+
+  while (todo) {
+    const int r = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int64_t c = c_begin + r;
+    const int64_t base = (g * cout + c) * cin + n * 16;
+    if (lane < 16) L.w[lane] = load_w(W, BF16, base + lane);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < 16) {
+      double acc = 0.0;
+      if (coupled)
+        for (int j = 0; j < 16; ++j) acc += (double)L.P[lane * 16 + j] * (double)L.w[j];
+      L.b[lane] = acc;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    double best = __builtin_inf();
+    int bestK = 1 << 20;
+    for (int h = 0; h < 2; ++h) {
+      const int k = lane + 1 + 64 * h;
+      if (k > 126) continue;
+      const float sk = cand_scale(k, gsc);
+      double e[16];
+      int nib;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) e[j] = exact_err(L.w[j], sk, &nib);
+      double Ls = 0.0;
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) {
+        double y = 0.0;
+        if (dead) {
+          y = e[r2];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) y += (double)L.H[r2 * 16 + j] * e[j];
+        }
+        Ls += e[r2] * (y + 2.0 * L.b[r2]);
+      }
+      if (Ls < best) { best = Ls; bestK = k; }
+    }
+    wave_argmin_d(best, bestK);
+    const float sw = cand_scale(bestK, gsc);
+    if (lane < 8 && fp4) {
+      int n0, n1;
+      exact_err(L.w[2 * lane], sw, &n0);
+      exact_err(L.w[2 * lane + 1], sw, &n1);
+      fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(n0 | (n1 << 4));
+    }
+    if (lane == 0) {
+      code[(g * cout + c) * nb + n] = (uint8_t)bestK;
+      if (loss) loss[(g * cout + c) * nb + n] = (float)best;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Diagonal (importance-weighted) sweep: float32 filter
+// ------------------------------------------------------------------------------------------
+template <bool BF16>
+__device__ inline void load_w16(const void* W, int64_t base, float w[16]) {
+  if (BF16) {
+    const unsigned* p = (const unsigned*)((const unsigned short*)W + base);   // 32-byte aligned
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const unsigned v = p[j];
+      w[2 * j] = __uint_as_float(v << 16);
+      w[2 * j + 1] = __uint_as_float(v & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = ((const float*)W)[base + j];
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
@@ -362,32 +600,42 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     for (int j = 0; j < 16; ++j) im[j] = 1.0f;
   }
   const float gsc = global_scale(amax[g]);
-  const bool force_exact = !(gsc >= 0x1p-116f) || !(gsc <= 0x1p+100f);
+  const bool fast = filter_ok(gsc);
   const int k0 = lane + 1, k1 = lane + 65;
   const bool v1 = k1 <= 126;
   const float s0 = cand_scale(k0, gsc), s1 = cand_scale(v1 ? k1 : 126, gsc);
-  const float is0 = s0 > 0.0f ? (float)(1.0 / (double)s0) : 0.0f;
-  const float is1 = s1 > 0.0f ? (float)(1.0 / (double)s1) : 0.0f;
+  const float is0 = inv_scale(s0), is1 = inv_scale(s1);
   const int p0 = lane, p1 = lane + 64;
-  const float img0 = (float)(1.0 / ((double)kMid[p0 % 7] * (double)gsc));
-  const float img1 = p1 < 112 ? (float)(1.0 / ((double)kMid[p1 % 7] * (double)gsc)) : 0.0f;
+  const float img0 = fast ? (float)(1.0 / ((double)kMid[p0 % 7] * (double)gsc)) : 0.0f;
+  const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)kMid[p1 % 7] * (double)gsc)) : 0.0f;
 
   for (int64_t c = c_begin; c < c_end; ++c) {
     const int64_t base = (g * cout + c) * cin + n * 16;
+    const int64_t oblk = (g * cout + c) * nb + n;
     float w[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) w[j] = load_w(W, BF16, base + j);
-    bool near = near_midpoint(fabsf(load_w(W, BF16, base + p0 / 7)), img0);
-    if (p1 < 112) near = near || near_midpoint(fabsf(load_w(W, BF16, base + p1 / 7)), img1);
-    const bool flag = __ballot(near) != 0ull || force_exact;
-
+    load_w16<BF16>(W, base, w);
+    const float wp0 = load_w(W, BF16, base + p0 / 7), wp1 = load_w(W, BF16, base + (p1 < 112 ? p1 : 0) / 7);
+    const bool near0 = near_midpoint(fabsf(wp0), img0);
+    const bool near1 = p1 < 112 && near_midpoint(fabsf(wp1), img1);
+    const unsigned long long m0 = __ballot(near0), m1 = __ballot(near1);
+    if (!fast) {
+      if (lane == 0) code[oblk] = 0;
+      continue;
+    }
+    const bool has_ovr = (m0 | m1) != 0ull;
+    int kv0 = 0, kv1 = 0;
+    float rv0 = 0.0f, rv1 = 0.0f;
+    if (has_ovr) {
+      pair_override(near0, p0, wp0, gsc, &kv0, &rv0);
+      pair_override(near1, p1, wp1, gsc, &kv1, &rv1);
+    }
     float L0 = 0.0f, L1 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
-      unsigned pk0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, w[j] * is0, w[j + 1] * is0, 1.0f, 0);
-      pk0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk0, w[j] * is1, w[j + 1] * is1, 1.0f, 1);
-      const v2f qa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk0, 1.0f, 0);
-      const v2f qb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk0, 1.0f, 1);
+      unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, w[j] * is0, w[j + 1] * is0, 1.0f, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, w[j] * is1, w[j + 1] * is1, 1.0f, 1);
+      const v2f qa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
+      const v2f qb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 1);
       const float ea0 = fmaf(qa[0], s0, -w[j]), ea1 = fmaf(qa[1], s0, -w[j + 1]);
       const float eb0 = fmaf(qb[0], s1, -w[j]), eb1 = fmaf(qb[1], s1, -w[j + 1]);
       L0 = fmaf(im[j] * ea0, ea0, L0);
@@ -395,63 +643,129 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
       L1 = fmaf(im[j] * eb0, eb0, L1);
       L1 = fmaf(im[j + 1] * eb1, eb1, L1);
     }
+    if (has_ovr) {
+      // a lane whose candidate has flagged elements re-scores it with the exact decisions
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = lane + 1 + 64 * h;
+        bool mine = false;
+        for (unsigned long long mm = m0 | m1; mm; mm &= mm - 1) {
+          const int b = __builtin_ctzll(mm);
+          mine |= (__builtin_amdgcn_readlane(kv0, b) == k && ((m0 >> b) & 1ull)) ||
+                  (__builtin_amdgcn_readlane(kv1, b) == k && ((m1 >> b) & 1ull));
+        }
+        if (mine) {
+          const float sh = h ? s1 : s0, ih = h ? is1 : is0;
+          float Lh = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float r = w[j] * ih;
+            r = override_for(m0, 0, kv0, rv0, k, j, r);
+            r = override_for(m1, 64, kv1, rv1, k, j, r);
+            const unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r, 0.0f, 1.0f, 0);
+            const float e = fmaf(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0)[0], sh, -w[j]);
+            Lh = fmaf(im[j] * e, e, Lh);
+          }
+          if (h) L1 = Lh; else L0 = Lh;
+        }
+      }
+    }
     if (!v1) L1 = __builtin_inff();
     float bestL = L0;
     int bestK = k0;
     if (L1 < bestL) { bestL = L1; bestK = k1; }
-    float minUB = fminf(L0 * (1.0f + kErrC), v1 ? L1 * (1.0f + kErrC) : __builtin_inff());
-    for (int o = 1; o < 64; o <<= 1) {
-      const float oL = __shfl_xor(bestL, o, 64);
-      const int oK = __shfl_xor(bestK, o, 64);
-      if (oL < bestL || (oL == bestL && oK < bestK)) { bestL = oL; bestK = oK; }
-      minUB = fminf(minUB, __shfl_xor(minUB, o, 64));
+    const float U = wave_min(fminf(L0 * (1.0f + kErrC), L1 * (1.0f + kErrC)));
+    const float mL = wave_min(bestL);
+    const int k_best = wave_min_i(bestL == mL ? bestK : (1 << 20));
+    const int cnt = __popcll(__ballot(L0 * (1.0f - kErrC) <= U)) + __popcll(__ballot(L1 * (1.0f - kErrC) <= U));
+    if (cnt != 1) {
+      if (lane == 0) code[oblk] = 0;
+      continue;
     }
-    const int cnt = __popcll(__ballot(L0 * (1.0f - kErrC) <= minUB)) +
-                    __popcll(__ballot(v1 && L1 * (1.0f - kErrC) <= minUB));
-    const int64_t oblk = (g * cout + c) * nb + n;
-    float outL = bestL;
-    if (flag || cnt != 1) {
-      double bestD = __builtin_inf();
-      int bestKD = 127;
-      for (int h = 0; h < 2; ++h) {
-        const int k = lane + 1 + 64 * h;
-        if (k > 126) continue;
-        const float sk = cand_scale(k, gsc);
-        double Ls = 0.0;
-        int dummy;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const double e = exact_err(w[j], sk, &dummy);
-          Ls += (double)im[j] * e * e;
-        }
-        if (Ls < bestD) { bestD = Ls; bestKD = k; }
-      }
-      for (int o = 1; o < 64; o <<= 1) {
-        const double oL = __shfl_xor(bestD, o, 64);
-        const int oK = __shfl_xor(bestKD, o, 64);
-        if (oL < bestD || (oL == bestD && oK < bestKD)) { bestD = oL; bestKD = oK; }
-      }
-      bestK = bestKD;
-      outL = (float)bestD;
-      if (lane < 8 && fp4) {
-        const float sw = cand_scale(bestK, gsc);
-        int n0, n1;
-        exact_err(load_w(W, BF16, base + 2 * lane), sw, &n0);
-        exact_err(load_w(W, BF16, base + 2 * lane + 1), sw, &n1);
-        fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(n0 | (n1 << 4));
-      }
-    } else if (lane < 8 && fp4) {
-      const float sw = cand_scale(bestK, gsc);
-      const float iw = (float)(1.0 / (double)sw);
+    if (lane < 8 && fp4) {
+      const float sw = cand_scale(k_best, gsc);
+      const float iw = inv_scale(sw);
       const float wa = load_w(W, BF16, base + 2 * lane), wb = load_w(W, BF16, base + 2 * lane + 1);
-      const unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, wa * iw, wb * iw, 1.0f, 0);
+      float ra = wa * iw, rb = wb * iw;
+      if (has_ovr) {
+        ra = override_for(m0, 0, kv0, rv0, k_best, 2 * lane, ra);
+        ra = override_for(m1, 64, kv1, rv1, k_best, 2 * lane, ra);
+        rb = override_for(m0, 0, kv0, rv0, k_best, 2 * lane + 1, rb);
+        rb = override_for(m1, 64, kv1, rv1, k_best, 2 * lane + 1, rb);
+      }
+      const unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ra, rb, 1.0f, 0);
       unsigned byte = pk & 0x77u;
       byte |= (wa < 0.0f ? 0x8u : 0u) | (wb < 0.0f ? 0x80u : 0u);
       fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)byte;
     }
     if (lane == 0) {
-      code[oblk] = (uint8_t)bestK;
-      if (loss) loss[oblk] = outL;
+      code[oblk] = (uint8_t)k_best;
+      if (loss) loss[oblk] = mL;
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
+    const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
+    const float* __restrict__ imp, uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
+    float* __restrict__ loss) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nb = cin / 16;
+  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t g = blockIdx.z;
+  const int64_t c_begin = (int64_t)blockIdx.y * kRowsPerWave;
+  if (n >= nb || c_begin >= cout) return;
+  const int64_t c_end = min(cout, c_begin + kRowsPerWave);
+  const int64_t myc = c_begin + lane;
+  const bool pend = lane < kRowsPerWave && myc < c_end && code[(g * cout + myc) * nb + n] == 0;
+  unsigned long long todo = __ballot(pend);
+  if (!todo) return;
+  float im[16];
+  double isum = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    im[j] = imp[g * cin + n * 16 + j];
+    isum += (double)im[j];
+  }
+  if (isum == 0.0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) im[j] = 1.0f;
+  }
+  const float gsc = global_scale(amax[g]);
+  while (todo) {
+    const int r = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int64_t c = c_begin + r;
+    const int64_t base = (g * cout + c) * cin + n * 16;
+    float w[16];
+    load_w16<BF16>(W, base, w);
+    double best = __builtin_inf();
+    int bestK = 1 << 20;
+    for (int h = 0; h < 2; ++h) {
+      const int k = lane + 1 + 64 * h;
+      if (k > 126) continue;
+      const float sk = cand_scale(k, gsc);
+      double Ls = 0.0;
+      int nib;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const double e = exact_err(w[j], sk, &nib);
+        Ls += (double)im[j] * e * e;
+      }
+      if (Ls < best) { best = Ls; bestK = k; }
+    }
+    wave_argmin_d(best, bestK);
+    if (lane < 8 && fp4) {
+      const float sw = cand_scale(bestK, gsc);
+      int n0, n1;
+      exact_err(load_w(W, BF16, base + 2 * lane), sw, &n0);
+      exact_err(load_w(W, BF16, base + 2 * lane + 1), sw, &n1);
+      fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(n0 | (n1 << 4));
+    }
+    if (lane == 0) {
+      code[(g * cout + c) * nb + n] = (uint8_t)bestK;
+      if (loss) loss[(g * cout + c) * nb + n] = (float)best;
     }
   }
 }
@@ -466,14 +780,21 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + kRowsPerWave - 1) / kRowsPerWave),
             (unsigned)n_groups);
   dim3 block(kWaves * 64);
-  if (bf16 && P)
-    hipLaunchKernelGGL((k_sweep_full<true, true>), grid, block, 0, stream, W, cout, cin, amax, H, P, code, fp4, loss);
-  else if (bf16)
-    hipLaunchKernelGGL((k_sweep_full<true, false>), grid, block, 0, stream, W, cout, cin, amax, H, P, code, fp4, loss);
-  else if (P)
-    hipLaunchKernelGGL((k_sweep_full<false, true>), grid, block, 0, stream, W, cout, cin, amax, H, P, code, fp4, loss);
-  else
-    hipLaunchKernelGGL((k_sweep_full<false, false>), grid, block, 0, stream, W, cout, cin, amax, H, P, code, fp4, loss);
+#define LH_SWEEP_PAIR(B, C)                                                                        \
+  hipLaunchKernelGGL((k_sweep_full<B, C>), grid, block, 0, stream, W, cout, cin, amax, H, P, code, \
+                     fp4, loss);                                                                   \
+  hipLaunchKernelGGL((k_sweep_full_exact<B, C>), grid, block, 0, stream, W, cout, cin, amax, H, P, \
+                     code, fp4, loss)
+  if (bf16 && P) {
+    LH_SWEEP_PAIR(true, true);
+  } else if (bf16) {
+    LH_SWEEP_PAIR(true, false);
+  } else if (P) {
+    LH_SWEEP_PAIR(false, true);
+  } else {
+    LH_SWEEP_PAIR(false, false);
+  }
+#undef LH_SWEEP_PAIR
   return hipGetLastError();
 }
 
@@ -485,10 +806,13 @@ hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + kRowsPerWave - 1) / kRowsPerWave),
             (unsigned)n_groups);
   dim3 block(kWaves * 64);
-  if (bf16)
+  if (bf16) {
     hipLaunchKernelGGL((k_sweep_diag<true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
-  else
+    hipLaunchKernelGGL((k_sweep_diag_exact<true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
+  } else {
     hipLaunchKernelGGL((k_sweep_diag<false>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
+    hipLaunchKernelGGL((k_sweep_diag_exact<false>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
+  }
   return hipGetLastError();
 }
 

@@ -225,6 +225,36 @@ def test_sweep_exact_midpoint_ties():
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
 
+@pytest.mark.parametrize("diag", [False, True])
+def test_sweep_power_of_two_fractions_of_amax(diag):
+    """bf16 weights equal to amax * 2^-j (times 1, 1.5, 1.25, 1.75) put |w|/s_k within a few ulps of
+    an E2M1 midpoint for several candidates: the filter must decide those quotients exactly."""
+    r = np.random.default_rng(8)
+    cout, cin = 200, 64
+    w32 = r.normal(0, 0.02, (1, cout, cin)).astype(np.float32)
+    amax = np.float32(0.10498046875)                      # a bf16 value (mantissa 215)
+    fr = np.array([1.0, 1.5, 1.25, 1.75])
+    mask = r.random(w32.shape) < 0.15
+    picks = amax * fr[r.integers(0, 4, w32.shape)] * 2.0 ** -r.integers(1, 9, w32.shape)
+    w32 = np.where(mask, np.sign(r.standard_normal(w32.shape)) * picks, w32).astype(np.float32)
+    w32[0, 0, 0] = amax
+    Wb = synth.bf16_bits_from_f32(w32)
+    Wf = synth.f32_from_bf16_bits(Wb).astype(np.float64)
+    a = oracle.absmax(Wf).astype(np.float32)
+    note(f"sweep power-of-two fractions of amax, diag={diag}")
+    Wd = torch.from_numpy(Wb).view(torch.bfloat16).to(DEV)
+    if diag:
+        imp = np.abs(r.standard_normal((1, cin))).astype(np.float32) + 0.1
+        code, fp4, loss = lh.lh_scale_sweep_diag(Wd, torch.from_numpy(a).to(DEV), torch.from_numpy(imp).to(DEV))
+        res = oracle.sweep_diag(Wf, a, imp)
+    else:
+        A = r.standard_normal((1, cin // 16, 16, 16)).astype(np.float32)
+        H = (np.einsum("gnij,gnkj->gnik", A, A) / 16 + 0.5 * np.eye(16)).astype(np.float32)
+        code, fp4, loss = lh.lh_scale_sweep(Wd, torch.from_numpy(a).to(DEV), torch.from_numpy(H).to(DEV))
+        res = oracle.sweep(Wf, a, H)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
 def test_sweep_deterministic():
     wl = synth.make("c2", cout=100, cin=64, rows=300)
     note("sweep determinism")
