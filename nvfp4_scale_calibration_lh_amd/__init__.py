@@ -15,7 +15,8 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblh.so")
+# The library built next to this file; LH_LIBRARY may name another build of the same library.
+LIB_PATH = os.environ.get("LH_LIBRARY") or os.path.join(_PKG, "liblh.so")
 
 LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1

@@ -16,9 +16,11 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "liblh.so")
 SOURCES = ["absmax.hip", "accumulate.hip", "sweep.hip", "lh_abi.cpp"]
 ARCH = "gfx950"
-# Packed fp32 ALU instructions are kept out of the generated code.
+# Packed fp32 ALU instructions are kept out of the generated code; MFMA results live in VGPRs
+# (no accumulator-register copies in the sweep loop).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-         "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
+         "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wall",
+         "-Wno-unused-function"]
 
 
 def _hipcc() -> str:

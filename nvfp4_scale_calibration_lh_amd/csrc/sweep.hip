@@ -36,6 +36,8 @@
 //    the float64 objective.
 #include "lh_internal.hpp"
 
+#include <type_traits>
+
 namespace lh {
 namespace {
 
@@ -44,7 +46,7 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per workgroup; wave w takes block column 4*bx + w
 constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
-constexpr float kErrC = 0x1p-17f;    // filter error bound factor (about 3x the derived bound)
+constexpr float kErrC = 0x1p-16f;    // filter error bound factor (about 4x the derived bound)
 constexpr int kNearUlps = 16;        // midpoint proximity test, in ulps of |w|/(m g)
 
 __device__ const float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
@@ -173,23 +175,12 @@ template <int CTRL>
 __device__ inline float dppf(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-template <int CTRL>
-__device__ inline int dppi(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
 // Minimum over the 16 lanes of each DPP row (row_ror by 8, 4, 2, 1); every lane gets the result.
 __device__ inline float row_min(float v) {
   v = fminf(v, dppf<0x128>(v));
   v = fminf(v, dppf<0x124>(v));
   v = fminf(v, dppf<0x122>(v));
   v = fminf(v, dppf<0x121>(v));
-  return v;
-}
-__device__ inline int row_min_i(int v) {
-  v = min(v, dppi<0x128>(v));
-  v = min(v, dppi<0x124>(v));
-  v = min(v, dppi<0x122>(v));
-  v = min(v, dppi<0x121>(v));
   return v;
 }
 // Minimum over all 64 lanes.
@@ -200,14 +191,6 @@ __device__ inline float wave_min(float v) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ inline int wave_min_i(int v) {
-  v = row_min_i(v);
-  auto a = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
-  v = min((int)a[0], (int)a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
-  return min((int)b[0], (int)b[1]);
-}
-
 // Lowest (loss, code) over the wave in float64 (exact re-scoring).
 __device__ inline void wave_argmin_d(double& L, int& k) {
   for (int o = 1; o < 64; o <<= 1) {
@@ -217,6 +200,17 @@ __device__ inline void wave_argmin_d(double& L, int& k) {
   }
 }
 
+// Sums each of p[0..3] over the 4 rows (16-lane groups) of the wave and leaves the total of p[r]
+// in row r.
+__device__ inline float quad_sum(const float p[4]) {
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const float s02 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float s13 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
 // ------------------------------------------------------------------------------------------
 // Full-Hessian sweep: float32 filter
 // ------------------------------------------------------------------------------------------
@@ -224,20 +218,27 @@ struct FullLds {
   float H[256];
   float P[256];
   float w[16][16];     // current 16-row tile: w[row][elem]
-  float b2[16][16];    // 2 * (P w)[row][elem]
-  float pw2[16][16];   // 2 * (|P| |w|)[row][elem]
+  float g[16][16];     // (H w - 2 P w)[row][elem]
+  float pw[16][16];    // (|P| |w|)[row][elem]
+  double ex[4][16];    // float64 refinement: e of up to 4 contenders
 };
 
-// Quantization error of the lane's 4 elements for scale s, from the quotients r = w / s.
-__device__ inline void quant4(const float w[4], const float r[4], float s, float e[4]) {
-  unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
-  pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, r[2], r[3], 1.0f, 1);
-  const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
-  const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 1);
-  e[0] = fmaf(q01[0], s, -w[0]);
-  e[1] = fmaf(q01[1], s, -w[1]);
-  e[2] = fmaf(q23[0], s, -w[2]);
-  e[3] = fmaf(q23[1], s, -w[3]);
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// bf16 round-to-nearest-even of a finite float, as bits in the low half.
+__device__ inline unsigned bf16_rne(float x) {
+  const unsigned b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+__device__ inline float bf16_val(unsigned h) { return __uint_as_float(h << 16); }
+
+// Sum over the 4 rows of the wave, result in every lane.
+__device__ inline float group_sum(float v) {
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
 
 template <bool BF16, bool COUPLED>
@@ -269,31 +270,47 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
   for (int j = 0; j < 16; ++j) tr += (double)L.H[j * 17];
   const bool dead = (tr == 0.0);                   // no activation energy: plain weight MSE
   const bool coupled = COUPLED && !dead;
+  // Lane (row i, group gg) holds, for elements col = 4*gg + t:
+  //   a[t]   = H[i][col] in fp32 (H w per 16-row tile), pv/pa = P and |P| (P w, |P||w|)
+  //   hb     = H[i][col] split into three bf16 pieces H1 + H2 + H3 (exact to 2^-27 relative):
+  //            A operand of the bf16 MFMAs that form H q for the candidates
+  //   dm[t]  = sqrt(max_j max(|H_col,j|, |H_j,col|)), so |H_ij| <= dm_i dm_j for any H
   float a[4], dm[4], pa[4], pv[4];
+  unsigned h1[4], h2[4], h3[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int col = 4 * gg + t;
     a[t] = dead ? (i == col ? 1.0f : 0.0f) : L.H[i * 16 + col];
+    h1[t] = bf16_rne(a[t]);
+    const float r1 = a[t] - bf16_val(h1[t]);      // exact
+    h2[t] = bf16_rne(r1);
+    const float r2 = r1 - bf16_val(h2[t]);        // exact
+    h3[t] = bf16_rne(r2);
     float mx = 1.0f;
     if (!dead) {
       mx = 0.0f;
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(fabsf(L.H[col * 16 + j]), fabsf(L.H[j * 16 + col])));
     }
-    dm[t] = sqrtf(mx) * 1.0000002f;               // |H_ij| <= dm_i dm_j, with sqrt rounding margin
+    dm[t] = sqrtf(mx) * 1.0000002f;               // with sqrt rounding margin
     pv[t] = coupled ? L.P[i * 16 + col] : 0.0f;
     pa[t] = fabsf(pv[t]);
   }
+  // two chained 16x16x32 bf16 MFMAs (same opcode): K slots [H1 | H2] and [H3 | 0]
+  const v4u A1u = {h1[0] | (h1[1] << 16), h1[2] | (h1[3] << 16), h2[0] | (h2[1] << 16), h2[2] | (h2[3] << 16)};
+  const v4u A2u = {h3[0] | (h3[1] << 16), h3[2] | (h3[3] << 16), 0u, 0u};
+  const v8bf A1 = __builtin_bit_cast(v8bf, A1u);
+  const v8bf A2 = __builtin_bit_cast(v8bf, A2u);
 
-  // ---- candidate scales for this lane's 8 tiles (codes 127, 128 repeat 126 and are masked)
+  // ---- candidate scales.  Tile tau holds codes 16*tau + i + 1.  Tile 0 (codes 1..16) uses
+  // s0/is0 directly.  For tau >= 1 the lane's codes share one E4M3 mantissa and step the exponent
+  // by 2 per tile, so s_k = s1 * 4^(tau-1) and 1/s_k = is1 * 4^-(tau-1) exactly (normal range):
+  // the lane forms w * is1 once per block and the FP4 converts apply the power of 4 through their
+  // exponent-only scale operand (on the way in and out), which is exact.  Codes 127 and 128
+  // (tile 7, i >= 14) do not exist and are masked.
   const float gsc = global_scale(amax[g]);
   const bool fast = filter_ok(gsc);
-  float s[8], is[8];
-#pragma unroll
-  for (int tau = 0; tau < 8; ++tau) {
-    const int k = min(16 * tau + i + 1, 126);
-    s[tau] = cand_scale(k, gsc);
-    is[tau] = inv_scale(s[tau]);
-  }
+  const float s0 = cand_scale(i + 1, gsc), is0 = inv_scale(s0);
+  const float s1 = cand_scale(i + 17, gsc), is1 = inv_scale(s1);
   // midpoint proximity: this lane tests pairs p = lane and lane + 64 of (element, midpoint)
   const int p0 = lane, p1 = lane + 64;
   const float img0 = fast ? (float)(1.0 / ((double)kMid[p0 % 7] * (double)gsc)) : 0.0f;
@@ -301,14 +318,16 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
-    // ---- 16-row tile: w, b = P w and |P||w| (MFMA, K index = element 4*gg + t)
+    // ---- 16-row tile: w, H w, P w and |P||w| (fp32 MFMA, K index = element 4*gg + t)
     const int64_t crow = c0 + i;
     const bool row_on = crow < c_end;
     float wt[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       wt[t] = row_on ? load_w(W, BF16, (g * cout + crow) * cin + n * 16 + 4 * gg + t) : 0.0f;
-    v4f bt = zero4, pwt = zero4;
+    v4f hw = zero4, bt = zero4, pwt = zero4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) hw = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], wt[t], hw, 0, 0, 0);
     if (coupled) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -318,12 +337,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t) {                  // lane holds elements 4gg+t of row i
       L.w[i][4 * gg + t] = wt[t];
-      if (COUPLED) {
-        L.b2[i][4 * gg + t] = 2.0f * bt[t];          // lane holds elements 4gg+t of row i
-        L.pw2[i][4 * gg + t] = 2.0f * pwt[t];
-      }
+      L.g[i][4 * gg + t] = coupled ? fmaf(-2.0f, bt[t], hw[t]) : hw[t];
+      if (COUPLED) L.pw[i][4 * gg + t] = pwt[t];
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -332,16 +349,19 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
       const int64_t oblk = (g * cout + c) * nb + n;
-      float w[4], pw2[4];
-      v4f cinit = zero4;
+      float w[4], gq[4], pw2[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         w[t] = L.w[rr][4 * gg + t];
-        if (COUPLED) {
-          cinit[t] = coupled ? L.b2[rr][4 * gg + t] : 0.0f;
-          pw2[t] = coupled ? L.pw2[rr][4 * gg + t] : 0.0f;
-        }
+        gq[t] = L.g[rr][4 * gg + t];
+        pw2[t] = (COUPLED && coupled) ? 2.0f * L.pw[rr][4 * gg + t] : 0.0f;
       }
+      float swp = fabsf(w[0]) * dm[0];
+      swp = fmaf(fabsf(w[1]), dm[1], swp);
+      swp = fmaf(fabsf(w[2]), dm[2], swp);
+      swp = fmaf(fabsf(w[3]), dm[3], swp);
+      const float S_w = group_sum(swp) * 1.0000005f;   // sum_j dm_j |w_j| (rounded up)
+
       // quotients within a few ulps of an E2M1 midpoint are decided exactly (fma sign test)
       const float wp0 = L.w[rr][p0 / 7], wp1 = L.w[rr][(p1 < 112 ? p1 : 0) / 7];
       const bool near0 = near_midpoint(fabsf(wp0), img0);
@@ -358,98 +378,186 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
         pair_override(near0, p0, wp0, gsc, &kv0, &rv0);
         pair_override(near1, p1, wp1, gsc, &kv1, &rv1);
       }
-      auto quotients = [&](int tau, float r[4]) {
+      float rb[4];                                   // w / s for this lane's tile-1 code
 #pragma unroll
-        for (int t = 0; t < 4; ++t) r[t] = w[t] * is[tau];
-        if (has_ovr) {
-          apply_overrides(m0, 0, kv0, rv0, tau, 0, i, gg, r);
-          apply_overrides(m1, 64, kv1, rv1, tau, 0, i, gg, r);
+      for (int t = 0; t < 4; ++t) rb[t] = w[t] * is1;
+
+      // Scoring of tile tau (16 codes): quotients (with exact overrides) -> FP4 round trip
+      // q' = q * 4^(tau-1) (exact in bf16), e = fma(q', s, -w), y = H q' on bf16 MFMA (H in
+      // three pieces, products exact, fp32 accumulation), (H e + 2b)_i = s y_i - (H w - 2b)_i,
+      // L = sum_i e_i (H e + 2b)_i.  Instantiated twice so the common case has no override code.
+      auto score = [&](auto ovr_tag, float Lq[2], float Aq[2]) {
+        constexpr bool OVR = decltype(ovr_tag)::value;
+        auto tile_err = [&](int tau, float e[4], unsigned& p01, unsigned& p23) {
+          const float sc = tau == 0 ? 1.0f : (float)(1u << (2 * (tau - 1)));   // 4^(tau-1)
+          float r[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) r[t] = tau == 0 ? w[t] * is0 : rb[t];
+          if (OVR) {                                  // overrides are actual quotients w / s_k
+            const float isc = 1.0f / sc;               // powers of two: exact
+            float o[4] = {r[0] * isc, r[1] * isc, r[2] * isc, r[3] * isc};
+            apply_overrides(m0, 0, kv0, rv0, tau, 0, i, gg, o);
+            apply_overrides(m1, 64, kv1, rv1, tau, 0, i, gg, o);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) r[t] = o[t] * sc;
+          }
+          unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], sc, 0);
+          pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, r[2], r[3], sc, 1);
+          const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc, 0);
+          const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc, 1);
+          const float sb = tau == 0 ? s0 : s1;
+          e[0] = fmaf(q01[0], sb, -w[0]);
+          e[1] = fmaf(q01[1], sb, -w[1]);
+          e[2] = fmaf(q23[0], sb, -w[2]);
+          e[3] = fmaf(q23[1], sb, -w[3]);
+          // q' has at most 2 significant bits: its bf16 is the top half of the float
+          p01 = __builtin_amdgcn_perm(__float_as_uint(q01[1]), __float_as_uint(q01[0]), 0x07060302u);
+          p23 = __builtin_amdgcn_perm(__float_as_uint(q23[1]), __float_as_uint(q23[0]), 0x07060302u);
+        };
+        float e[4], en[4];
+        unsigned p01, p23, pn01 = 0, pn23 = 0;
+        tile_err(0, e, p01, p23);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float pl[4], pa4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int tau = 4 * q + u;
+            const v4u Bu = {p01, p23, p01, p23};
+            const v8bf B = __builtin_bit_cast(v8bf, Bu);
+            v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, zero4, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, y, 0, 0, 0);
+            if (tau < 7) tile_err(tau + 1, en, pn01, pn23);         // overlaps the MFMAs
+            const float sb = tau == 0 ? s0 : s1;
+            float sp = fabsf(e[0]) * dm[0];
+            sp = fmaf(fabsf(e[1]), dm[1], sp);
+            sp = fmaf(fabsf(e[2]), dm[2], sp);
+            sp = fmaf(fabsf(e[3]), dm[3], sp);
+            float ap = sp * fmaf(4.0f, sp, S_w);
+            if (COUPLED) {
+              float bp = fabsf(e[0]) * pw2[0];
+              bp = fmaf(fabsf(e[1]), pw2[1], bp);
+              bp = fmaf(fabsf(e[2]), pw2[2], bp);
+              bp = fmaf(fabsf(e[3]), pw2[3], bp);
+              ap += bp;
+            }
+            float lp = e[0] * fmaf(sb, y[0], -gq[0]);
+            lp = fmaf(e[1], fmaf(sb, y[1], -gq[1]), lp);
+            lp = fmaf(e[2], fmaf(sb, y[2], -gq[2]), lp);
+            lp = fmaf(e[3], fmaf(sb, y[3], -gq[3]), lp);
+            pl[u] = lp;
+            pa4[u] = ap;
+            if (tau < 7) {
+#pragma unroll
+              for (int t = 0; t < 4; ++t) e[t] = en[t];
+              p01 = pn01;
+              p23 = pn23;
+            }
+          }
+          Lq[q] = quad_sum(pl);
+          Aq[q] = quad_sum(pa4);
         }
       };
+      float Lq[2], Aq[2];
+      if (has_ovr) score(std::true_type{}, Lq, Aq);
+      else score(std::false_type{}, Lq, Aq);
 
-      float Lk[8], Ak[8];
-      float e[4], en[4], rq[4];
-      quotients(0, rq);
-      quant4(w, rq, s[0], e);
-#pragma unroll
-      for (int tau = 0; tau < 8; ++tau) {
-        v4f D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], e[0], cinit, 0, 0, 0);
-        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], e[1], D, 0, 0, 0);
-        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], e[2], D, 0, 0, 0);
-        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], e[3], D, 0, 0, 0);
-        if (tau < 7) {                                            // overlaps the MFMA chain
-          quotients(tau + 1, rq);
-          quant4(w, rq, s[tau + 1], en);
+      // lane (row gg, column i) now holds codes k_q = 16*(4q+gg) + i + 1 for q = 0, 1
+      const int kq0 = 16 * gg + i + 1, kq1 = 16 * (4 + gg) + i + 1;
+      if (kq1 > 126) Lq[1] = __builtin_inff();
+      float bestL = Lq[0], bestA = Aq[0];
+      int bestK = kq0;
+      if (Lq[1] < bestL) { bestL = Lq[1]; bestA = Aq[1]; bestK = kq1; }
+      // winner k* = a lane holding the wave minimum.  k* is the exact argmin when every other
+      // candidate's lower bound exceeds k*'s upper bound (L_k - cA_k > L* + cA*).
+      const float mL = wave_min(bestL);
+      const int owner = (int)__builtin_ctzll(__ballot(bestL == mL));
+      const int k_best = __builtin_amdgcn_readlane(bestK, owner);
+      const float A_best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bestA), owner));
+      const float U = fmaf(kErrC, A_best, mL);
+      const unsigned long long M0 = __ballot(fmaf(-kErrC, Aq[0], Lq[0]) <= U);
+      const unsigned long long M1 = __ballot(fmaf(-kErrC, Aq[1], Lq[1]) <= U);
+      const int cnt = __popcll(M0) + __popcll(M1);
+      if (cnt == 1) {
+        // unique winner: emit its codes.  Its reciprocal scale comes from the lane that owns it.
+        const int kb0 = k_best - 1;
+        const int src = kb0 & 15;
+        float iw;
+        if (kb0 < 16) {
+          iw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(is0), src));
+        } else {
+          const float sc = (float)(1u << (2 * ((kb0 >> 4) - 1)));
+          iw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(is1), src)) / sc;
         }
-        float sp = fabsf(e[0]) * dm[0];
-        sp = fmaf(fabsf(e[1]), dm[1], sp);
-        sp = fmaf(fabsf(e[2]), dm[2], sp);
-        sp = fmaf(fabsf(e[3]), dm[3], sp);
-        float ap = 4.0f * sp * sp;
-        if (COUPLED) {
-          float bp = fabsf(e[0]) * pw2[0];
-          bp = fmaf(fabsf(e[1]), pw2[1], bp);
-          bp = fmaf(fabsf(e[2]), pw2[2], bp);
-          bp = fmaf(fabsf(e[3]), pw2[3], bp);
-          ap += bp;
+        float rw[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rw[t] = w[t] * iw;
+        if (has_ovr) {
+          apply_overrides(m0, 0, kv0, rv0, -1, k_best, i, gg, rw);
+          apply_overrides(m1, 64, kv1, rv1, -1, k_best, i, gg, rw);
         }
-        float lp = e[0] * D[0];
-        lp = fmaf(e[1], D[1], lp);
-        lp = fmaf(e[2], D[2], lp);
-        lp = fmaf(e[3], D[3], lp);
-        // reduce lp and ap over the 4 lane groups: lanes 0-31 end with L, 32-63 with A; then
-        // spread both over the wave
-        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(ap), false, false);
-        float z = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
-        z = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-        auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
-        Lk[tau] = __uint_as_float(u[0]);
-        Ak[tau] = __uint_as_float(u[1]);
-        if (tau < 7) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) e[t] = en[t];
+        unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, rw[0], rw[1], 1.0f, 0);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, rw[2], rw[3], 1.0f, 1);
+        unsigned nb4 = pk & 0x7777u;                                   // magnitudes
+        nb4 |= (w[0] < 0.0f ? 0x8u : 0u) | (w[1] < 0.0f ? 0x80u : 0u) |
+               (w[2] < 0.0f ? 0x800u : 0u) | (w[3] < 0.0f ? 0x8000u : 0u);
+        if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
+        if (lane == 0) {
+          code[oblk] = (uint8_t)k_best;
+          if (loss) loss[oblk] = mL;
         }
-      }
-      if (i >= 14) Lk[7] = __builtin_inff();        // codes 127 and 128 do not exist
-
-      float bestL = __builtin_inff(), ub = __builtin_inff();
-      int bestK = 1 << 20;
+      } else if (cnt <= 4) {
+        // 2..4 contenders: re-score them exactly in float64, 16 lanes (one per element) each
+        unsigned long long ma = M0, mb = M1;
+        auto next = [&]() -> int {
+          if (ma) { const int b = __builtin_ctzll(ma); ma &= ma - 1; return b + 1; }
+          if (mb) { const int b = __builtin_ctzll(mb); mb &= mb - 1; return b + 65; }
+          return 0;
+        };
+        const int kc0 = next(), kc1 = next(), kc2 = next(), kc3 = next();
+        const int my_k = gg == 0 ? kc0 : (gg == 1 ? kc1 : (gg == 2 ? kc2 : kc3));
+        const float sk = cand_scale(my_k > 0 ? my_k : 1, gsc);
+        int nib;
+        const double ei = exact_err(L.w[rr][i], sk, &nib);
+        L.ex[gg][i] = ei;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        double y = 0.0, bi = 0.0;
+        if (dead) {
+          y = ei;
+        } else {
 #pragma unroll
-      for (int tau = 0; tau < 8; ++tau) {
-        ub = fminf(ub, fmaf(kErrC, Ak[tau], Lk[tau]));
-        if (Lk[tau] < bestL) { bestL = Lk[tau]; bestK = 16 * tau + i + 1; }
-      }
-      const float U = row_min(ub);
-      const float mL = row_min(bestL);
-      const int k_best = row_min_i(bestL == mL ? bestK : (1 << 20));
-      int cnt = 0;
+          for (int j = 0; j < 16; ++j) y = fma((double)L.H[i * 16 + j], L.ex[gg][j], y);
+        }
+        if (coupled) {
 #pragma unroll
-      for (int tau = 0; tau < 8; ++tau)
-        cnt += __popcll(__ballot(fmaf(-kErrC, Ak[tau], Lk[tau]) <= U) & 0xFFFFull);
-      if (cnt != 1) {
-        if (lane == 0) code[oblk] = 0;              // several candidates can win: float64 pass
-        continue;
-      }
-      // unique winner: emit its codes
-      const float sw = cand_scale(k_best, gsc);
-      const float iw = inv_scale(sw);
-      float rw[4];
+          for (int j = 0; j < 16; ++j) bi = fma((double)L.P[i * 16 + j], (double)L.w[rr][j], bi);
+        }
+        double z = ei * (y + 2.0 * bi);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rw[t] = w[t] * iw;
-      if (has_ovr) {
-        apply_overrides(m0, 0, kv0, rv0, -1, k_best, i, gg, rw);
-        apply_overrides(m1, 64, kv1, rv1, -1, k_best, i, gg, rw);
-      }
-      unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, rw[0], rw[1], 1.0f, 0);
-      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, rw[2], rw[3], 1.0f, 1);
-      unsigned nb4 = pk & 0x7777u;                                   // magnitudes
-      nb4 |= (w[0] < 0.0f ? 0x8u : 0u) | (w[1] < 0.0f ? 0x80u : 0u) |
-             (w[2] < 0.0f ? 0x800u : 0u) | (w[3] < 0.0f ? 0x8000u : 0u);
-      if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
-      if (lane == 0) {
-        code[oblk] = (uint8_t)k_best;
-        if (loss) loss[oblk] = mL;
+        for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);   // sum over the row's lanes
+        double bestD = __builtin_inf();
+        int bestKD = 1 << 20;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kr = r == 0 ? kc0 : (r == 1 ? kc1 : (r == 2 ? kc2 : kc3));
+          const double Lr = __shfl(z, 16 * r, 64);
+          if (kr > 0 && (Lr < bestD || (Lr == bestD && kr < bestKD))) { bestD = Lr; bestKD = kr; }
+        }
+        const float sw = cand_scale(bestKD, gsc);
+        if (lane < 8 && fp4) {
+          int n0, n1;
+          exact_err(L.w[rr][2 * lane], sw, &n0);
+          exact_err(L.w[rr][2 * lane + 1], sw, &n1);
+          fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(n0 | (n1 << 4));
+        }
+        if (lane == 0) {
+          code[oblk] = (uint8_t)bestKD;
+          if (loss) loss[oblk] = (float)bestD;
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        if (lane == 0) code[oblk] = 0;              // many contenders: float64 pass
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -674,9 +782,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     float bestL = L0;
     int bestK = k0;
     if (L1 < bestL) { bestL = L1; bestK = k1; }
-    const float U = wave_min(fminf(L0 * (1.0f + kErrC), L1 * (1.0f + kErrC)));
+    // the winner is exact when every other candidate's lower bound exceeds its upper bound
     const float mL = wave_min(bestL);
-    const int k_best = wave_min_i(bestL == mL ? bestK : (1 << 20));
+    const int k_best = __builtin_amdgcn_readlane(bestK, (int)__builtin_ctzll(__ballot(bestL == mL)));
+    const float U = mL * (1.0f + kErrC);
     const int cnt = __popcll(__ballot(L0 * (1.0f - kErrC) <= U)) + __popcll(__ballot(L1 * (1.0f - kErrC) <= U));
     if (cnt != 1) {
       if (lane == 0) code[oblk] = 0;
