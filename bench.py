@@ -37,6 +37,33 @@ FLOPS_COUPLED = 126 * (32 + 512 + 32 + 32) + 512
 FLOPS_DIAG = 126 * (32 + 48)
 
 
+def measured_traffic(cfg, prefix):
+    """HBM bytes per call of the kernels whose names start with `prefix`, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes recorded in profiles/traffic.json, scaled by the copy-kernel
+    calibration factors.  None when no record exists or a kernel source changed since."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    kern = rec.get("workloads", {}).get(cfg, {})
+    total, found = 0.0, False
+    for name, v in kern.items():
+        if not name.startswith(prefix):
+            continue
+        src = os.path.join(ROOT, "nvfp4_scale_calibration_lh_amd", "csrc", v.get("source", ""))
+        try:
+            with open(src, "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != v["source_sha256"]:
+                    return None
+        except OSError:
+            return None
+        total += v["fetch_kib"] * 1024 * rec["fetch_factor"] + v["write_kib"] * 1024 * rec["write_factor"]
+        found = True
+    return total if found else None
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -195,6 +222,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": sweep_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": sweep_tflops / FP32_PEAK_TFLOPS, "traffic": None}
+    roof["traffic"] = measured_traffic(args.config, "k_sweep")
     roof.update({"kernel": "sweep", "flops_per_block": flops_blk, "blocks_per_launch": blocks,
                  "avg_launch_ms": ms_sw})
 
@@ -216,7 +244,8 @@ def main():
                    "mode": wl.mode, "rotating_copies": copies},
         "roofline": roof,
         "accumulate": {"avg_launch_ms": ms_acc, "algorithmic_bytes": acc_bytes, "achieved_gbs": acc_gbs,
-                       "peak_gbs": HBM_PEAK_GBS, "frac": acc_gbs / HBM_PEAK_GBS},
+                       "peak_gbs": HBM_PEAK_GBS, "frac": acc_gbs / HBM_PEAK_GBS,
+                       "traffic": measured_traffic(args.config, "k_acc")},
         "absmax": {"avg_launch_ms": ms_abs, "achieved_gbs": abs_gbs, "frac": abs_gbs / HBM_PEAK_GBS},
         "sweep": {"avg_launch_ms": ms_sw, "blocks_per_s": blocks / (ms_sw * 1e-3), "tflops": sweep_tflops},
     }

@@ -24,8 +24,10 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null stream of
  *     the pointers' device).  The library never synchronizes the host, launches on the device that
  *     owns the pointers and restores the caller's current device.
- *   - Scratch memory, when an entry point needs it, is taken with hipMallocAsync on `stream` and
- *     released with hipFreeAsync on the same stream before the call returns.
+ *   - Scratch memory, when an entry point needs it (accumulation partial sums), comes from a
+ *     library-owned memory pool of the device, allocated and freed stream-ordered on `stream`
+ *     within the call; the pool keeps the memory for reuse, so steady-state calls do not reach
+ *     the driver's allocator.
  *   - Return: LH_OK, or an error code with a message available from lh_last_error().  Argument
  *     checks run before any launch.  Faults inside kernels surface at the caller's next
  *     synchronization, as usual in HIP.  NaN or Inf in any input gives undefined results.

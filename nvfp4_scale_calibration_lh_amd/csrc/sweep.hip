@@ -11,29 +11,35 @@
 // and the block keeps the argmin (lowest code on ties).
 //
 // MI355X design
-//  * Full form: one wave per block, 16 candidates per MFMA tile (8 tiles cover the 126 codes).
-//    Lane l owns candidate l%16 of the tile and elements 4*(l/16)..+3.  The lane quantizes its 4
-//    elements (r = w * (1/s) in fp32, then the gfx950 FP4 convert, which rounds to nearest-even
-//    on the E2M1 grid and saturates at 6, and the FP4->fp32 convert back), forms
-//    e = fma(q, s, -w), and four chained v_mfma_f32_16x16x4_f32 compute H e + 2b for the 16
-//    candidates (H_n is the A operand, resident in registers for the whole column; the K index
-//    is permuted so that each lane's output rows are exactly its own 4 elements).  The quadratic
-//    form and an error bound are reduced across the 4 lane groups with permlane swaps; the
-//    argmin over the 16 candidate lanes uses DPP row rotations.  Quantization of the next tile
-//    is issued before the current tile's MFMA result is consumed.  b = P_n w and |P_n||w| come
-//    from the same MFMA shape once per 16-row tile.
+//  * Full form: one wave per block column n (H_n is loaded once and kept in registers) walking 32
+//    rows c; per block, 8 tiles of 16 candidates cover the 126 codes.  Lane l owns candidate
+//    l%16 of a tile and elements 4*(l/16)..+3.  The lane quantizes its 4 elements in fp32
+//    (r = w * (1/s), the gfx950 FP4 convert, which rounds to nearest-even on the E2M1 grid and
+//    saturates at 6, and the convert back), and forms e = fma(q, s, -w).
+//  * The contraction H_n e is reorganized so the matrix cores see exact small integers:
+//    (H e)_i = s (H q)_i - (H w)_i, where q holds E2M1 grid values times a power of 4 (at most
+//    2 significant bits, exact in bf16).  H_n is split once per column into three bf16 pieces
+//    (H1 + H2 + H3 equals H to 2^-27 relative), so two chained v_mfma_f32_16x16x32_bf16 with
+//    K slots [H1 | H2] and [H3 | 0] give H q for 16 candidates with exact products and fp32
+//    accumulation.  H w (and P w, |P||w| in the coupled form) comes from v_mfma_f32_16x16x4_f32
+//    once per 16-row tile.  The loss L = e^T (H e + 2 P w) is a 4-term dot per lane reduced over
+//    the 4 lane groups with permlane swaps; the argmin over lanes uses DPP row rotations and
+//    permlane swaps.  Quantization of the next tile is issued before the current tile's MFMA
+//    result is consumed.
 //  * Diagonal form: VALU only (there is no contraction to map onto MFMA); lane l scores
 //    candidates l+1 and l+65 over all 16 elements, whose weights are wave-uniform.
 //  * Exactness.  The float32 pass is a filter: each candidate carries a rigorous bound c*A_k on
-//    its rounding error (A_k = (sum|e_i| dmax_i)^2 + 2|e|^T(|P||w|), dmax_i^2 = max_j |H_ij|, or
-//    L_k itself in the diagonal form).  If exactly one candidate can be the minimum, it is the
-//    exact argmin; otherwise the block's code is left at 0 and a second kernel re-scores it in
-//    float64 with exact quotient rounding.  The fp32 quotient w*(1/s) can fall on the wrong side
-//    of an E2M1 rounding midpoint m only when |w|/s_k is within a few ulps of m, i.e. when
-//    |w|/(m g) is within a few ulps of an E4M3 value; once per block every (element, midpoint)
-//    pair is tested, and for a flagged pair the one affected candidate gets the exact decision
-//    (the sign of fma(m, s_k, -|w|)) in place of its fp32 quotient.  The result is the argmin of
-//    the float64 objective.
+//    its rounding error (A_k = S_e (4 S_e + S_w) + 2|e|^T(|P||w|) with S_e = sum_i |e_i| d_i,
+//    S_w = sum_i |w_i| d_i and d_i^2 = max_j max(|H_ij|, |H_ji|); L_k itself in the diagonal
+//    form).  If exactly one candidate can be
+//    the minimum it is the exact argmin; with 2 to 4 contenders the wave re-scores them in
+//    float64 with exact quantization; otherwise the block's code is left at 0 and a second
+//    kernel re-scores all 126 candidates in float64.  The fp32 quotient w*(1/s) can fall on the
+//    wrong side of an E2M1 rounding midpoint m only when |w|/s_k is within a few ulps of m, i.e.
+//    when |w|/(m g) is within a few ulps of an E4M3 value; once per block every (element,
+//    midpoint) pair is tested, and for a flagged pair the one affected candidate gets the exact
+//    decision (the sign of fma(m, s_k, -|w|)) in place of its fp32 quotient.  The result is the
+//    argmin of the float64 objective.
 #include "lh_internal.hpp"
 
 #include <type_traits>
