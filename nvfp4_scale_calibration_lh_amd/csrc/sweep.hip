@@ -226,6 +226,9 @@ struct FullLds {
   float w[16][16];     // current 16-row tile: w[row][elem]
   float g[16][16];     // (H w - 2 P w)[row][elem]
   float pw[16][16];    // (|P| |w|)[row][elem]
+  float b[16][16];     // (P w)[row][elem]           } the loss of the tile's
+  float ws[16];        // winner's scale per row      } filter-decided winners
+  unsigned short wn[16][4];   // winner's signed nibbles per row and lane group
   double ex[4][16];    // float64 refinement: e of up to 4 contenders
 };
 
@@ -247,8 +250,10 @@ __device__ inline float group_sum(float v) {
   return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
 
+// 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
+// more and drop to 3 waves, which costs about 10%; the cap spills two values outside the row loop).
 template <bool BF16, bool COUPLED>
-__global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
     uint8_t* __restrict__ fp4, float* __restrict__ loss) {
@@ -346,12 +351,16 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
     for (int t = 0; t < 4; ++t) {                  // lane holds elements 4gg+t of row i
       L.w[i][4 * gg + t] = wt[t];
       L.g[i][4 * gg + t] = coupled ? fmaf(-2.0f, bt[t], hw[t]) : hw[t];
-      if (COUPLED) L.pw[i][4 * gg + t] = pwt[t];
+      if (COUPLED) {
+        L.pw[i][4 * gg + t] = pwt[t];
+        L.b[i][4 * gg + t] = bt[t];
+      }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
     const int rows_here = (int)min((int64_t)16, c_end - c0);
+    unsigned emitted = 0u;                           // rows whose winner came from the filter
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
       const int64_t oblk = (g * cout + c) * nb + n;
@@ -485,15 +494,18 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
       const unsigned long long M1 = __ballot(fmaf(-kErrC, Aq[1], Lq[1]) <= U);
       const int cnt = __popcll(M0) + __popcll(M1);
       if (cnt == 1) {
-        // unique winner: emit its codes.  Its reciprocal scale comes from the lane that owns it.
+        // unique winner: emit its codes.  Its scale and reciprocal come from the lane that owns
+        // it (tiles >= 1 apply their power of 4 exactly).
         const int kb0 = k_best - 1;
         const int src = kb0 & 15;
-        float iw;
+        float iw, sw;
         if (kb0 < 16) {
           iw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(is0), src));
+          sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s0), src));
         } else {
           const float sc = (float)(1u << (2 * ((kb0 >> 4) - 1)));
           iw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(is1), src)) / sc;
+          sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), src)) * sc;
         }
         float rw[4];
 #pragma unroll
@@ -508,9 +520,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
         nb4 |= (w[0] < 0.0f ? 0x8u : 0u) | (w[1] < 0.0f ? 0x80u : 0u) |
                (w[2] < 0.0f ? 0x800u : 0u) | (w[3] < 0.0f ? 0x8000u : 0u);
         if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
-        if (lane == 0) {
-          code[oblk] = (uint8_t)k_best;
-          if (loss) loss[oblk] = mL;
+        if (lane == 0) code[oblk] = (uint8_t)k_best;
+        if (loss) {
+          // The filter's mL carries the cancellation error of s(Hq) - Hw; the reported loss is
+          // re-evaluated from the winner's codes once per tile (below).
+          if (i == 0) L.wn[rr][gg] = (unsigned short)nb4;
+          if (lane == 0) L.ws[rr] = sw;
+          emitted |= 1u << rr;
         }
       } else if (cnt <= 4) {
         // 2..4 contenders: re-score them exactly in float64, 16 lanes (one per element) each
@@ -565,6 +581,31 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full(
       } else {
         if (lane == 0) code[oblk] = 0;              // many contenders: float64 pass
       }
+    }
+    if (emitted) {
+      // Loss of the filter-decided winners of this tile from their codes: e* = q s* - w, then
+      // (H e*) on fp32 MFMA in the layout of H w (lane: row i, elements 4gg..4gg+3) and
+      // e*^T (H e* + 2 P w).
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const bool on = (emitted >> i) & 1u;
+      const unsigned nbits = on ? (unsigned)L.wn[i][gg] : 0u;
+      const float sw = on ? L.ws[i] : 0.0f;
+      const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nbits, 1.0f, 0);
+      const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nbits, 1.0f, 1);
+      const float qv[4] = {q01[0], q01[1], q23[0], q23[1]};
+      float ev[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ev[t] = on ? fmaf(qv[t], sw, -L.w[i][4 * gg + t]) : 0.0f;
+      v4f he = zero4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) he = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], ev[t], he, 0, 0, 0);
+      float part = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        part = fmaf(ev[t], coupled ? fmaf(2.0f, L.b[i][4 * gg + t], he[t]) : he[t], part);
+      const float Lrow = group_sum(part);
+      if (gg == 0 && on) loss[((g * cout + c0 + i) * nb) + n] = Lrow;
     }
     __builtin_amdgcn_wave_barrier();
   }
