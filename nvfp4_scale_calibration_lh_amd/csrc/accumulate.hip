@@ -7,21 +7,29 @@
 //                                                      What / How)
 //
 // Design (HBM-bound streaming contraction over tokens):
-//  * A workgroup owns a tile of kAccTileRows rows x 64 channels (four 16-channel blocks, one per
-//    wave).  X is read once, with 16-byte coalesced loads (each 64-channel row slice is one
-//    128-byte line), staged through LDS, and each wave gathers its block's operand with the token
-//    index along K.
+//  * Work is split into 64-channel slices (four 16-channel blocks) and row ranges.  A wave streams
+//    32-row chunks of its range with coalesced 16-byte loads (a 64-channel row slice is one
+//    128-byte line), keeps the next chunk's loads in flight, stages the chunk in its own LDS
+//    buffer and gathers, for each of the four blocks, the MFMA operand with the token index along
+//    K.
 //  * bf16 inputs use v_mfma_f32_16x16x32_bf16: 32 tokens per instruction, products exact, fp32
 //    accumulation.  The operand A[i][k] = x_{t_k}[i] is also B[k][i], so one register set feeds
 //    both.  fp32 inputs use v_mfma_f32_16x16x4_f32 with the same mapping.
 //  * The cross matrix uses D = X_q - X formed in fp32 (exact for bf16 data) and split into a bf16
 //    high part (truncation) and the exact bf16 remainder, so P = X_q^T D_hi + X_q^T D_lo needs two
 //    more MFMAs and no catastrophic cancellation.
-//  * Rows of one tile can belong to several groups (MoE experts).  The tile is walked segment by
-//    segment; a group wholly inside the tile is finalized in place (beta, 1/T_g), a group that
-//    crosses a tile edge leaves its partial sums in scratch slot 0 (it started earlier) or 1 (it
-//    continues later), and k_acc_finalize adds the pieces of each such group in tile order.
-//    Nothing uses atomics, so results are bit-identical run to run.
+//  * Dense layer (one group): a workgroup owns a tile of R rows whose chunks its four waves take
+//    in turn; the waves add their sums in LDS at the end.  With several tiles, each tile stores
+//    its sums and a second kernel adds them in tile order, one thread per output entry.
+//  * Grouped rows (MoE experts): a small planning kernel cuts every group into pieces of at most
+//    R rows (a group without rows is one empty piece); each wave owns one piece, so a group of at
+//    most R rows is finished by one wave with no synchronization.  Pieces of larger groups leave
+//    partial sums and the last of them to finish adds them in piece order.
+//  * Pieces' partial sums cross workgroups through agent-scope relaxed atomic stores and loads (coherent
+//    across the per-XCD L2 caches without whole-cache flushes), ordered by waiting for the stores
+//    before an arrival counter is incremented; the last arrival clears the counter for the next
+//    call.  Summation orders never depend on timing: results are bit-identical run to run.
+//  * When only the importance is wanted, partial sums keep just the 16 diagonal entries.
 #include "lh_internal.hpp"
 
 namespace lh {
@@ -32,271 +40,525 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 32;      // rows staged per step
-constexpr int kCh = 64;         // channels per workgroup
+constexpr int kChunk = 32;          // rows per chunk (one 16x16x32 MFMA per block)
+constexpr int kCh = 64;             // channels per slice (four blocks)
 constexpr int kPitchH = kCh + 8;    // bf16 LDS row pitch (halves); 144 bytes keeps 16-byte alignment
 constexpr int kPitchF = kCh + 4;    // fp32 LDS row pitch (floats)
+constexpr int kEntry = 4;           // int64 words of one piece-table entry
 
-// Row offset j of the group table; a dense layer passes no table (one group of all rows).
-__device__ inline int64_t offv(const int64_t* off, int64_t j, int64_t rows) {
-  return off ? off[j] : (j == 0 ? 0 : rows);
+template <bool BF16>
+struct Geo {
+  static constexpr int kLoads = BF16 ? 4 : 8;             // 16-byte loads per lane per chunk
+  static constexpr int kRowsPerLoad = BF16 ? 8 : 4;       // rows one wave-wide load covers
+  static constexpr int kWords = BF16 ? kChunk * kPitchH / 2 : kChunk * kPitchF;  // per matrix
+};
+
+__device__ inline void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ inline int64_t find_group(const int64_t* off, int64_t G, int64_t t, int64_t rows) {
-  // largest g with off[g] <= t; then off[g+1] > t because off[G] = rows > t
-  int64_t lo = 0, hi = G - 1;
-  while (lo < hi) {
-    int64_t mid = (lo + hi + 1) >> 1;
-    if (offv(off, mid, rows) <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+__device__ inline float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_agent2(float* p, float a, float b) {   // 8-byte aligned pair
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void ld_agent2(const float* p, float& a, float& b) {
+  const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a = __uint_as_float((unsigned)v);
+  b = __uint_as_float((unsigned)(v >> 32));
+}
+__device__ inline unsigned arrive(unsigned* c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void clear(unsigned* c) {
+  __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
 __device__ inline float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// Writes one wave's 16x16 result (lane layout of the 16x16 MFMA: lane l holds rows 4*(l/16)+r,
-// column l%16) either finalized into out (beta, /T) or raw into a scratch slot.
-__device__ inline void store_block(const v4f acc, float* dst, bool final_, float beta, float T,
-                                   int lane) {
-  const int i = lane & 15, gg = lane >> 4;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int idx = (4 * gg + r) * 16 + i;
-    float v = acc[r];
-    if (final_) {
-      v = v / T;
-      if (beta != 0.0f) v = beta * dst[idx] + v;
-    }
-    dst[idx] = v;
-  }
-}
-
-__device__ inline void store_imp(const v4f acc, float* imp_blk, float beta, int lane) {
-  const int i = lane & 15, gg = lane >> 4;
-  const int r = i - 4 * gg;
-  if (r >= 0 && r < 4) {
-    float v = acc[r];
-    if (beta != 0.0f) v = beta * imp_blk[i] + v;
-    imp_blk[i] = v;
-  }
-}
-
+// One wave's streaming contraction of rows [r0, r1) of a 64-channel slice into four blocks of
+// accumulators, using the wave's own LDS stage.  Chunks are taken with a stride of `step` chunks
+// starting at chunk `first` (counted from r0), so several waves can share a range.
 template <bool BF16, bool ACT>
-__global__ __launch_bounds__(kThreads) void k_acc_tile(
-    const void* __restrict__ Xv, const void* __restrict__ Xqv, int64_t rows, int64_t cin,
-    const int64_t* __restrict__ off, int64_t G, float beta, float* __restrict__ H,
-    float* __restrict__ P, float* __restrict__ imp, float* __restrict__ ws, int64_t nb) {
-  constexpr int kTiles = ACT ? 2 : 1;
-  constexpr int kTileElems = BF16 ? kChunk * kPitchH / 2 : kChunk * kPitchF;  // in 4-byte words
-  __shared__ __attribute__((aligned(16))) unsigned lds[kTiles][kTileElems];
+struct Streamer {
+  using Gm = Geo<BF16>;
+  static constexpr int kM = ACT ? 2 : 1;
+  const char* X;
+  const char* Xq;
+  int64_t cin, ch0;
+  int nblk, lane, i, gg;
+  unsigned* stage;              // [kM][kWords] of this wave
+  v4f accH[4], accP[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, gg = lane >> 4;
-  const int64_t tile = blockIdx.x;
-  const int64_t t0 = tile * kAccTileRows;
-  const int64_t t1 = min(rows, t0 + kAccTileRows);
-  const int64_t ch0 = (int64_t)blockIdx.y * kCh;
-  const int64_t n = blockIdx.y * 4 + wave;        // this wave's block
-  const bool wave_on = n < nb;
-
-  // loader mapping: bf16 -> 8 threads per 64-channel row, 32 rows; fp32 -> 16 threads per row,
-  // 16 rows per pass, two passes.
-  constexpr int kPass = BF16 ? 1 : 2;
-  const int lrow = BF16 ? (tid >> 3) : (tid >> 4);
-  const int lcol = BF16 ? (tid & 7) * 8 : (tid & 15) * 4;          // in elements
-  const bool col_on = ch0 + lcol < cin;
-  const int esz = BF16 ? 2 : 4;
-  const char* Xb = (const char*)Xv;
-  const char* Xqb = (const char*)Xqv;
-
-  v4u pre[kTiles][kPass];
-  auto load = [&](int64_t r0, int64_t rend) {
+  __device__ void run(int64_t r0, int64_t r1, int first, int step) {
 #pragma unroll
-    for (int p = 0; p < kPass; ++p) {
-      const int64_t r = r0 + lrow + p * 16;
-      const bool on = col_on && r < rend;
-      const int64_t byte = (r * cin + ch0 + lcol) * esz;
+    for (int b = 0; b < 4; ++b) accH[b] = accP[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (r1 <= r0) return;
+    const int nchunks = (int)((r1 - r0 + kChunk - 1) / kChunk);
+    const int lrow = BF16 ? (lane >> 3) : (lane >> 4);
+    const int lcol = BF16 ? (lane & 7) * 8 : (lane & 15) * 4;
+    const bool col_on = ch0 + lcol < cin;
+    const int esz = BF16 ? 2 : 4;
+    v4u pre[kM][Gm::kLoads];
+    // Every lane issues the same loads on every path (rows past the range re-read its last row,
+    // channels past cin read channel 0; both are zeroed when staged).
+    auto issue = [&](int j) {
 #pragma unroll
-      for (int m = 0; m < kTiles; ++m) {
-        const char* base = (m == 0) ? (ACT ? Xqb : Xb) : Xb;    // act-aware: tile 0 = X_q, 1 = X
-        pre[m][p] = on ? __builtin_nontemporal_load((const v4u*)(base + byte)) : v4u{0u, 0u, 0u, 0u};
+      for (int q = 0; q < Gm::kLoads; ++q) {
+        const int64_t r = min(r0 + (int64_t)j * kChunk + lrow + q * Gm::kRowsPerLoad, r1 - 1);
+        const int64_t byte = (r * cin + (col_on ? ch0 + lcol : 0)) * esz;
+#pragma unroll
+        for (int m = 0; m < kM; ++m) {
+          const char* base = (m == 0) ? (ACT ? Xq : X) : X;    // act-aware: matrix 0 = X_q, 1 = X
+          pre[m][q] = __builtin_nontemporal_load((const v4u*)(base + byte));
+        }
       }
+    };
+    int j = first;
+    if (j < nchunks) issue(j);
+    for (; j < nchunks; j += step) {
+      const int64_t c0 = r0 + (int64_t)j * kChunk;
+#pragma unroll
+      for (int q = 0; q < Gm::kLoads; ++q) {
+        const int row = lrow + q * Gm::kRowsPerLoad;
+        const bool on = col_on && c0 + row < r1;
+        const int word = BF16 ? (row * kPitchH + lcol) / 2 : row * kPitchF + lcol;
+#pragma unroll
+        for (int m = 0; m < kM; ++m) *(v4u*)&stage[m * Gm::kWords + word] = on ? pre[m][q] : v4u{0u, 0u, 0u, 0u};
+      }
+      if (j + step < nchunks) issue(j + step);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      contract();
     }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int p = 0; p < kPass; ++p) {
-      const int row = lrow + p * 16;
-      const int word = BF16 ? (row * kPitchH + lcol) / 2 : row * kPitchF + lcol;
-#pragma unroll
-      for (int m = 0; m < kTiles; ++m) *(v4u*)&lds[m][word] = pre[m][p];
-    }
-  };
+  }
 
-  int64_t g = find_group(off, G, t0, rows);
-  int64_t a = t0;
-  while (a < t1 && g < G) {
-    const int64_t gbeg = offv(off, g, rows), gend = offv(off, g + 1, rows);
-    const int64_t b = max(a, min(gend, t1));   // never below a, even for offsets outside the contract
-    v4f accH = {0.f, 0.f, 0.f, 0.f};
-    v4f accP = {0.f, 0.f, 0.f, 0.f};
-
-    load(a, b);
-    for (int64_t r0 = a; r0 < b; r0 += kChunk) {
-      __syncthreads();                 // every wave is done with the previous chunk
-      stash();
-      __syncthreads();
-      if (r0 + kChunk < b) load(r0 + kChunk, b);   // in flight while this chunk is contracted
-      if (wave_on) {
-        if (BF16) {
-          const unsigned short* t0h = (const unsigned short*)&lds[0][0];
-          v4u aq;
+  // Adds the staged chunk (rows past the range are zero) to the four blocks' accumulators.
+  __device__ void contract() {
+    if (BF16) {
+      const unsigned short* th = (const unsigned short*)stage;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const unsigned lo = t0h[(8 * gg + 2 * j) * kPitchH + 16 * wave + i];
-            const unsigned hi = t0h[(8 * gg + 2 * j + 1) * kPitchH + 16 * wave + i];
-            aq[j] = lo | (hi << 16);
+      for (int b = 0; b < 4; ++b) {
+        if (b >= nblk) break;
+        v4u aq;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const unsigned a0 = th[(8 * gg + 2 * u) * kPitchH + 16 * b + i];
+          const unsigned a1 = th[(8 * gg + 2 * u + 1) * kPitchH + 16 * b + i];
+          aq[u] = a0 | (a1 << 16);
+        }
+        const v8bf A = __builtin_bit_cast(v8bf, aq);
+        accH[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, accH[b], 0, 0, 0);
+        if (ACT) {
+          const unsigned short* tx = (const unsigned short*)(stage + (kM - 1) * Gm::kWords);
+          v4u dh, dl;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const unsigned x0 = tx[(8 * gg + 2 * u) * kPitchH + 16 * b + i];
+            const unsigned x1 = tx[(8 * gg + 2 * u + 1) * kPitchH + 16 * b + i];
+            const float d0 = bf16_lo(aq[u]) - bf16_lo(x0);     // exact: both are bf16
+            const float d1 = bf16_hi(aq[u]) - bf16_lo(x1);
+            const unsigned h0 = __float_as_uint(d0) & 0xFFFF0000u;
+            const unsigned h1 = __float_as_uint(d1) & 0xFFFF0000u;
+            const float l0 = d0 - __uint_as_float(h0);         // exact remainder
+            const float l1 = d1 - __uint_as_float(h1);
+            dh[u] = (h0 >> 16) | h1;
+            dl[u] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
           }
-          const v8bf A = __builtin_bit_cast(v8bf, aq);
-          accH = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, accH, 0, 0, 0);
+          accP[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dh), accP[b], 0, 0, 0);
+          accP[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dl), accP[b], 0, 0, 0);
+        }
+      }
+    } else {
+      const float* tf = (const float*)stage;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b >= nblk) break;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const float q = tf[(4 * s + gg) * kPitchF + 16 * b + i];
+          accH[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(q, q, accH[b], 0, 0, 0);
           if (ACT) {
-            const unsigned short* t1h = (const unsigned short*)&lds[kTiles - 1][0];
-            v4u dh, dl;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const unsigned x0 = t1h[(8 * gg + 2 * j) * kPitchH + 16 * wave + i];
-              const unsigned x1 = t1h[(8 * gg + 2 * j + 1) * kPitchH + 16 * wave + i];
-              const float d0 = bf16_lo(aq[j]) - bf16_lo(x0);     // exact: both are bf16
-              const float d1 = bf16_hi(aq[j]) - bf16_lo(x1);
-              const unsigned h0 = __float_as_uint(d0) & 0xFFFF0000u;
-              const unsigned h1 = __float_as_uint(d1) & 0xFFFF0000u;
-              const float l0 = d0 - __uint_as_float(h0);         // exact remainder
-              const float l1 = d1 - __uint_as_float(h1);
-              dh[j] = (h0 >> 16) | h1;
-              dl[j] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
-            }
-            accP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dh), accP, 0, 0, 0);
-            accP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dl), accP, 0, 0, 0);
-          }
-        } else {
-          const float* t0f = (const float*)&lds[0][0];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const float q = t0f[(4 * s + gg) * kPitchF + 16 * wave + i];
-            accH = __builtin_amdgcn_mfma_f32_16x16x4f32(q, q, accH, 0, 0, 0);
-            if (ACT) {
-              const float x = ((const float*)&lds[kTiles - 1][0])[(4 * s + gg) * kPitchF + 16 * wave + i];
-              accP = __builtin_amdgcn_mfma_f32_16x16x4f32(q, q - x, accP, 0, 0, 0);
-            }
+            const float x = ((const float*)(stage + (kM - 1) * Gm::kWords))[(4 * s + gg) * kPitchF + 16 * b + i];
+            accP[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(q, q - x, accP[b], 0, 0, 0);
           }
         }
       }
     }
+  }
+};
 
-    if (wave_on) {
-      const bool head = gbeg < t0, tail = gend > t1;
-      const float T = (float)(gend - gbeg);
-      const int64_t blk = g * nb + n;
-      if (!head && !tail) {
-        if (H) store_block(accH, H + blk * 256, true, beta, T, lane);
-        if (ACT) store_block(accP, P + blk * 256, true, beta, T, lane);
-        if (imp) store_imp(accH, imp + g * nb * 16 + n * 16, beta, lane);
-      } else {
-        const int slot = head ? 0 : 1;
-        float* w = ws + ((tile * 2 + slot) * kTiles * nb + n) * 256;
-        store_block(accH, w, false, 0.f, 1.f, lane);
-        if (ACT) store_block(accP, w + nb * 256, false, 0.f, 1.f, lane);
-      }
+// Output writer for one finished block (lane layout of the MFMA result: lane holds rows 4*gg + r,
+// column i): H or P (sum / T, beta), and the importance from H's diagonal.
+template <bool DIAG>
+__device__ inline void emit_block(int m, const v4f s, int64_t T, int64_t blk, float beta, float* H,
+                                  float* P, float* imp_blk, int i, int gg) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * gg + r;
+    if (m == 0 && imp_blk && row == i) imp_blk[i] = beta != 0.0f ? beta * imp_blk[i] + s[r] : s[r];
+    if (!DIAG) {
+      float* o = (m == 0 ? H : P) + blk * 256 + row * 16 + i;
+      const float v = T > 0 ? s[r] / (float)T : 0.0f;
+      *o = beta != 0.0f ? beta * *o + v : v;
     }
-    a = b;
-    ++g;
-    while (g < G && offv(off, g + 1, rows) <= a) ++g;     // skip empty groups
   }
 }
 
-// One workgroup per (group, 4 blocks): combines the partial sums of groups that cross tile
-// edges, in tile order, and writes empty groups (T_g = 0: only the beta term remains).
-template <bool ACT>
-__global__ __launch_bounds__(kThreads) void k_acc_finalize(
-    const int64_t* __restrict__ off, int64_t rows, int64_t nb, float beta, float* __restrict__ H,
-    float* __restrict__ P, float* __restrict__ imp, const float* __restrict__ ws) {
-  constexpr int kMats = ACT ? 2 : 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t g = blockIdx.x;
-  const int64_t n = blockIdx.y * 4 + wave;
-  if (n >= nb) return;
-  const int64_t gbeg = offv(off, g, rows), gend = offv(off, g + 1, rows);
-  if (gbeg < 0 || gend > rows || gbeg > gend) return;     // offsets outside the contract
-  const int64_t T = gend - gbeg;
-  const int64_t blk = g * nb + n;
-  float* outs[2] = {H ? H + blk * 256 : nullptr, ACT ? P + blk * 256 : nullptr};
-  float* imp_blk = imp ? imp + g * nb * 16 + n * 16 : nullptr;
-  if (T == 0) {
-    for (int m = 0; m < kMats; ++m) {
-      if (!outs[m]) continue;
-      for (int q = 0; q < 4; ++q) {
-        const int idx = lane * 4 + q;
-        outs[m][idx] = beta != 0.0f ? beta * outs[m][idx] : 0.0f;
-      }
-    }
-    if (imp_blk && lane < 16) imp_blk[lane] = beta != 0.0f ? beta * imp_blk[lane] : 0.0f;
+// Partial sums of one block: lane-major (lane l's four accumulator values at 4l..4l+3), or the 16
+// diagonal entries (entry c = H[c][c]) when only the importance is produced.
+template <bool DIAG>
+__device__ inline void store_partial(float* w, const v4f s, int lane, int i, int gg) {
+  if (DIAG) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * gg + r == i) st_agent(w + i, s[r]);
+  } else {
+    st_agent2(w + 4 * lane, s[0], s[1]);
+    st_agent2(w + 4 * lane + 2, s[2], s[3]);
+  }
+}
+template <bool DIAG>
+__device__ inline v4f load_partial(const float* w, int lane, int i, int gg) {
+  v4f s = {0.f, 0.f, 0.f, 0.f};
+  if (DIAG) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * gg + r == i) s[r] = ld_agent(w + i);
+  } else {
+    float a, b, c, d;
+    ld_agent2(w + 4 * lane, a, b);
+    ld_agent2(w + 4 * lane + 2, c, d);
+    s = v4f{a, b, c, d};
+  }
+  return s;
+}
+
+// Sum of n partial blocks w0, w0 + stride, ... in order, eight loads in flight.
+template <bool DIAG>
+__device__ inline v4f sum_partials(const float* w0, int64_t stride, int64_t n, int lane, int i, int gg) {
+  v4f s = {0.f, 0.f, 0.f, 0.f};
+  int64_t t = 0;
+  for (; t + 8 <= n; t += 8) {
+    v4f p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = load_partial<DIAG>(w0 + (t + u) * stride, lane, i, gg);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += p[u];
+  }
+  for (; t < n; ++t) s += load_partial<DIAG>(w0 + t * stride, lane, i, gg);
+  return s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Dense layer: grid (tiles, slices), four waves per tile, chunks interleaved between the waves.
+// Partial layout: [slice][tile][m][block][kPart].
+// ---------------------------------------------------------------------------------------------
+template <bool BF16, bool ACT, bool DIAG>
+__global__ __launch_bounds__(kThreads) void k_acc_dense(
+    const void* __restrict__ Xv, const void* __restrict__ Xqv, int64_t rows, int64_t cin,
+    int64_t R, float beta, float* __restrict__ H, float* __restrict__ P, float* __restrict__ imp,
+    float* __restrict__ ws, int64_t nb) {
+  using St = Streamer<BF16, ACT>;
+  constexpr int kM = St::kM;
+  constexpr int kPart = DIAG ? 16 : 256;
+  constexpr int kStage = 4 * kM * Geo<BF16>::kWords;
+  constexpr int kComb = 4 * 4 * 64 * 4;       // [wave][block][lane] v4f, in words
+  __shared__ __attribute__((aligned(16))) unsigned smem[kStage > kComb ? kStage : kComb];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, gg = lane >> 4;
+  const int64_t tiles = gridDim.x, tile = blockIdx.x, slice = blockIdx.y;
+  const int64_t n0 = slice * 4;
+  const int nblk = (int)min((int64_t)4, nb - n0);
+  const int64_t t0 = tile * R, t1 = min(rows, t0 + R);
+
+  St st{(const char*)Xv, (const char*)Xqv, cin, slice * kCh, nblk, lane, i, gg,
+        smem + wave * kM * Geo<BF16>::kWords, {}, {}};
+  st.run(t0, t1, wave, 4);
+
+  const bool mine = wave < nblk;
+  const int64_t blk = n0 + wave;              // group 0
+  float* imp_blk = imp ? imp + blk * 16 : nullptr;
+  v4f* comb = (v4f*)smem;
+  v4f tot[kM];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    __syncthreads();                          // stage (or previous comb) no longer read
+#pragma unroll
+    for (int b = 0; b < 4; ++b) comb[(wave * 4 + b) * 64 + lane] = m == 0 ? st.accH[b] : st.accP[b];
+    __syncthreads();
+    tot[m] = ((comb[(0 * 4 + wave) * 64 + lane] + comb[(1 * 4 + wave) * 64 + lane]) +
+              comb[(2 * 4 + wave) * 64 + lane]) + comb[(3 * 4 + wave) * 64 + lane];
+  }
+  if (tiles == 1) {
+    if (mine)
+#pragma unroll
+      for (int m = 0; m < kM; ++m) emit_block<DIAG>(m, tot[m], rows, blk, beta, H, P, imp_blk, i, gg);
     return;
   }
-  const int64_t ta = gbeg / kAccTileRows, tb = (gend - 1) / kAccTileRows;
-  if (ta == tb) return;                   // finalized by its tile
-  for (int m = 0; m < kMats; ++m) {
-    float s[4];
-    for (int q = 0; q < 4; ++q) s[q] = ws[((ta * 2 + 1) * kMats * nb + m * nb + n) * 256 + lane * 4 + q];
-    for (int64_t t = ta + 1; t <= tb; ++t)
-      for (int q = 0; q < 4; ++q) s[q] += ws[((t * 2 + 0) * kMats * nb + m * nb + n) * 256 + lane * 4 + q];
-    for (int q = 0; q < 4; ++q) {
-      const int idx = lane * 4 + q;
-      if (m == 0 && imp_blk && (idx >> 4) == (idx & 15)) {
-        const int c = idx & 15;
-        imp_blk[c] = beta != 0.0f ? beta * imp_blk[c] + s[q] : s[q];
-      }
-      if (outs[m]) {
-        const float v = s[q] / (float)T;
-        outs[m][idx] = beta != 0.0f ? beta * outs[m][idx] + v : v;
+  // several tiles: plain stores of this tile's sums; k_acc_dense_sum adds them after this kernel
+  if (mine) {
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      float* w = ws + (((slice * tiles + tile) * kM + m) * 4 + wave) * kPart;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (DIAG) {
+          if (4 * gg + r == i) w[i] = tot[m][r];
+        } else {
+          w[4 * lane + r] = tot[m][r];
+        }
       }
     }
   }
+}
+
+// Dense layer with several tiles: one thread per output entry adds the tiles' sums in tile order
+// (eight loads in flight) and writes H, P (sum / rows, beta) and the importance.
+template <bool ACT, bool DIAG>
+__global__ __launch_bounds__(kThreads) void k_acc_dense_sum(
+    const float* __restrict__ ws, int64_t tiles, int64_t slices, int64_t nb, int64_t rows,
+    float beta, float* __restrict__ H, float* __restrict__ P, float* __restrict__ imp) {
+  constexpr int kM = ACT ? 2 : 1;
+  constexpr int kPart = DIAG ? 16 : 256;
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // over [slice][m][block][kPart]
+  if (e >= slices * kM * 4 * kPart) return;
+  const int64_t q = e % kPart, b = (e / kPart) % 4, m = (e / (4 * kPart)) % kM, slice = e / (kM * 4 * kPart);
+  const int64_t n = slice * 4 + b;
+  if (n >= nb) return;
+  const float* w0 = ws + ((slice * tiles * kM + m) * 4 + b) * kPart + q;
+  const int64_t stride = (int64_t)kM * 4 * kPart;
+  float s = 0.0f;
+  int64_t t = 0;
+  for (; t + 8 <= tiles; t += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = w0[(t + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; t < tiles; ++t) s += w0[t * stride];
+  if (DIAG) {
+    float* o = imp + n * 16 + q;
+    *o = beta != 0.0f ? beta * *o + s : s;
+    return;
+  }
+  // entry q of the lane-major layout: lane l = q / 4 holds row 4 * (l / 16) + q % 4, column l % 16
+  const int64_t l = q / 4, row = 4 * (l / 16) + q % 4, col = l % 16;
+  if (m == 0 && imp && row == col) {
+    float* o = imp + n * 16 + col;
+    *o = beta != 0.0f ? beta * *o + s : s;
+  }
+  float* o = (m == 0 ? H : P) + n * 256 + row * 16 + col;
+  const float v = rows > 0 ? s / (float)rows : 0.0f;
+  *o = beta != 0.0f ? beta * *o + v : v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grouped rows: planning.  One workgroup cuts every group into pieces of at most R rows and
+// writes the piece table: word 0 = number of pieces; entry p (at 4 + 4p) = {group, first row,
+// end row, piece index in group << 32 | pieces in group}.  Pieces of one group are consecutive.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict__ off, int64_t G,
+                                                       int64_t rows, int64_t R, int64_t cap,
+                                                       int64_t* __restrict__ table) {
+  __shared__ int64_t scan[kThreads];
+  const int tid = threadIdx.x;
+  const int64_t per = (G + kThreads - 1) / kThreads;
+  const int64_t g0 = min(G, tid * per), g1 = min(G, g0 + per);
+  // rows of group g, clamped to [0, rows] so that offsets outside the contract never address
+  // memory outside X
+  auto span = [&](int64_t g, int64_t& a, int64_t& e) {
+    a = min(max(off[g], (int64_t)0), rows);
+    e = min(max(off[g + 1], a), rows);
+  };
+  auto npieces = [&](int64_t g) -> int64_t {
+    int64_t a, e;
+    span(g, a, e);
+    return e > a ? (e - a + R - 1) / R : 1;   // a group without rows is one empty piece
+  };
+  int64_t cnt = 0;
+  for (int64_t g = g0; g < g1; ++g) cnt += npieces(g);
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int d = 1; d < kThreads; d <<= 1) {    // inclusive scan
+    const int64_t v = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int64_t total = scan[kThreads - 1];
+  if (tid == 0) table[0] = total <= cap ? total : 0;      // more pieces only if offsets break the contract
+  if (total > cap) return;
+  int64_t p = scan[tid] - cnt;
+  for (int64_t g = g0; g < g1; ++g) {
+    int64_t a, e;
+    span(g, a, e);
+    const int64_t n = npieces(g);
+    for (int64_t k = 0; k < n; ++k, ++p) {
+      int64_t* t = table + kEntry + p * kEntry;
+      t[0] = g;
+      t[1] = min(e, a + k * R);
+      t[2] = min(e, a + (k + 1) * R);
+      t[3] = (k << 32) | n;
+    }
+  }
+}
+
+// Grouped rows: grid (ceil(capacity / 4), slices); wave w of workgroup x owns piece 4x + w.
+// Partial layout: [piece][slice][m][block][kPart]; counters: [group][slice].
+template <bool BF16, bool ACT, bool DIAG>
+__global__ __launch_bounds__(kThreads) void k_acc_pieces(
+    const void* __restrict__ Xv, const void* __restrict__ Xqv, int64_t cin,
+    const int64_t* __restrict__ table, float beta, float* __restrict__ H, float* __restrict__ P,
+    float* __restrict__ imp, float* __restrict__ ws, unsigned* __restrict__ counters, int64_t nb) {
+  using St = Streamer<BF16, ACT>;
+  constexpr int kM = St::kM;
+  constexpr int kPart = DIAG ? 16 : 256;
+  __shared__ __attribute__((aligned(16))) unsigned smem[4 * kM * Geo<BF16>::kWords];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, gg = lane >> 4;
+  const int64_t slices = gridDim.y, slice = blockIdx.y;
+  const int64_t p = (int64_t)blockIdx.x * 4 + wave;
+  if (p >= table[0]) return;                  // whole wave leaves; no workgroup barriers here
+  const int64_t* e = table + kEntry + p * kEntry;
+  const int64_t g = e[0], r0 = e[1], r1 = e[2];
+  const int64_t k = e[3] >> 32, npieces = e[3] & 0xFFFFFFFF;
+  const int64_t n0 = slice * 4;
+  const int nblk = (int)min((int64_t)4, nb - n0);
+
+  St st{(const char*)Xv, (const char*)Xqv, cin, slice * kCh, nblk, lane, i, gg,
+        smem + wave * kM * Geo<BF16>::kWords, {}, {}};
+  st.run(r0, r1, 0, 1);
+
+  const int64_t gbeg = table[kEntry + (p - k) * kEntry + 1];
+  const int64_t gend = table[kEntry + (p - k + npieces - 1) * kEntry + 2];
+  const int64_t T = gend - gbeg;
+  float* imp_g = imp ? imp + g * nb * 16 : nullptr;
+  // (block loops have a constant trip count so the accumulators stay in registers)
+  if (npieces == 1) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b >= nblk) break;
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+        emit_block<DIAG>(m, m == 0 ? st.accH[b] : st.accP[b], T, g * nb + n0 + b, beta, H, P,
+                         imp_g ? imp_g + (n0 + b) * 16 : nullptr, i, gg);
+    }
+    return;
+  }
+  auto part = [&](int64_t q, int m, int b) { return ws + (((q * slices + slice) * kM + m) * 4 + b) * kPart; };
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (b >= nblk) break;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) store_partial<DIAG>(part(p, m, b), m == 0 ? st.accH[b] : st.accP[b], lane, i, gg);
+  }
+  __builtin_amdgcn_s_waitcnt(0);              // the partial stores have completed
+  unsigned prev = 0;
+  if (lane == 0) prev = arrive(&counters[g * slices + slice]);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != (unsigned)(npieces - 1)) return;
+  // the group's last piece to arrive adds all pieces in order
+  const int64_t pfirst = p - k;
+  for (int b = 0; b < nblk; ++b)
+    for (int m = 0; m < kM; ++m)
+      emit_block<DIAG>(m, sum_partials<DIAG>(part(pfirst, m, b), slices * kM * 4 * kPart, npieces, lane, i, gg),
+                       T, g * nb + n0 + b, beta, H, P, imp_g ? imp_g + (n0 + b) * 16 : nullptr, i, gg);
+  if (lane == 0) clear(&counters[g * slices + slice]);
+}
+
+// Rows per tile of a dense layer: the longest of 256, 512, 1024 that still gives 2048 workgroups.
+int64_t dense_tile_rows(int64_t rows, int64_t nb) {
+  const int64_t slices = (nb + 3) / 4;
+  int64_t R = 256;
+  while (R < 1024 && ((rows + 2 * R - 1) / (2 * R)) * slices >= 2048) R *= 2;
+  return R;
+}
+
+// Rows per piece of grouped rows: about 8192 pieces over all slices (32 waves per compute unit),
+// a multiple of the chunk, between 64 and 1024 rows.
+int64_t piece_rows(int64_t rows, int64_t nb) {
+  const int64_t slices = (nb + 3) / 4;
+  int64_t R = rows * slices / 8192;
+  R = (R + kChunk - 1) / kChunk * kChunk;
+  return R < 64 ? 64 : (R > 1024 ? 1024 : R);
+}
+
+bool is_dense(const int64_t* offsets, int64_t n_groups) { return !offsets || n_groups == 1; }
+
+template <bool BF16, bool ACT, bool DIAG>
+hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off, int64_t G,
+                       const void* X, const void* Xq, float beta, float* H, float* P, float* imp,
+                       void* work, unsigned* counters, hipStream_t stream) {
+  const int64_t nb = cin / 16, slices = (nb + 3) / 4;
+  if (dense) {
+    const int64_t R = dense_tile_rows(rows, nb);
+    const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
+    hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG>), dim3((unsigned)tiles, (unsigned)slices),
+                       dim3(kThreads), 0, stream, X, Xq, rows, cin, R, beta, H, P, imp,
+                       (float*)work, nb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || tiles == 1) return e;
+    const int64_t outs = slices * (ACT ? 2 : 1) * 4 * (DIAG ? 16 : 256);
+    hipLaunchKernelGGL((k_acc_dense_sum<ACT, DIAG>), dim3((unsigned)((outs + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, (const float*)work, tiles, slices, nb, rows, beta,
+                       H, P, imp);
+    return hipGetLastError();
+  }
+  const int64_t R = piece_rows(rows, nb);
+  const int64_t cap = rows / R + 2 * G;       // >= the number of pieces
+  int64_t* table = (int64_t*)work;
+  float* ws = (float*)(table + kEntry + cap * kEntry);
+  hipLaunchKernelGGL(k_acc_plan, dim3(1), dim3(kThreads), 0, stream, off, G, rows, R, cap, table);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG>), dim3((unsigned)((cap + 3) / 4), (unsigned)slices),
+                     dim3(kThreads), 0, stream, X, Xq, cin, table, beta, H, P, imp, ws, counters, nb);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-size_t accumulate_scratch_floats(int64_t rows, int64_t nb, bool act_aware) {
-  const int64_t tiles = (rows + kAccTileRows - 1) / kAccTileRows;
-  return (size_t)tiles * 2 * (act_aware ? 2 : 1) * nb * 256;
+AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, int64_t n_groups,
+                              bool act_aware, bool imp_only) {
+  const int64_t slices = (nb + 3) / 4;
+  const size_t part = (size_t)(act_aware ? 2 : 1) * 4 * (imp_only ? 16 : 256) * sizeof(float);
+  AccScratch s;
+  if (is_dense(offsets, n_groups)) {
+    const int64_t R = dense_tile_rows(rows, nb);
+    const int64_t tiles = (rows + R - 1) / R;
+    s.work_bytes = (size_t)slices * tiles * part;
+    s.counters = (size_t)slices;
+  } else {
+    const int64_t R = piece_rows(rows, nb);
+    const int64_t cap = rows / R + 2 * n_groups;
+    s.work_bytes = (size_t)(kEntry + cap * kEntry) * sizeof(int64_t) + (size_t)cap * slices * part;
+    s.counters = (size_t)n_groups * slices;
+  }
+  return s;
 }
 
 hipError_t launch_accumulate(const void* X, const void* Xq, bool bf16, int64_t rows, int64_t cin,
                              const int64_t* offsets, int64_t n_groups, float beta, float* H,
-                             float* P, float* imp, float* scratch, hipStream_t stream) {
-  const int64_t nb = cin / 16;
+                             float* P, float* imp, void* work, size_t work_bytes,
+                             unsigned* counters, size_t n_counters, hipStream_t stream) {
   const bool act = Xq != nullptr;
-  const int64_t tiles = (rows + kAccTileRows - 1) / kAccTileRows;
-  const unsigned gy = (unsigned)((nb + 3) / 4);
-  if (tiles > 0) {
-    dim3 grid((unsigned)tiles, gy);
-    if (bf16 && act)
-      hipLaunchKernelGGL((k_acc_tile<true, true>), grid, dim3(kThreads), 0, stream, X, Xq, rows, cin, offsets, n_groups, beta, H, P, imp, scratch, nb);
-    else if (bf16)
-      hipLaunchKernelGGL((k_acc_tile<true, false>), grid, dim3(kThreads), 0, stream, X, Xq, rows, cin, offsets, n_groups, beta, H, P, imp, scratch, nb);
-    else if (act)
-      hipLaunchKernelGGL((k_acc_tile<false, true>), grid, dim3(kThreads), 0, stream, X, Xq, rows, cin, offsets, n_groups, beta, H, P, imp, scratch, nb);
-    else
-      hipLaunchKernelGGL((k_acc_tile<false, false>), grid, dim3(kThreads), 0, stream, X, Xq, rows, cin, offsets, n_groups, beta, H, P, imp, scratch, nb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  dim3 fgrid((unsigned)n_groups, gy);
+  const bool diag = !act && H == nullptr;
+  const bool dense = is_dense(offsets, n_groups);
+  const AccScratch need = accumulate_scratch(rows, cin / 16, offsets, n_groups, act, diag);
+  if (work_bytes < need.work_bytes || n_counters < need.counters) return hipErrorInvalidValue;
   if (act)
-    hipLaunchKernelGGL((k_acc_finalize<true>), fgrid, dim3(kThreads), 0, stream, offsets, rows, nb, beta, H, P, imp, scratch);
-  else
-    hipLaunchKernelGGL((k_acc_finalize<false>), fgrid, dim3(kThreads), 0, stream, offsets, rows, nb, beta, H, P, imp, scratch);
-  return hipGetLastError();
+    return bf16 ? launch_kind<true, true, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream)
+                : launch_kind<false, true, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream);
+  if (diag)
+    return bf16 ? launch_kind<true, false, true>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream)
+                : launch_kind<false, false, true>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream);
+  return bf16 ? launch_kind<true, false, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream)
+              : launch_kind<false, false, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream);
 }
 
 }  // namespace lh

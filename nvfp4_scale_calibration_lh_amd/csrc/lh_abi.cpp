@@ -1,13 +1,14 @@
 // C ABI of the calibration library (declarations and contracts in include/lh.h).
 //
 // This file validates arguments before anything is launched, selects the device that owns the
-// pointers (restoring the caller's current device), takes accumulation scratch memory from a
-// library-owned stream-ordered pool, and launches the kernels on the caller's stream.  It keeps
-// no state besides the per-device pool and a thread-local error message.
+// pointers (restoring the caller's current device), keeps per-device accumulation scratch memory
+// (from a library-owned stream-ordered pool) that calls hand on in stream order, and launches the
+// kernels on the caller's stream.  Its only other state is a thread-local error message.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -151,6 +152,40 @@ lh_status check_shapes_x(int64_t rows, int64_t cin, const int64_t* offsets, int6
   return LH_OK;
 }
 
+// Accumulation scratch of one device, kept between calls: a work area and arrival counters
+// (zero between calls: set to zero when allocated, and every call leaves them zero).  The memory is
+// handed from call to call in stream order: `ready` is recorded on the stream of the last call
+// that used it and the next call's stream waits for it, so two calls never use it at once.
+struct DeviceScratch {
+  std::mutex mu;
+  void* work = nullptr;
+  size_t work_bytes = 0;
+  unsigned* counters = nullptr;
+  size_t n_counters = 0;
+  hipEvent_t ready = nullptr;
+};
+
+DeviceScratch& device_scratch(int dev) {
+  static DeviceScratch table[64];
+  return table[dev];
+}
+
+// Grows a buffer in stream order (the old one is freed on `s` after the waits already queued).
+hipError_t grow(void** buf, size_t* have, size_t need, size_t elem, hipMemPool_t pool, hipStream_t s,
+                bool zero) {
+  if (need <= *have) return hipSuccess;
+  if (*buf) {
+    hipError_t e = hipFreeAsync(*buf, s);
+    if (e != hipSuccess) return e;
+    *buf = nullptr;
+    *have = 0;
+  }
+  hipError_t e = hipMallocFromPoolAsync(buf, need * elem, pool, s);
+  if (e != hipSuccess) return e;
+  *have = need;
+  return zero ? hipMemsetAsync(*buf, 0, need * elem, s) : hipSuccess;
+}
+
 lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t rows, int64_t cin,
                          const int64_t* offsets, int64_t n_groups, float beta, float* H, float* P,
                          float* imp, void* stream) {
@@ -164,21 +199,32 @@ lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t row
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t nb = cin / 16;
   const bool act = Xq != nullptr;
-  const size_t floats = lh::accumulate_scratch_floats(rows, nb, act);
+  const lh::AccScratch need = lh::accumulate_scratch(rows, nb, offsets, n_groups, act, !act && H == nullptr);
   hipMemPool_t pool;
   hipError_t e = scratch_pool(dev, &pool);
   if (e != hipSuccess) return hip_fail(e, "scratch pool");
-  void* scratch = nullptr;
-  if (floats) {
-    e = hipMallocFromPoolAsync(&scratch, floats * sizeof(float), pool, s);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocFromPoolAsync");
+
+  DeviceScratch& sc = device_scratch(dev);
+  std::lock_guard<std::mutex> lk(sc.mu);
+  if (!sc.ready) {
+    e = hipEventCreateWithFlags(&sc.ready, hipEventDisableTiming);
+    if (e != hipSuccess) { sc.ready = nullptr; return hip_fail(e, "hipEventCreateWithFlags"); }
+  } else {
+    e = hipStreamWaitEvent(s, sc.ready, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
-  const int64_t* off = offsets;   // NULL: dense layer, handled inside the kernels
-  e = lh::launch_accumulate(X, Xq, dt == LH_DTYPE_BF16, rows, cin, off, n_groups, beta, H, P, imp,
-                            static_cast<float*>(scratch), s);
-  hipError_t e2 = scratch ? hipFreeAsync(scratch, s) : hipSuccess;
+  e = grow(&sc.work, &sc.work_bytes, std::max<size_t>(need.work_bytes, 16), 1, pool, s, false);
+  if (e == hipSuccess)
+    e = grow(reinterpret_cast<void**>(&sc.counters), &sc.n_counters, std::max<size_t>(need.counters, 1), sizeof(unsigned), pool, s, true);
+  if (e != hipSuccess) {
+    (void)hipEventRecord(sc.ready, s);
+    return hip_fail(e, "accumulation scratch");
+  }
+  e = lh::launch_accumulate(X, Xq, dt == LH_DTYPE_BF16, rows, cin, offsets, n_groups, beta, H, P, imp,
+                            sc.work, sc.work_bytes, sc.counters, sc.n_counters, s);
+  hipError_t e2 = hipEventRecord(sc.ready, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
-  if (e2 != hipSuccess) return hip_fail(e2, "hipFreeAsync");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipEventRecord");
   return ok();
 }
 

@@ -6,13 +6,16 @@
 
 namespace lh {
 
-// Rows of X processed by one accumulation workgroup (a "tile"); a group (MoE expert) that spans
-// several tiles leaves partial sums in scratch memory that a second kernel combines in tile order.
-constexpr int kAccTileRows = 256;
-
-// Scratch floats needed by launch_accumulate for `rows` rows and `nb` 16-channel blocks
-// (two partial-sum slots per tile, one or two 16x16 matrices per slot).
-size_t accumulate_scratch_floats(int64_t rows, int64_t nb, bool act_aware);
+// Scratch of one launch_accumulate call: a work area (piece table of grouped rows and partial
+// sums of row ranges that are added across workgroups) and arrival counters.  The counters must be
+// zero when a call starts and are zero again when it ends.  launch_accumulate checks the sizes it
+// is given against this and launches nothing if they are short.
+struct AccScratch {
+  size_t work_bytes;
+  size_t counters;
+};
+AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, int64_t n_groups,
+                              bool act_aware, bool imp_only);
 
 hipError_t launch_absmax(const void* W, bool bf16, int64_t n_groups, int64_t elems, float* amax,
                          hipStream_t stream);
@@ -20,7 +23,8 @@ hipError_t launch_absmax(const void* W, bool bf16, int64_t n_groups, int64_t ele
 // act_aware: X and Xq given; H and P required.  Otherwise Xq == nullptr and H and/or imp given.
 hipError_t launch_accumulate(const void* X, const void* Xq, bool bf16, int64_t rows, int64_t cin,
                              const int64_t* offsets, int64_t n_groups, float beta, float* H,
-                             float* P, float* imp, float* scratch, hipStream_t stream);
+                             float* P, float* imp, void* work, size_t work_bytes,
+                             unsigned* counters, size_t n_counters, hipStream_t stream);
 
 hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout, int64_t cin,
                         const float* amax, const float* H, const float* P, uint8_t* code,
