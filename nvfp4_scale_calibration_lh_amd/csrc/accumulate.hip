@@ -208,6 +208,39 @@ __device__ inline void emit_block(int m, const v4f s, int64_t T, int64_t blk, fl
   }
 }
 
+__device__ inline void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Same output as emit_block, written as one contiguous 1 KiB row-major block: the wave turns its
+// MFMA-layout sums into rows through `tmp` (256 floats of its own LDS), then every lane stores 16
+// bytes (row lane/4, columns 4*(lane%4)..+3).
+template <bool DIAG>
+__device__ inline void emit_block_rows(int m, const v4f s, int64_t T, int64_t blk, float beta,
+                                       float* H, float* P, float* imp_blk, int lane, int i, int gg,
+                                       float* tmp) {
+  if (DIAG) {
+    emit_block<true>(m, s, T, blk, beta, H, P, imp_blk, i, gg);
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) tmp[(4 * gg + r) * 16 + i] = s[r];
+  wave_sync_lds();
+  const v4f v = *(const v4f*)&tmp[4 * lane];
+  wave_sync_lds();                            // tmp may be rewritten by the next block
+  const int row = lane >> 2, c0 = (lane & 3) * 4;
+  if (m == 0 && imp_blk && (row >> 2) == (lane & 3)) {
+    const float d = v[row - c0];
+    imp_blk[row] = beta != 0.0f ? beta * imp_blk[row] + d : d;
+  }
+  v4f o = T > 0 ? v / (float)T : v4f{0.f, 0.f, 0.f, 0.f};
+  v4f* dst = (v4f*)((m == 0 ? H : P) + blk * 256 + 4 * lane);
+  if (beta != 0.0f) o += beta * *dst;
+  *dst = o;
+}
+
 // Partial sums of one block: lane-major (lane l's four accumulator values at 4l..4l+3), or the 16
 // diagonal entries (entry c = H[c][c]) when only the importance is produced.
 template <bool DIAG>
@@ -360,7 +393,8 @@ __global__ __launch_bounds__(kThreads) void k_acc_dense_sum(
 // ---------------------------------------------------------------------------------------------
 // Grouped rows: planning.  One workgroup cuts every group into pieces of at most R rows and
 // writes the piece table: word 0 = number of pieces; entry p (at 4 + 4p) = {group, first row,
-// end row, piece index in group << 32 | pieces in group}.  Pieces of one group are consecutive.
+// end row, piece index in group << 32 | pieces in group}, pieces of one group consecutive; then,
+// at 4 + 4 cap, the schedule: piece numbers with the R-row pieces first.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict__ off, int64_t G,
                                                        int64_t rows, int64_t R, int64_t cap,
@@ -380,9 +414,16 @@ __global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict
     span(g, a, e);
     return e > a ? (e - a + R - 1) / R : 1;   // a group without rows is one empty piece
   };
-  int64_t cnt = 0;
-  for (int64_t g = g0; g < g1; ++g) cnt += npieces(g);
-  scan[tid] = cnt;
+  // pieces of exactly R rows are scheduled first (longest work first), the others after them
+  int64_t nfull = 0, nrest = 0;
+  for (int64_t g = g0; g < g1; ++g) {
+    int64_t a, e;
+    span(g, a, e);
+    const int64_t n = npieces(g), f = (e - a) / R;
+    nfull += f;
+    nrest += n - f;
+  }
+  scan[tid] = nfull | (nrest << 32);          // both counts scanned at once (each < 2^31)
   __syncthreads();
   for (int d = 1; d < kThreads; d <<= 1) {    // inclusive scan
     const int64_t v = tid >= d ? scan[tid - d] : 0;
@@ -390,10 +431,13 @@ __global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict
     scan[tid] += v;
     __syncthreads();
   }
-  const int64_t total = scan[kThreads - 1];
+  const int64_t tot_full = scan[kThreads - 1] & 0xFFFFFFFF, total = tot_full + (scan[kThreads - 1] >> 32);
   if (tid == 0) table[0] = total <= cap ? total : 0;      // more pieces only if offsets break the contract
   if (total > cap) return;
-  int64_t p = scan[tid] - cnt;
+  int64_t* sched = table + kEntry + cap * kEntry;
+  int64_t sf = (scan[tid] & 0xFFFFFFFF) - nfull;          // next schedule slot of a full piece
+  int64_t sr = tot_full + (scan[tid] >> 32) - nrest;      // ... and of any other piece
+  int64_t p = sf + sr - tot_full;                         // pieces of earlier threads
   for (int64_t g = g0; g < g1; ++g) {
     int64_t a, e;
     span(g, a, e);
@@ -404,26 +448,30 @@ __global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict
       t[1] = min(e, a + k * R);
       t[2] = min(e, a + (k + 1) * R);
       t[3] = (k << 32) | n;
+      sched[t[2] - t[1] == R ? sf++ : sr++] = p;
     }
   }
 }
 
-// Grouped rows: grid (ceil(capacity / 4), slices); wave w of workgroup x owns piece 4x + w.
+// Grouped rows: a 1-D grid of ceil(capacity / 4) x slices workgroups, slice fastest (the slices of
+// the same rows run together); wave w of workgroup x owns the piece in schedule slot 4x + w.
 // Partial layout: [piece][slice][m][block][kPart]; counters: [group][slice].
 template <bool BF16, bool ACT, bool DIAG>
 __global__ __launch_bounds__(kThreads) void k_acc_pieces(
     const void* __restrict__ Xv, const void* __restrict__ Xqv, int64_t cin,
-    const int64_t* __restrict__ table, float beta, float* __restrict__ H, float* __restrict__ P,
-    float* __restrict__ imp, float* __restrict__ ws, unsigned* __restrict__ counters, int64_t nb) {
+    const int64_t* __restrict__ table, int64_t cap, float beta, float* __restrict__ H,
+    float* __restrict__ P, float* __restrict__ imp, float* __restrict__ ws,
+    unsigned* __restrict__ counters, int64_t nb) {
   using St = Streamer<BF16, ACT>;
   constexpr int kM = St::kM;
   constexpr int kPart = DIAG ? 16 : 256;
   __shared__ __attribute__((aligned(16))) unsigned smem[4 * kM * Geo<BF16>::kWords];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, gg = lane >> 4;
-  const int64_t slices = gridDim.y, slice = blockIdx.y;
-  const int64_t p = (int64_t)blockIdx.x * 4 + wave;
-  if (p >= table[0]) return;                  // whole wave leaves; no workgroup barriers here
+  const int64_t slices = (nb + 3) / 4, slice = blockIdx.x % slices;
+  const int64_t sidx = (int64_t)(blockIdx.x / slices) * 4 + wave;
+  if (sidx >= table[0]) return;               // whole wave leaves; no workgroup barriers here
+  const int64_t p = table[kEntry + cap * kEntry + sidx];
   const int64_t* e = table + kEntry + p * kEntry;
   const int64_t g = e[0], r0 = e[1], r1 = e[2];
   const int64_t k = e[3] >> 32, npieces = e[3] & 0xFFFFFFFF;
@@ -445,8 +493,8 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
       if (b >= nblk) break;
 #pragma unroll
       for (int m = 0; m < kM; ++m)
-        emit_block<DIAG>(m, m == 0 ? st.accH[b] : st.accP[b], T, g * nb + n0 + b, beta, H, P,
-                         imp_g ? imp_g + (n0 + b) * 16 : nullptr, i, gg);
+        emit_block_rows<DIAG>(m, m == 0 ? st.accH[b] : st.accP[b], T, g * nb + n0 + b, beta, H, P,
+                              imp_g ? imp_g + (n0 + b) * 16 : nullptr, lane, i, gg, (float*)st.stage);
     }
     return;
   }
@@ -466,8 +514,9 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
   const int64_t pfirst = p - k;
   for (int b = 0; b < nblk; ++b)
     for (int m = 0; m < kM; ++m)
-      emit_block<DIAG>(m, sum_partials<DIAG>(part(pfirst, m, b), slices * kM * 4 * kPart, npieces, lane, i, gg),
-                       T, g * nb + n0 + b, beta, H, P, imp_g ? imp_g + (n0 + b) * 16 : nullptr, i, gg);
+      emit_block_rows<DIAG>(m, sum_partials<DIAG>(part(pfirst, m, b), slices * kM * 4 * kPart, npieces, lane, i, gg),
+                            T, g * nb + n0 + b, beta, H, P, imp_g ? imp_g + (n0 + b) * 16 : nullptr,
+                            lane, i, gg, (float*)st.stage);
   if (lane == 0) clear(&counters[g * slices + slice]);
 }
 
@@ -512,12 +561,12 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
   const int64_t R = piece_rows(rows, nb);
   const int64_t cap = rows / R + 2 * G;       // >= the number of pieces
   int64_t* table = (int64_t*)work;
-  float* ws = (float*)(table + kEntry + cap * kEntry);
+  float* ws = (float*)(table + kEntry + 2 * cap * kEntry);
   hipLaunchKernelGGL(k_acc_plan, dim3(1), dim3(kThreads), 0, stream, off, G, rows, R, cap, table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG>), dim3((unsigned)((cap + 3) / 4), (unsigned)slices),
-                     dim3(kThreads), 0, stream, X, Xq, cin, table, beta, H, P, imp, ws, counters, nb);
+  hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG>), dim3((unsigned)(((cap + 3) / 4) * slices)),
+                     dim3(kThreads), 0, stream, X, Xq, cin, table, cap, beta, H, P, imp, ws, counters, nb);
   return hipGetLastError();
 }
 
@@ -536,7 +585,7 @@ AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, 
   } else {
     const int64_t R = piece_rows(rows, nb);
     const int64_t cap = rows / R + 2 * n_groups;
-    s.work_bytes = (size_t)(kEntry + cap * kEntry) * sizeof(int64_t) + (size_t)cap * slices * part;
+    s.work_bytes = (size_t)(kEntry + 2 * cap * kEntry) * sizeof(int64_t) + (size_t)cap * slices * part;
     s.counters = (size_t)n_groups * slices;
   }
   return s;
