@@ -68,7 +68,7 @@ __device__ inline float global_scale(float amax) { return (float)((double)amax /
 __device__ inline float cand_scale(int k, float g) { return (float)(e4m3_value(k) * (double)g); }
 __device__ inline float inv_scale(float s) { return s > 0.0f ? (float)(1.0 / (double)s) : 0.0f; }
 // The float32 filter is used only where scales and quotients stay normal and finite.
-__device__ inline bool filter_ok(float g) { return g >= 0x1p-116f && g <= 0x1p+100f; }
+__device__ inline bool filter_ok(float g) { return g >= 0x1p-100f && g <= 0x1p+100f; }
 
 // Exact E2M1 grid index of the quotient r = |w|/s given as float64 (ties to the even index).
 // |w| and m*s have at most 27 significant bits, so a float64 quotient is on the same side of
@@ -730,11 +730,33 @@ __device__ inline void load_w16(const void* W, int64_t base, float w[16]) {
   }
 }
 
+// Exact E2M1 grid index of |w|/s for s > 0 (normal range): each rounding midpoint m is compared
+// through the sign of fma(m, s, -|w|), which is the sign of the exact m*s - |w|; ties go to the
+// even index (down at 0.25, 1.25, 2.5, 5; up at 0.75, 1.75, 3.5).
+__device__ inline int e2m1_index_fma(float aw, float s) {
+  return (int)(fmaf(0.25f, s, -aw) < 0.0f) + (int)(fmaf(0.75f, s, -aw) <= 0.0f) +
+         (int)(fmaf(1.25f, s, -aw) < 0.0f) + (int)(fmaf(1.75f, s, -aw) <= 0.0f) +
+         (int)(fmaf(2.5f, s, -aw) < 0.0f) + (int)(fmaf(3.5f, s, -aw) <= 0.0f) +
+         (int)(fmaf(5.0f, s, -aw) < 0.0f);
+}
+__device__ inline float e2m1_valf(int c) {
+  return c <= 4 ? 0.5f * (float)c : (c == 5 ? 3.0f : (c == 6 ? 4.0f : 6.0f));
+}
+
+// Diagonal form.  Every candidate is scored with the fp32 quotient and the gfx950 FP4 converts.
+// No midpoint correction is needed here: at a rounding midpoint both neighbours are equally far,
+// so a quotient on the wrong side by its rounding error (|r' - r| <= 2^-23 r) changes that
+// element's e^2 by at most 4 (m / h) 2^-23 <= 28 * 2^-23 of itself (m a midpoint, h the half
+// spacing around it); with the fp32 arithmetic (under 19 * 2^-24) every L_k is within 5e-6 of
+// its exact value, inside the filter's 2^-16 bound.  Only the winner's nibbles and loss are then
+// recomputed with exact rounding decisions.
 template <bool BF16>
 __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ imp, uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
     float* __restrict__ loss) {
+  __shared__ __attribute__((aligned(16))) float wt_all[kWaves][kRowsPerWave][16];
+  __shared__ float im_all[kWaves][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = cin / 16;
   const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
@@ -743,6 +765,29 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
   if (n >= nb || c_begin >= cout) return;
   const int64_t c_end = min(cout, c_begin + kRowsPerWave);
 
+  // The wave's 32 blocks (rows c_begin.., column n) come in with one coalesced load per lane
+  // (lane l: row l/2, elements 8*(l%2)..+7) and wait in LDS as fp32.
+  float (*wt)[16] = wt_all[wave];
+  {
+    const int rr = lane >> 1, h = lane & 1;
+    const int64_t c = c_begin + rr;
+    const int64_t e0 = (g * cout + min(c, c_end - 1)) * cin + n * 16 + 8 * h;
+    float v[8];
+    if (BF16) {
+      const v4u u = *(const v4u*)((const unsigned short*)W + e0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(u[q] << 16);
+        v[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
+      }
+    } else {
+      const v4f u0 = *(const v4f*)((const float*)W + e0), u1 = *(const v4f*)((const float*)W + e0 + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v[q] = u0[q]; v[4 + q] = u1[q]; }
+    }
+    *(v4f*)&wt[rr][8 * h] = v4f{v[0], v[1], v[2], v[3]};
+    *(v4f*)&wt[rr][8 * h + 4] = v4f{v[4], v[5], v[6], v[7]};
+  }
   float im[16];
   double isum = 0.0;
 #pragma unroll
@@ -754,35 +799,33 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
 #pragma unroll
     for (int j = 0; j < 16; ++j) im[j] = 1.0f;
   }
+  if (lane < 16) im_all[wave][lane] = im[lane & 15];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
   const float gsc = global_scale(amax[g]);
   const bool fast = filter_ok(gsc);
   const int k0 = lane + 1, k1 = lane + 65;
   const bool v1 = k1 <= 126;
   const float s0 = cand_scale(k0, gsc), s1 = cand_scale(v1 ? k1 : 126, gsc);
   const float is0 = inv_scale(s0), is1 = inv_scale(s1);
-  const int p0 = lane, p1 = lane + 64;
-  const float img0 = fast ? (float)(1.0 / ((double)kMid[p0 % 7] * (double)gsc)) : 0.0f;
-  const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)kMid[p1 % 7] * (double)gsc)) : 0.0f;
+  // the winner's exact decisions are taken by lanes 0..7, two elements each
+  const int el0 = 2 * (lane & 7), el1 = el0 + 1;
+  const float ima = im_all[wave][el0], imb = im_all[wave][el1];
 
   for (int64_t c = c_begin; c < c_end; ++c) {
-    const int64_t base = (g * cout + c) * cin + n * 16;
     const int64_t oblk = (g * cout + c) * nb + n;
-    float w[16];
-    load_w16<BF16>(W, base, w);
-    const float wp0 = load_w(W, BF16, base + p0 / 7), wp1 = load_w(W, BF16, base + (p1 < 112 ? p1 : 0) / 7);
-    const bool near0 = near_midpoint(fabsf(wp0), img0);
-    const bool near1 = p1 < 112 && near_midpoint(fabsf(wp1), img1);
-    const unsigned long long m0 = __ballot(near0), m1 = __ballot(near1);
     if (!fast) {
-      if (lane == 0) code[oblk] = 0;
+      if (lane == 0) code[oblk] = 0;              // resolved by the float64 pass
       continue;
     }
-    const bool has_ovr = (m0 | m1) != 0ull;
-    int kv0 = 0, kv1 = 0;
-    float rv0 = 0.0f, rv1 = 0.0f;
-    if (has_ovr) {
-      pair_override(near0, p0, wp0, gsc, &kv0, &rv0);
-      pair_override(near1, p1, wp1, gsc, &kv1, &rv1);
+    const int rr = (int)(c - c_begin);
+    float w[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f t = *(const v4f*)&wt[rr][4 * q];
+      w[4 * q] = t[0]; w[4 * q + 1] = t[1]; w[4 * q + 2] = t[2]; w[4 * q + 3] = t[3];
     }
     float L0 = 0.0f, L1 = 0.0f;
 #pragma unroll
@@ -798,65 +841,37 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
       L1 = fmaf(im[j] * eb0, eb0, L1);
       L1 = fmaf(im[j + 1] * eb1, eb1, L1);
     }
-    if (has_ovr) {
-      // a lane whose candidate has flagged elements re-scores it with the exact decisions
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = lane + 1 + 64 * h;
-        bool mine = false;
-        for (unsigned long long mm = m0 | m1; mm; mm &= mm - 1) {
-          const int b = __builtin_ctzll(mm);
-          mine |= (__builtin_amdgcn_readlane(kv0, b) == k && ((m0 >> b) & 1ull)) ||
-                  (__builtin_amdgcn_readlane(kv1, b) == k && ((m1 >> b) & 1ull));
-        }
-        if (mine) {
-          const float sh = h ? s1 : s0, ih = h ? is1 : is0;
-          float Lh = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            float r = w[j] * ih;
-            r = override_for(m0, 0, kv0, rv0, k, j, r);
-            r = override_for(m1, 64, kv1, rv1, k, j, r);
-            const unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r, 0.0f, 1.0f, 0);
-            const float e = fmaf(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0)[0], sh, -w[j]);
-            Lh = fmaf(im[j] * e, e, Lh);
-          }
-          if (h) L1 = Lh; else L0 = Lh;
-        }
-      }
-    }
     if (!v1) L1 = __builtin_inff();
     float bestL = L0;
     int bestK = k0;
     if (L1 < bestL) { bestL = L1; bestK = k1; }
     // the winner is exact when every other candidate's lower bound exceeds its upper bound
     const float mL = wave_min(bestL);
-    const int k_best = __builtin_amdgcn_readlane(bestK, (int)__builtin_ctzll(__ballot(bestL == mL)));
+    const int owner = (int)__builtin_ctzll(__ballot(bestL == mL));
+    const int k_best = __builtin_amdgcn_readlane(bestK, owner);
     const float U = mL * (1.0f + kErrC);
     const int cnt = __popcll(__ballot(L0 * (1.0f - kErrC) <= U)) + __popcll(__ballot(L1 * (1.0f - kErrC) <= U));
     if (cnt != 1) {
       if (lane == 0) code[oblk] = 0;
       continue;
     }
+    // exact nibbles and loss of the winner (lanes 0..7: elements 2l, 2l+1)
+    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k_best <= 64 ? s0 : s1), owner));
+    const float wa = wt[rr][el0], wb = wt[rr][el1];
+    const int ca = e2m1_index_fma(fabsf(wa), sw), cb = e2m1_index_fma(fabsf(wb), sw);
+    const float qa = e2m1_valf(ca), qb = e2m1_valf(cb);
+    const float ea = fmaf(wa < 0.0f ? -qa : qa, sw, -wa), eb = fmaf(wb < 0.0f ? -qb : qb, sw, -wb);
+    float part = lane < 8 ? fmaf(imb * eb, eb, ima * ea * ea) : 0.0f;
+    part += __shfl_xor(part, 1, 64);
+    part += __shfl_xor(part, 2, 64);
+    part += __shfl_xor(part, 4, 64);
     if (lane < 8 && fp4) {
-      const float sw = cand_scale(k_best, gsc);
-      const float iw = inv_scale(sw);
-      const float wa = load_w(W, BF16, base + 2 * lane), wb = load_w(W, BF16, base + 2 * lane + 1);
-      float ra = wa * iw, rb = wb * iw;
-      if (has_ovr) {
-        ra = override_for(m0, 0, kv0, rv0, k_best, 2 * lane, ra);
-        ra = override_for(m1, 64, kv1, rv1, k_best, 2 * lane, ra);
-        rb = override_for(m0, 0, kv0, rv0, k_best, 2 * lane + 1, rb);
-        rb = override_for(m1, 64, kv1, rv1, k_best, 2 * lane + 1, rb);
-      }
-      const unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ra, rb, 1.0f, 0);
-      unsigned byte = pk & 0x77u;
-      byte |= (wa < 0.0f ? 0x8u : 0u) | (wb < 0.0f ? 0x80u : 0u);
+      const unsigned byte = (unsigned)(ca | (wa < 0.0f ? 8 : 0)) | ((unsigned)(cb | (wb < 0.0f ? 8 : 0)) << 4);
       fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)byte;
     }
     if (lane == 0) {
       code[oblk] = (uint8_t)k_best;
-      if (loss) loss[oblk] = mL;
+      if (loss) loss[oblk] = part;
     }
   }
 }
