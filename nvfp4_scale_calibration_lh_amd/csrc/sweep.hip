@@ -757,6 +757,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     float* __restrict__ loss) {
   __shared__ __attribute__((aligned(16))) float wt_all[kWaves][kRowsPerWave][16];
   __shared__ float im_all[kWaves][16];
+  __shared__ float win_s[kWaves][kRowsPerWave];   // winner's scale per row (0: no winner here)
+  __shared__ int win_k[kWaves][kRowsPerWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = cin / 16;
   const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
@@ -810,17 +812,17 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
   const bool v1 = k1 <= 126;
   const float s0 = cand_scale(k0, gsc), s1 = cand_scale(v1 ? k1 : 126, gsc);
   const float is0 = inv_scale(s0), is1 = inv_scale(s1);
-  // the winner's exact decisions are taken by lanes 0..7, two elements each
-  const int el0 = 2 * (lane & 7), el1 = el0 + 1;
-  const float ima = im_all[wave][el0], imb = im_all[wave][el1];
 
   for (int64_t c = c_begin; c < c_end; ++c) {
     const int64_t oblk = (g * cout + c) * nb + n;
+    const int rr = (int)(c - c_begin);
     if (!fast) {
-      if (lane == 0) code[oblk] = 0;              // resolved by the float64 pass
+      if (lane == 0) {
+        code[oblk] = 0;                           // resolved by the float64 pass
+        win_k[wave][rr] = 0;
+      }
       continue;
     }
-    const int rr = (int)(c - c_begin);
     float w[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -851,27 +853,44 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     const int k_best = __builtin_amdgcn_readlane(bestK, owner);
     const float U = mL * (1.0f + kErrC);
     const int cnt = __popcll(__ballot(L0 * (1.0f - kErrC) <= U)) + __popcll(__ballot(L1 * (1.0f - kErrC) <= U));
-    if (cnt != 1) {
-      if (lane == 0) code[oblk] = 0;
-      continue;
-    }
-    // exact nibbles and loss of the winner (lanes 0..7: elements 2l, 2l+1)
     const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k_best <= 64 ? s0 : s1), owner));
+    if (lane == 0) {
+      if (cnt != 1) code[oblk] = 0;               // several contenders: float64 pass
+      win_k[wave][rr] = cnt == 1 ? k_best : 0;
+      win_s[wave][rr] = sw;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // exact nibbles and loss of every row's winner, eight rows at a time: lane l takes row
+  // 8*pass + l/8 and its elements 2*(l%8), 2*(l%8)+1
+  const int sub = lane & 7, el0 = 2 * sub, el1 = el0 + 1;
+  const float ima = im_all[wave][el0], imb = im_all[wave][el1];
+#pragma unroll
+  for (int pass = 0; pass < kRowsPerWave / 8; ++pass) {
+    const int rr = 8 * pass + (lane >> 3);
+    const int64_t c = c_begin + rr;
+    const bool row_on = c < c_end;
+    const int kw = row_on ? win_k[wave][rr] : 0;
+    const float sw = row_on ? win_s[wave][rr] : 1.0f;
     const float wa = wt[rr][el0], wb = wt[rr][el1];
     const int ca = e2m1_index_fma(fabsf(wa), sw), cb = e2m1_index_fma(fabsf(wb), sw);
     const float qa = e2m1_valf(ca), qb = e2m1_valf(cb);
     const float ea = fmaf(wa < 0.0f ? -qa : qa, sw, -wa), eb = fmaf(wb < 0.0f ? -qb : qb, sw, -wb);
-    float part = lane < 8 ? fmaf(imb * eb, eb, ima * ea * ea) : 0.0f;
+    float part = fmaf(imb * eb, eb, ima * ea * ea);
     part += __shfl_xor(part, 1, 64);
     part += __shfl_xor(part, 2, 64);
     part += __shfl_xor(part, 4, 64);
-    if (lane < 8 && fp4) {
-      const unsigned byte = (unsigned)(ca | (wa < 0.0f ? 8 : 0)) | ((unsigned)(cb | (wb < 0.0f ? 8 : 0)) << 4);
-      fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)byte;
-    }
-    if (lane == 0) {
-      code[oblk] = (uint8_t)k_best;
-      if (loss) loss[oblk] = part;
+    if (kw != 0) {
+      if (fp4) {
+        const unsigned byte = (unsigned)(ca | (wa < 0.0f ? 8 : 0)) | ((unsigned)(cb | (wb < 0.0f ? 8 : 0)) << 4);
+        fp4[(g * cout + c) * (cin / 2) + n * 8 + sub] = (uint8_t)byte;
+      }
+      if (sub == 0) {
+        code[(g * cout + c) * nb + n] = (uint8_t)kw;
+        if (loss) loss[(g * cout + c) * nb + n] = part;
+      }
     }
   }
 }
