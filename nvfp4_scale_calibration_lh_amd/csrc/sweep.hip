@@ -197,6 +197,23 @@ __device__ inline float wave_min(float v) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Minimum over all 64 lanes of a value >= 0 (or +inf): the bit patterns of such floats are
+// ordered like unsigned integers, so the reduction needs no float canonicalization.
+template <int CTRL>
+__device__ inline unsigned dppu(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ inline float wave_min_nonneg(float x) {
+  unsigned v = __float_as_uint(x);
+  v = min(v, dppu<0x128>(v));
+  v = min(v, dppu<0x124>(v));
+  v = min(v, dppu<0x122>(v));
+  v = min(v, dppu<0x121>(v));
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min((unsigned)a[0], (unsigned)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(min((unsigned)b[0], (unsigned)b[1]));
+}
 // Lowest (loss, code) over the wave in float64 (exact re-scoring).
 __device__ inline void wave_argmin_d(double& L, int& k) {
   for (int o = 1; o < 64; o <<= 1) {
@@ -848,15 +865,43 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     int bestK = k0;
     if (L1 < bestL) { bestL = L1; bestK = k1; }
     // the winner is exact when every other candidate's lower bound exceeds its upper bound
-    const float mL = wave_min(bestL);
+    const float mL = wave_min_nonneg(bestL);     // losses are sums of Imp * e^2 >= 0
     const int owner = (int)__builtin_ctzll(__ballot(bestL == mL));
     const int k_best = __builtin_amdgcn_readlane(bestK, owner);
     const float U = mL * (1.0f + kErrC);
-    const int cnt = __popcll(__ballot(L0 * (1.0f - kErrC) <= U)) + __popcll(__ballot(L1 * (1.0f - kErrC) <= U));
-    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k_best <= 64 ? s0 : s1), owner));
+    const unsigned long long M0 = __ballot(L0 * (1.0f - kErrC) <= U), M1 = __ballot(L1 * (1.0f - kErrC) <= U);
+    const int cnt = __popcll(M0) + __popcll(M1);
+    int kwin = k_best;
+    if (cnt > 1 && cnt <= 4) {
+      // 2..4 contenders: exact float64 losses, one contender per 16 lanes (lane: element l%16)
+      unsigned long long ma = M0, mb = M1;
+      auto next = [&]() -> int {
+        if (ma) { const int bb = __builtin_ctzll(ma); ma &= ma - 1; return bb + 1; }
+        if (mb) { const int bb = __builtin_ctzll(mb); mb &= mb - 1; return bb + 65; }
+        return 0;
+      };
+      const int kc0 = next(), kc1 = next(), kc2 = next(), kc3 = next();
+      const int q = lane >> 4, j = lane & 15;
+      const int my_k = q == 0 ? kc0 : (q == 1 ? kc1 : (q == 2 ? kc2 : kc3));
+      int nib;
+      const double e = exact_err(wt[rr][j], cand_scale(my_k > 0 ? my_k : 1, gsc), &nib);
+      double z = (double)im_all[wave][j] * e * e;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+      double bestD = __builtin_inf();
+      kwin = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = r == 0 ? kc0 : (r == 1 ? kc1 : (r == 2 ? kc2 : kc3));
+        const double Lr = __shfl(z, 16 * r, 64);
+        if (kr > 0 && (Lr < bestD || (Lr == bestD && kr < kwin))) { bestD = Lr; kwin = kr; }
+      }
+    }
+    const int wl = (kwin - 1) & 63;               // the lane that holds code kwin
+    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kwin <= 64 ? s0 : s1), wl));
     if (lane == 0) {
-      if (cnt != 1) code[oblk] = 0;               // several contenders: float64 pass
-      win_k[wave][rr] = cnt == 1 ? k_best : 0;
+      if (cnt > 4) code[oblk] = 0;                // many contenders: float64 pass
+      win_k[wave][rr] = cnt <= 4 ? kwin : 0;
       win_s[wave][rr] = sw;
     }
   }
