@@ -18,8 +18,8 @@
 //  * The cross matrix uses D = X_q - X formed in fp32 (exact for bf16 data) and split into a bf16
 //    high part (truncation) and the exact bf16 remainder, so P = X_q^T D_hi + X_q^T D_lo needs two
 //    more MFMAs and no catastrophic cancellation.
-//  * Dense layer (one group): a workgroup owns a tile of R rows whose chunks its four waves take
-//    in turn; the waves add their sums in LDS at the end.  With several tiles, each tile stores
+//  * Dense layer (one group): a workgroup of 16 waves owns a tile of R rows whose chunks the
+//    waves take in turn; the waves add their sums in LDS at the end.  With several tiles, each tile stores
 //    its sums and a second kernel adds them in tile order, one thread per output entry.
 //  * Grouped rows (MoE experts): a small planning kernel cuts every group into pieces of at most
 //    R rows (a group without rows is one empty piece); each wave owns one piece, so a group of at
@@ -287,19 +287,23 @@ __device__ inline v4f sum_partials(const float* w0, int64_t stride, int64_t n, i
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense layer: grid (tiles, slices), four waves per tile, chunks interleaved between the waves.
+// Dense layer: grid (tiles, slices), NW waves per tile, chunks interleaved between the waves
+// (many waves per tile: few tiles, so few partial sums, yet enough loads in flight).
 // Partial layout: [slice][tile][m][block][kPart].
 // ---------------------------------------------------------------------------------------------
-template <bool BF16, bool ACT, bool DIAG>
-__global__ __launch_bounds__(kThreads) void k_acc_dense(
+template <bool BF16>
+constexpr int dense_waves() { return BF16 ? 16 : 4; }
+
+template <bool BF16, bool ACT, bool DIAG, int NW>
+__global__ __launch_bounds__(NW * 64) void k_acc_dense(
     const void* __restrict__ Xv, const void* __restrict__ Xqv, int64_t rows, int64_t cin,
     int64_t R, float beta, float* __restrict__ H, float* __restrict__ P, float* __restrict__ imp,
     float* __restrict__ ws, int64_t nb) {
   using St = Streamer<BF16, ACT>;
   constexpr int kM = St::kM;
   constexpr int kPart = DIAG ? 16 : 256;
-  constexpr int kStage = 4 * kM * Geo<BF16>::kWords;
-  constexpr int kComb = 4 * 4 * 64 * 4;       // [wave][block][lane] v4f, in words
+  constexpr int kStage = NW * kM * Geo<BF16>::kWords;
+  constexpr int kComb = NW * 4 * 64 * 4;      // [wave][block][lane] v4f, in words
   __shared__ __attribute__((aligned(16))) unsigned smem[kStage > kComb ? kStage : kComb];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, gg = lane >> 4;
@@ -310,9 +314,9 @@ __global__ __launch_bounds__(kThreads) void k_acc_dense(
 
   St st{(const char*)Xv, (const char*)Xqv, cin, slice * kCh, nblk, lane, i, gg,
         smem + wave * kM * Geo<BF16>::kWords, {}, {}};
-  st.run(t0, t1, wave, 4);
+  st.run(t0, t1, wave, NW);
 
-  const bool mine = wave < nblk;
+  const bool mine = wave < nblk;              // waves 0..3 own the slice's four blocks
   const int64_t blk = n0 + wave;              // group 0
   float* imp_blk = imp ? imp + blk * 16 : nullptr;
   v4f* comb = (v4f*)smem;
@@ -323,8 +327,11 @@ __global__ __launch_bounds__(kThreads) void k_acc_dense(
 #pragma unroll
     for (int b = 0; b < 4; ++b) comb[(wave * 4 + b) * 64 + lane] = m == 0 ? st.accH[b] : st.accP[b];
     __syncthreads();
-    tot[m] = ((comb[(0 * 4 + wave) * 64 + lane] + comb[(1 * 4 + wave) * 64 + lane]) +
-              comb[(2 * 4 + wave) * 64 + lane]) + comb[(3 * 4 + wave) * 64 + lane];
+    tot[m] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (wave < 4) {
+#pragma unroll
+      for (int v = 0; v < NW; ++v) tot[m] += comb[(v * 4 + wave) * 64 + lane];   // wave order
+    }
   }
   if (tiles == 1) {
     if (mine)
@@ -520,11 +527,16 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
   if (lane == 0) clear(&counters[g * slices + slice]);
 }
 
-// Rows per tile of a dense layer: the longest of 256, 512, 1024 that still gives 2048 workgroups.
-int64_t dense_tile_rows(int64_t rows, int64_t nb) {
+// Rows per tile of a dense layer: NW waves x 32 rows x c chunks per wave, with the largest c of
+// 1, 2, 4, 8 that still gives 256 workgroups (one per compute unit; the 16-wave workgroups of
+// H and P fill a compute unit's LDS), or 1024 when only the importance is produced (smaller
+// workgroups, several per compute unit).  Measured on MI355X for the dense shapes.
+int64_t dense_tile_rows(int64_t rows, int64_t nb, bool bf16, bool imp_only) {
   const int64_t slices = (nb + 3) / 4;
-  int64_t R = 256;
-  while (R < 1024 && ((rows + 2 * R - 1) / (2 * R)) * slices >= 2048) R *= 2;
+  const int64_t base = (bf16 ? dense_waves<true>() : dense_waves<false>()) * kChunk;
+  const int64_t want = imp_only ? 1024 : 256;
+  int64_t R = base;
+  while (R < 8 * base && ((rows + 2 * R - 1) / (2 * R)) * slices >= want) R *= 2;
   return R;
 }
 
@@ -545,10 +557,11 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
                        void* work, unsigned* counters, hipStream_t stream) {
   const int64_t nb = cin / 16, slices = (nb + 3) / 4;
   if (dense) {
-    const int64_t R = dense_tile_rows(rows, nb);
+    constexpr int NW = dense_waves<BF16>();
+    const int64_t R = dense_tile_rows(rows, nb, BF16, DIAG);
     const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
-    hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG>), dim3((unsigned)tiles, (unsigned)slices),
-                       dim3(kThreads), 0, stream, X, Xq, rows, cin, R, beta, H, P, imp,
+    hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG, NW>), dim3((unsigned)tiles, (unsigned)slices),
+                       dim3(NW * 64), 0, stream, X, Xq, rows, cin, R, beta, H, P, imp,
                        (float*)work, nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || tiles == 1) return e;
@@ -573,12 +586,12 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
 }  // namespace
 
 AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, int64_t n_groups,
-                              bool act_aware, bool imp_only) {
+                              bool bf16, bool act_aware, bool imp_only) {
   const int64_t slices = (nb + 3) / 4;
   const size_t part = (size_t)(act_aware ? 2 : 1) * 4 * (imp_only ? 16 : 256) * sizeof(float);
   AccScratch s;
   if (is_dense(offsets, n_groups)) {
-    const int64_t R = dense_tile_rows(rows, nb);
+    const int64_t R = dense_tile_rows(rows, nb, bf16, imp_only);
     const int64_t tiles = (rows + R - 1) / R;
     s.work_bytes = (size_t)slices * tiles * part;
     s.counters = (size_t)slices;
@@ -598,7 +611,7 @@ hipError_t launch_accumulate(const void* X, const void* Xq, bool bf16, int64_t r
   const bool act = Xq != nullptr;
   const bool diag = !act && H == nullptr;
   const bool dense = is_dense(offsets, n_groups);
-  const AccScratch need = accumulate_scratch(rows, cin / 16, offsets, n_groups, act, diag);
+  const AccScratch need = accumulate_scratch(rows, cin / 16, offsets, n_groups, bf16, act, diag);
   if (work_bytes < need.work_bytes || n_counters < need.counters) return hipErrorInvalidValue;
   if (act)
     return bf16 ? launch_kind<true, true, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream)

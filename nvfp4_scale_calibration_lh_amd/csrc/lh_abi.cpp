@@ -199,7 +199,8 @@ lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t row
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t nb = cin / 16;
   const bool act = Xq != nullptr;
-  const lh::AccScratch need = lh::accumulate_scratch(rows, nb, offsets, n_groups, act, !act && H == nullptr);
+  const lh::AccScratch need = lh::accumulate_scratch(rows, nb, offsets, n_groups, dt == LH_DTYPE_BF16, act,
+                                                    !act && H == nullptr);
   hipMemPool_t pool;
   hipError_t e = scratch_pool(dev, &pool);
   if (e != hipSuccess) return hip_fail(e, "scratch pool");

@@ -15,7 +15,7 @@ struct AccScratch {
   size_t counters;
 };
 AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, int64_t n_groups,
-                              bool act_aware, bool imp_only);
+                              bool bf16, bool act_aware, bool imp_only);
 
 hipError_t launch_absmax(const void* W, bool bf16, int64_t n_groups, int64_t elems, float* amax,
                          hipStream_t stream);

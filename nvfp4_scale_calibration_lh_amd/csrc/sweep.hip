@@ -18,9 +18,9 @@
 //    saturates at 6, and the convert back), and forms e = fma(q, s, -w).
 //  * The contraction H_n e is reorganized so the matrix cores see exact small integers:
 //    (H e)_i = s (H q)_i - (H w)_i, where q holds E2M1 grid values times a power of 4 (at most
-//    2 significant bits, exact in bf16).  H_n is split once per column into three bf16 pieces
-//    (H1 + H2 + H3 equals H to 2^-27 relative), so two chained v_mfma_f32_16x16x32_bf16 with
-//    K slots [H1 | H2] and [H3 | 0] give H q for 16 candidates with exact products and fp32
+//    2 significant bits, exact in bf16).  H_n is split once per column into two bf16 pieces
+//    (H1 + H2 equals H to 2^-18 relative, a residual the error bound below covers), so one
+//    v_mfma_f32_16x16x32_bf16 with K slots [H1 | H2] gives H q for 16 candidates with exact products and fp32
 //    accumulation.  H w (and P w, |P||w| in the coupled form) comes from v_mfma_f32_16x16x4_f32
 //    once per 16-row tile.  The loss L = e^T (H e + 2 P w) is a 4-term dot per lane reduced over
 //    the 4 lane groups with permlane swaps; the argmin over lanes uses DPP row rotations and
@@ -52,7 +52,10 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per workgroup; wave w takes block column 4*bx + w
 constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
-constexpr float kErrC = 0x1p-16f;    // filter error bound factor (about 4x the derived bound)
+// Filter error bound factor.  Full form: the fp32 arithmetic contributes at most about
+// 2^-19 A and the two-piece bf16 split of H at most 2^-18 A (A_k as in the header), so 2^-16
+// leaves a margin above 2.5x; diagonal form: under 5e-6 L.
+constexpr float kErrC = 0x1p-16f;
 constexpr int kNearUlps = 16;        // midpoint proximity test, in ulps of |w|/(m g)
 
 __device__ const float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
@@ -300,11 +303,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const bool coupled = COUPLED && !dead;
   // Lane (row i, group gg) holds, for elements col = 4*gg + t:
   //   a[t]   = H[i][col] in fp32 (H w per 16-row tile), pv/pa = P and |P| (P w, |P||w|)
-  //   hb     = H[i][col] split into three bf16 pieces H1 + H2 + H3 (exact to 2^-27 relative):
-  //            A operand of the bf16 MFMAs that form H q for the candidates
+  //   h1, h2 = H[i][col] split into two bf16 pieces, |H - H1 - H2| <= 2^-18 |H|: A operand of
+  //            the bf16 MFMA that forms H q for the candidates
   //   dm[t]  = sqrt(max_j max(|H_col,j|, |H_j,col|)), so |H_ij| <= dm_i dm_j for any H
   float a[4], dm[4], pa[4], pv[4];
-  unsigned h1[4], h2[4], h3[4];
+  unsigned h1[4], h2[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int col = 4 * gg + t;
@@ -312,8 +315,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     h1[t] = bf16_rne(a[t]);
     const float r1 = a[t] - bf16_val(h1[t]);      // exact
     h2[t] = bf16_rne(r1);
-    const float r2 = r1 - bf16_val(h2[t]);        // exact
-    h3[t] = bf16_rne(r2);
     float mx = 1.0f;
     if (!dead) {
       mx = 0.0f;
@@ -323,11 +324,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     pv[t] = coupled ? L.P[i * 16 + col] : 0.0f;
     pa[t] = fabsf(pv[t]);
   }
-  // two chained 16x16x32 bf16 MFMAs (same opcode): K slots [H1 | H2] and [H3 | 0]
+  // one 16x16x32 bf16 MFMA per tile: K slots [H1 | H2] against [q | q]
   const v4u A1u = {h1[0] | (h1[1] << 16), h1[2] | (h1[3] << 16), h2[0] | (h2[1] << 16), h2[2] | (h2[3] << 16)};
-  const v4u A2u = {h3[0] | (h3[1] << 16), h3[2] | (h3[3] << 16), 0u, 0u};
   const v8bf A1 = __builtin_bit_cast(v8bf, A1u);
-  const v8bf A2 = __builtin_bit_cast(v8bf, A2u);
 
   // ---- candidate scales.  Tile tau holds codes 16*tau + i + 1.  Tile 0 (codes 1..16) uses
   // s0/is0 directly.  For tau >= 1 the lane's codes share one E4M3 mantissa and step the exponent
@@ -416,7 +415,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 
       // Scoring of tile tau (16 codes): quotients (with exact overrides) -> FP4 round trip
       // q' = q * 4^(tau-1) (exact in bf16), e = fma(q', s, -w), y = H q' on bf16 MFMA (H in
-      // three pieces, products exact, fp32 accumulation), (H e + 2b)_i = s y_i - (H w - 2b)_i,
+      // two pieces, products exact, fp32 accumulation), (H e + 2b)_i = s y_i - (H w - 2b)_i,
       // L = sum_i e_i (H e + 2b)_i.  Instantiated twice so the common case has no override code.
       auto score = [&](auto ovr_tag, float Lq[2], float Aq[2]) {
         constexpr bool OVR = decltype(ovr_tag)::value;
@@ -457,8 +456,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
             const int tau = 4 * q + u;
             const v4u Bu = {p01, p23, p01, p23};
             const v8bf B = __builtin_bit_cast(v8bf, Bu);
-            v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, zero4, 0, 0, 0);
-            y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, y, 0, 0, 0);
+            const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, zero4, 0, 0, 0);
             if (tau < 7) tile_err(tau + 1, en, pn01, pn23);         // overlaps the MFMAs
             const float sb = tau == 0 ? s0 : s1;
             float sp = fabsf(e[0]) * dm[0];
