@@ -52,6 +52,7 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per workgroup; wave w takes block column 4*bx + w
 constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
+constexpr int kExactRows = 16;       // rows per wave of the float64 passes
 // Filter error bound factor.  Full form: the fp32 arithmetic contributes at most about
 // 2^-19 A and the two-piece bf16 split of H at most 2^-18 A (A_k as in the header), so 2^-16
 // leaves a margin above 2.5x; diagonal form: under 5e-6 L.
@@ -645,84 +646,80 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ExactLds& L = lds_all[wave];
   const int64_t nb = cin / 16;
-  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  // wave: rows c0 .. c0+kExactRows-1, block columns n0 .. n0+63 (a row's code bytes are
+  // contiguous, so each row's scan is one coalesced 64-byte read)
+  const int64_t c0 = ((int64_t)blockIdx.x * kWaves + wave) * kExactRows;
+  const int64_t n0 = (int64_t)blockIdx.y * 64;
   const int64_t g = blockIdx.z;
-  const int64_t c_begin = (int64_t)blockIdx.y * kRowsPerWave;
-  if (n >= nb || c_begin >= cout) return;
-  const int64_t c_end = min(cout, c_begin + kRowsPerWave);
-  // which of this wave's rows are pending (one row per lane)
-  const int64_t myc = c_begin + lane;
-  const bool pend = lane < kRowsPerWave && myc < c_end && code[(g * cout + myc) * nb + n] == 0;
-  unsigned long long todo = __ballot(pend);
-  if (!todo) return;
-
-  const float* Hn = Hg + (g * nb + n) * 256;
-  for (int q = 0; q < 4; ++q) L.H[lane * 4 + q] = Hn[lane * 4 + q];
-  if (COUPLED) {
-    const float* Pn = Pg + (g * nb + n) * 256;
-    for (int q = 0; q < 4; ++q) L.P[lane * 4 + q] = Pn[lane * 4 + q];
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  double tr = 0.0;
-  for (int j = 0; j < 16; ++j) tr += (double)L.H[j * 17];
-  const bool dead = (tr == 0.0);
-  const bool coupled = COUPLED && !dead;
   const float gsc = global_scale(amax[g]);
-
-  while (todo) {
-    const int r = __builtin_ctzll(todo);
-    todo &= todo - 1;
-    const int64_t c = c_begin + r;
-    const int64_t base = (g * cout + c) * cin + n * 16;
-    if (lane < 16) L.w[lane] = load_w(W, BF16, base + lane);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    if (lane < 16) {
-      double acc = 0.0;
-      if (coupled)
-        for (int j = 0; j < 16; ++j) acc += (double)L.P[lane * 16 + j] * (double)L.w[j];
-      L.b[lane] = acc;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    double best = __builtin_inf();
-    int bestK = 1 << 20;
-    for (int h = 0; h < 2; ++h) {
-      const int k = lane + 1 + 64 * h;
-      if (k > 126) continue;
-      const float sk = cand_scale(k, gsc);
-      double e[16];
-      int nib;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) e[j] = exact_err(L.w[j], sk, &nib);
-      double Ls = 0.0;
-#pragma unroll
-      for (int r2 = 0; r2 < 16; ++r2) {
-        double y = 0.0;
-        if (dead) {
-          y = e[r2];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) y += (double)L.H[r2 * 16 + j] * e[j];
-        }
-        Ls += e[r2] * (y + 2.0 * L.b[r2]);
+  const int64_t myn = n0 + lane;
+  for (int64_t c = c0; c < min(cout, c0 + kExactRows); ++c) {
+    unsigned long long todo = __ballot(myn < nb && code[(g * cout + c) * nb + myn] == 0);
+    while (todo) {
+      const int64_t n = n0 + __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const float* Hn = Hg + (g * nb + n) * 256;
+      for (int q = 0; q < 4; ++q) L.H[lane * 4 + q] = Hn[lane * 4 + q];
+      if (COUPLED) {
+        const float* Pn = Pg + (g * nb + n) * 256;
+        for (int q = 0; q < 4; ++q) L.P[lane * 4 + q] = Pn[lane * 4 + q];
       }
-      if (Ls < best) { best = Ls; bestK = k; }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      double tr = 0.0;
+      for (int j = 0; j < 16; ++j) tr += (double)L.H[j * 17];
+      const bool dead = (tr == 0.0);
+      const bool coupled = COUPLED && !dead;
+      const int64_t base = (g * cout + c) * cin + n * 16;
+      if (lane < 16) L.w[lane] = load_w(W, BF16, base + lane);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      if (lane < 16) {
+        double acc = 0.0;
+        if (coupled)
+          for (int j = 0; j < 16; ++j) acc += (double)L.P[lane * 16 + j] * (double)L.w[j];
+        L.b[lane] = acc;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      double best = __builtin_inf();
+      int bestK = 1 << 20;
+      for (int h = 0; h < 2; ++h) {
+        const int k = lane + 1 + 64 * h;
+        if (k > 126) continue;
+        const float sk = cand_scale(k, gsc);
+        double e[16];
+        int nib;
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) e[j] = exact_err(L.w[j], sk, &nib);
+        double Ls = 0.0;
+  #pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) {
+          double y = 0.0;
+          if (dead) {
+            y = e[r2];
+          } else {
+  #pragma unroll
+            for (int j = 0; j < 16; ++j) y += (double)L.H[r2 * 16 + j] * e[j];
+          }
+          Ls += e[r2] * (y + 2.0 * L.b[r2]);
+        }
+        if (Ls < best) { best = Ls; bestK = k; }
+      }
+      wave_argmin_d(best, bestK);
+      const float sw = cand_scale(bestK, gsc);
+      if (lane < 8 && fp4) {
+        int lo, hi;
+        exact_err(L.w[2 * lane], sw, &lo);
+        exact_err(L.w[2 * lane + 1], sw, &hi);
+        fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(lo | (hi << 4));
+      }
+      if (lane == 0) {
+        code[(g * cout + c) * nb + n] = (uint8_t)bestK;
+        if (loss) loss[(g * cout + c) * nb + n] = (float)best;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    wave_argmin_d(best, bestK);
-    const float sw = cand_scale(bestK, gsc);
-    if (lane < 8 && fp4) {
-      int n0, n1;
-      exact_err(L.w[2 * lane], sw, &n0);
-      exact_err(L.w[2 * lane + 1], sw, &n1);
-      fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(n0 | (n1 << 4));
-    }
-    if (lane == 0) {
-      code[(g * cout + c) * nb + n] = (uint8_t)bestK;
-      if (loss) loss[(g * cout + c) * nb + n] = (float)best;
-    }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -945,60 +942,58 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
     float* __restrict__ loss) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = cin / 16;
-  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  // wave: rows c0 .. c0+kExactRows-1, block columns n0 .. n0+63 (see k_sweep_full_exact)
+  const int64_t c0 = ((int64_t)blockIdx.x * kWaves + wave) * kExactRows;
+  const int64_t n0 = (int64_t)blockIdx.y * 64;
   const int64_t g = blockIdx.z;
-  const int64_t c_begin = (int64_t)blockIdx.y * kRowsPerWave;
-  if (n >= nb || c_begin >= cout) return;
-  const int64_t c_end = min(cout, c_begin + kRowsPerWave);
-  const int64_t myc = c_begin + lane;
-  const bool pend = lane < kRowsPerWave && myc < c_end && code[(g * cout + myc) * nb + n] == 0;
-  unsigned long long todo = __ballot(pend);
-  if (!todo) return;
-  float im[16];
-  double isum = 0.0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    im[j] = imp[g * cin + n * 16 + j];
-    isum += (double)im[j];
-  }
-  if (isum == 0.0) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) im[j] = 1.0f;
-  }
   const float gsc = global_scale(amax[g]);
-  while (todo) {
-    const int r = __builtin_ctzll(todo);
-    todo &= todo - 1;
-    const int64_t c = c_begin + r;
-    const int64_t base = (g * cout + c) * cin + n * 16;
-    float w[16];
-    load_w16<BF16>(W, base, w);
-    double best = __builtin_inf();
-    int bestK = 1 << 20;
-    for (int h = 0; h < 2; ++h) {
-      const int k = lane + 1 + 64 * h;
-      if (k > 126) continue;
-      const float sk = cand_scale(k, gsc);
-      double Ls = 0.0;
-      int nib;
-#pragma unroll
+  const int64_t myn = n0 + lane;
+  for (int64_t c = c0; c < min(cout, c0 + kExactRows); ++c) {
+    unsigned long long todo = __ballot(myn < nb && code[(g * cout + c) * nb + myn] == 0);
+    while (todo) {
+      const int64_t n = n0 + __builtin_ctzll(todo);
+      todo &= todo - 1;
+      float im[16];
+      double isum = 0.0;
+  #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const double e = exact_err(w[j], sk, &nib);
-        Ls += (double)im[j] * e * e;
+        im[j] = imp[g * cin + n * 16 + j];
+        isum += (double)im[j];
       }
-      if (Ls < best) { best = Ls; bestK = k; }
-    }
-    wave_argmin_d(best, bestK);
-    if (lane < 8 && fp4) {
-      const float sw = cand_scale(bestK, gsc);
-      int n0, n1;
-      exact_err(load_w(W, BF16, base + 2 * lane), sw, &n0);
-      exact_err(load_w(W, BF16, base + 2 * lane + 1), sw, &n1);
-      fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(n0 | (n1 << 4));
-    }
-    if (lane == 0) {
-      code[(g * cout + c) * nb + n] = (uint8_t)bestK;
-      if (loss) loss[(g * cout + c) * nb + n] = (float)best;
+      if (isum == 0.0) {
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) im[j] = 1.0f;
+      }
+      const int64_t base = (g * cout + c) * cin + n * 16;
+      float w[16];
+      load_w16<BF16>(W, base, w);
+      double best = __builtin_inf();
+      int bestK = 1 << 20;
+      for (int h = 0; h < 2; ++h) {
+        const int k = lane + 1 + 64 * h;
+        if (k > 126) continue;
+        const float sk = cand_scale(k, gsc);
+        double Ls = 0.0;
+        int nib;
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const double e = exact_err(w[j], sk, &nib);
+          Ls += (double)im[j] * e * e;
+        }
+        if (Ls < best) { best = Ls; bestK = k; }
+      }
+      wave_argmin_d(best, bestK);
+      if (lane < 8 && fp4) {
+        const float sw = cand_scale(bestK, gsc);
+        int lo, hi;
+        exact_err(load_w(W, BF16, base + 2 * lane), sw, &lo);
+        exact_err(load_w(W, BF16, base + 2 * lane + 1), sw, &hi);
+        fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(lo | (hi << 4));
+      }
+      if (lane == 0) {
+        code[(g * cout + c) * nb + n] = (uint8_t)bestK;
+        if (loss) loss[(g * cout + c) * nb + n] = (float)best;
+      }
     }
   }
 }
@@ -1013,10 +1008,13 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + kRowsPerWave - 1) / kRowsPerWave),
             (unsigned)n_groups);
   dim3 block(kWaves * 64);
+  // float64 pass: a wave per (kExactRows rows, 64 block columns)
+  const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
+                   (unsigned)((nb + 63) / 64), (unsigned)n_groups);
 #define LH_SWEEP_PAIR(B, C)                                                                        \
   hipLaunchKernelGGL((k_sweep_full<B, C>), grid, block, 0, stream, W, cout, cin, amax, H, P, code, \
                      fp4, loss);                                                                   \
-  hipLaunchKernelGGL((k_sweep_full_exact<B, C>), grid, block, 0, stream, W, cout, cin, amax, H, P, \
+  hipLaunchKernelGGL((k_sweep_full_exact<B, C>), xgrid, block, 0, stream, W, cout, cin, amax, H, P, \
                      code, fp4, loss)
   if (bf16 && P) {
     LH_SWEEP_PAIR(true, true);
@@ -1039,12 +1037,14 @@ hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + kRowsPerWave - 1) / kRowsPerWave),
             (unsigned)n_groups);
   dim3 block(kWaves * 64);
+  const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
+                   (unsigned)((nb + 63) / 64), (unsigned)n_groups);
   if (bf16) {
     hipLaunchKernelGGL((k_sweep_diag<true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
-    hipLaunchKernelGGL((k_sweep_diag_exact<true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
+    hipLaunchKernelGGL((k_sweep_diag_exact<true>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
   } else {
     hipLaunchKernelGGL((k_sweep_diag<false>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
-    hipLaunchKernelGGL((k_sweep_diag_exact<false>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
+    hipLaunchKernelGGL((k_sweep_diag_exact<false>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
   }
   return hipGetLastError();
 }
