@@ -114,8 +114,8 @@ lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype,
  * fp4         [n_groups, cout, cin/2] uint8 or NULL: nibble = (w < 0) << 3 | grid index,
  *             element 2j in the low nibble of byte j.
  * best_loss   [n_groups, cout, cin/16] fp32 or NULL: L_{k*} (may be negative with P).
- * Errors: INVALID_ARGUMENT for n_groups < 1, cout < 0, cin <= 0 or cin % 16, NULL required
- * pointers, non-device or mixed-device pointers.
+ * Errors: INVALID_ARGUMENT for n_groups outside [1, 65535], cout outside [0, 2097120], cin <= 0
+ * or cin % 16, NULL required pointers, non-device or mixed-device pointers.
  */
 lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
                          int64_t cin, const float* global_amax, const float* H, const float* P,

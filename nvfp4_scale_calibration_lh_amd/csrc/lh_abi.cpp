@@ -231,7 +231,8 @@ lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t row
 
 lh_status check_sweep_shapes(int64_t n_groups, int64_t cout, int64_t cin) {
   if (n_groups < 1 || n_groups > 65535) return fail(LH_ERR_INVALID_ARGUMENT, "n_groups must be in [1, 65535] (got %lld)", (long long)n_groups);
-  if (cout < 0 || cout > 65535LL * 64) return fail(LH_ERR_INVALID_ARGUMENT, "cout out of range (got %lld)", (long long)cout);
+  // the sweep grid takes 32 rows per workgroup along its 16-bit y dimension
+  if (cout < 0 || cout > 65535LL * 32) return fail(LH_ERR_INVALID_ARGUMENT, "cout must be in [0, 2097120] (got %lld)", (long long)cout);
   if (cin <= 0 || cin % 16) return fail(LH_ERR_INVALID_ARGUMENT, "cin must be a positive multiple of 16 (got %lld)", (long long)cin);
   return LH_OK;
 }

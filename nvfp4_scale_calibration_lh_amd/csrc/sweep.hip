@@ -36,10 +36,12 @@
 //    float64 with exact quantization; otherwise the block's code is left at 0 and a second
 //    kernel re-scores all 126 candidates in float64.  The fp32 quotient w*(1/s) can fall on the
 //    wrong side of an E2M1 rounding midpoint m only when |w|/s_k is within a few ulps of m, i.e.
-//    when |w|/(m g) is within a few ulps of an E4M3 value; once per block every (element,
-//    midpoint) pair is tested, and for a flagged pair the one affected candidate gets the exact
-//    decision (the sign of fma(m, s_k, -|w|)) in place of its fp32 quotient.  The result is the
-//    argmin of the float64 objective.
+//    when |w|/(m g) is within a few ulps of an E4M3 value; in the full form every (element,
+//    midpoint) pair of a block is tested once, and for a flagged pair the one affected candidate
+//    gets the exact decision (the sign of fma(m, s_k, -|w|)) in place of its fp32 quotient.  The
+//    diagonal form needs no such override (see k_sweep_diag).  Winners' codes, nibbles and
+//    losses are always recomputed from exact rounding decisions.  The result is the argmin of
+//    the float64 objective.
 #include "lh_internal.hpp"
 
 #include <type_traits>

@@ -62,6 +62,9 @@ def test_validation_errors_without_device():
     # sweep
     assert L.lh_scale_sweep(FAKE, 1, 0, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_scale_sweep(FAKE, 1, 1, 4, 33, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep(FAKE, 1, 65536, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep(FAKE, 1, 1, 65535 * 32 + 1, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep_diag(FAKE, 1, 1, -1, 32, FAKE, FAKE, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_scale_sweep(FAKE, 1, 1, 4, 32, None, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_scale_sweep(FAKE, 9, 1, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_UNSUPPORTED
     assert L.lh_scale_sweep_diag(FAKE, 1, 1, 4, 32, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
