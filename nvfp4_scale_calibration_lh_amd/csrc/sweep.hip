@@ -39,9 +39,9 @@
 //    when |w|/(m g) is within a few ulps of an E4M3 value; in the full form every (element,
 //    midpoint) pair of a block is tested once, and for a flagged pair the one affected candidate
 //    gets the exact decision (the sign of fma(m, s_k, -|w|)) in place of its fp32 quotient.  The
-//    diagonal form needs no such override (see k_sweep_diag).  Winners' codes, nibbles and
-//    losses are always recomputed from exact rounding decisions.  The result is the argmin of
-//    the float64 objective.
+//    diagonal form needs no such override (see k_sweep_diag).  A winner's nibbles are always
+//    exact rounding decisions and its reported loss is evaluated again from them.  The result
+//    is the argmin of the float64 objective.
 #include "lh_internal.hpp"
 
 #include <type_traits>
