@@ -37,11 +37,22 @@ FLOPS_COUPLED = 126 * (32 + 512 + 32 + 32) + 512
 FLOPS_DIAG = 126 * (32 + 48)
 
 
+def code_digest(path):
+    """sha256 of a kernel source with its comments and whitespace removed: it changes when the
+    code changes, not when a comment does."""
+    import hashlib
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def measured_traffic(cfg, prefix):
     """HBM bytes per call of the kernels whose names start with `prefix`, from the rocprofv3
     FETCH_SIZE / WRITE_SIZE passes recorded in profiles/traffic.json, scaled by the copy-kernel
-    calibration factors.  None when no record exists or a kernel source changed since."""
-    import hashlib
+    calibration factors.  None when no record exists or a kernel's code changed since."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             rec = json.load(f)
@@ -54,9 +65,8 @@ def measured_traffic(cfg, prefix):
             continue
         src = os.path.join(ROOT, "nvfp4_scale_calibration_lh_amd", "csrc", v.get("source", ""))
         try:
-            with open(src, "rb") as f:
-                if hashlib.sha256(f.read()).hexdigest() != v["source_sha256"]:
-                    return None
+            if code_digest(src) != v.get("code_sha256"):
+                return None
         except OSError:
             return None
         total += v["fetch_kib"] * 1024 * rec["fetch_factor"] + v["write_kib"] * 1024 * rec["write_factor"]
