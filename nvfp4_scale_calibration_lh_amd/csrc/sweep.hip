@@ -29,10 +29,13 @@
 //  * Diagonal form: VALU only (there is no contraction to map onto MFMA); lane l scores
 //    candidates l+1 and l+65 over all 16 elements, whose weights are wave-uniform.
 //  * Exactness.  The float32 pass is a filter: each candidate carries a rigorous bound c*A_k on
-//    its rounding error (A_k = S_e (4 S_e + S_w) + 2|e|^T(|P||w|) with S_e = sum_i |e_i| d_i,
-//    S_w = sum_i |w_i| d_i and d_i^2 = max_j max(|H_ij|, |H_ji|); L_k itself in the diagonal
-//    form).  If exactly one candidate can be
-//    the minimum it is the exact argmin; with 2 to 4 contenders the wave re-scores them in
+//    its rounding error, with A_k >= S_e^2 + S_e S_w + 2|e|^T(|P||w|), S_e = sum_i |e_i| d_i,
+//    S_w = sum_i |w_i| d_i and d_i^2 = max_j max(|H_ij|, |H_ji|) (A_k = S_e (4 S_e + S_w)
+//    without P; with P the 4 S_e^2 is taken as 4 times the sum of the squared parts of S_e over
+//    the four lane groups, which is >= S_e^2; L_k itself in the diagonal form).  Every exact
+//    L_k lies in [L_k - cA_k, L_k + cA_k]; the candidates whose interval starts below the
+//    lowest upper end are the only ones that can be the minimum.  If there is one, it is
+//    the exact argmin; with 2 to 4 contenders the wave re-scores them in
 //    float64 with exact quantization; otherwise the block's code is left at 0 and a second
 //    kernel re-scores all 126 candidates in float64.  The fp32 quotient w*(1/s) can fall on the
 //    wrong side of an E2M1 rounding midpoint m only when |w|/s_k is within a few ulps of m, i.e.
@@ -55,9 +58,9 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;            // waves per workgroup; wave w takes block column 4*bx + w
 constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
 constexpr int kExactRows = 16;       // rows per wave of the float64 passes
-// Filter error bound factor.  Full form: the fp32 arithmetic contributes at most about
-// 2^-19 A and the two-piece bf16 split of H at most 2^-18 A (A_k as in the header), so 2^-16
-// leaves a margin above 2.5x; diagonal form: under 5e-6 L.
+// Filter error bound factor.  Full form: the fp32 arithmetic and the two-piece bf16 split of H
+// together contribute at most about 2^-17.2 (S_e^2 + S_e S_w + 2|e|^T(|P||w|)) <= 2^-17.2 A
+// (A_k as in the header), so 2^-16 leaves a margin above 2x; diagonal form: under 5e-6 L.
 constexpr float kErrC = 0x1p-16f;
 constexpr int kNearUlps = 16;        // midpoint proximity test, in ulps of |w|/(m g)
 
@@ -183,26 +186,6 @@ __device__ inline float load_w(const void* W, bool bf16, int64_t idx) {
   return ((const float*)W)[idx];
 }
 
-template <int CTRL>
-__device__ inline float dppf(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// Minimum over the 16 lanes of each DPP row (row_ror by 8, 4, 2, 1); every lane gets the result.
-__device__ inline float row_min(float v) {
-  v = fminf(v, dppf<0x128>(v));
-  v = fminf(v, dppf<0x124>(v));
-  v = fminf(v, dppf<0x122>(v));
-  v = fminf(v, dppf<0x121>(v));
-  return v;
-}
-// Minimum over all 64 lanes.
-__device__ inline float wave_min(float v) {
-  v = row_min(v);
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 // Minimum over all 64 lanes of a value >= 0 (or +inf): the bit patterns of such floats are
 // ordered like unsigned integers, so the reduction needs no float canonicalization.
 template <int CTRL>
@@ -219,6 +202,24 @@ __device__ inline float wave_min_nonneg(float x) {
   v = min((unsigned)a[0], (unsigned)a[1]);
   auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return __uint_as_float(min((unsigned)b[0], (unsigned)b[1]));
+}
+// Minimum over all 64 lanes of a float that is not NaN, taken on integer keys whose signed
+// order is the float order (negative values have their magnitude bits flipped).
+template <int CTRL>
+__device__ inline int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ inline int order_key(int b) { return b ^ ((b >> 31) & 0x7FFFFFFF); }   // an involution
+__device__ inline float wave_min_ordered(float x) {
+  int v = order_key(__float_as_int(x));
+  v = min(v, dppi<0x128>(v));
+  v = min(v, dppi<0x124>(v));
+  v = min(v, dppi<0x122>(v));
+  v = min(v, dppi<0x121>(v));
+  auto a = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = min((int)a[0], (int)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return __int_as_float(order_key(min((int)b[0], (int)b[1])));
 }
 // Lowest (loss, code) over the wave in float64 (exact re-scoring).
 __device__ inline void wave_argmin_d(double& L, int& k) {
@@ -308,7 +309,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   //   a[t]   = H[i][col] in fp32 (H w per 16-row tile), pv/pa = P and |P| (P w, |P||w|)
   //   h1, h2 = H[i][col] split into two bf16 pieces, |H - H1 - H2| <= 2^-18 |H|: A operand of
   //            the bf16 MFMA that forms H q for the candidates
-  //   dm[t]  = sqrt(max_j max(|H_col,j|, |H_j,col|)), so |H_ij| <= dm_i dm_j for any H
+  //   dm[t]  = d_col = sqrt(max_j max(|H_col,j|, |H_j,col|)), so |H_ij| <= d_i d_j for any H
+  //            (2 d_col in the coupled form)
   float a[4], dm[4], pa[4], pv[4];
   unsigned h1[4], h2[4];
 #pragma unroll
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       mx = 0.0f;
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(fabsf(L.H[col * 16 + j]), fabsf(L.H[j * 16 + col])));
     }
-    dm[t] = sqrtf(mx) * 1.0000002f;               // with sqrt rounding margin
+    dm[t] = sqrtf(mx) * (COUPLED ? 2.0000004f : 1.0000002f);   // (2x when coupled) with sqrt margin
     pv[t] = coupled ? L.P[i * 16 + col] : 0.0f;
     pa[t] = fabsf(pv[t]);
   }
@@ -383,18 +385,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
       const int64_t oblk = (g * cout + c) * nb + n;
-      float w[4], gq[4], pw2[4];
+      float w[4], gq[4], om[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         w[t] = L.w[rr][4 * gg + t];
         gq[t] = L.g[rr][4 * gg + t];
-        pw2[t] = (COUPLED && coupled) ? 2.0f * L.pw[rr][4 * gg + t] : 0.0f;
       }
       float swp = fabsf(w[0]) * dm[0];
       swp = fmaf(fabsf(w[1]), dm[1], swp);
       swp = fmaf(fabsf(w[2]), dm[2], swp);
       swp = fmaf(fabsf(w[3]), dm[3], swp);
-      const float S_w = group_sum(swp) * 1.0000005f;   // sum_j dm_j |w_j| (rounded up)
+      // S_w = sum_j d_j |w_j| (rounded up; the coupled form's dm carries 2 d)
+      const float S_w = group_sum(swp) * (COUPLED ? 0.50000025f : 1.0000005f);
+      if (COUPLED) {
+        // weights of |e_t| in the linear part of the bound: d_t S_w + 2 (|P||w|)_t
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          om[t] = fmaf(dm[t], 0.5f * S_w, coupled ? 2.0f * L.pw[rr][4 * gg + t] : 0.0f);
+      }
 
       // quotients within a few ulps of an E2M1 midpoint are decided exactly (fma sign test)
       const float wp0 = L.w[rr][p0 / 7], wp1 = L.w[rr][(p1 < 112 ? p1 : 0) / 7];
@@ -462,17 +470,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
             const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, zero4, 0, 0, 0);
             if (tau < 7) tile_err(tau + 1, en, pn01, pn23);         // overlaps the MFMAs
             const float sb = tau == 0 ? s0 : s1;
+            // bound: uncoupled, this lane's part of S_e = sum_i d_i |e_i| (A follows after the
+            // group sum); coupled, (2 S_e,g)^2 + sum_i |e_i| om_i over the lane's 4 elements,
+            // whose sum over the 4 groups is >= S_e^2 + S_e S_w + 2|e|^T(|P||w|) (Cauchy-Schwarz)
             float sp = fabsf(e[0]) * dm[0];
             sp = fmaf(fabsf(e[1]), dm[1], sp);
             sp = fmaf(fabsf(e[2]), dm[2], sp);
             sp = fmaf(fabsf(e[3]), dm[3], sp);
-            float ap = sp * fmaf(4.0f, sp, S_w);
+            float ap = sp;
             if (COUPLED) {
-              float bp = fabsf(e[0]) * pw2[0];
-              bp = fmaf(fabsf(e[1]), pw2[1], bp);
-              bp = fmaf(fabsf(e[2]), pw2[2], bp);
-              bp = fmaf(fabsf(e[3]), pw2[3], bp);
-              ap += bp;
+              float tp = fabsf(e[0]) * om[0];
+              tp = fmaf(fabsf(e[1]), om[1], tp);
+              tp = fmaf(fabsf(e[2]), om[2], tp);
+              tp = fmaf(fabsf(e[3]), om[3], tp);
+              ap = fmaf(sp, sp, tp);
             }
             float lp = e[0] * fmaf(sb, y[0], -gq[0]);
             lp = fmaf(e[1], fmaf(sb, y[1], -gq[1]), lp);
@@ -489,31 +500,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
           }
           Lq[q] = quad_sum(pl);
           Aq[q] = quad_sum(pa4);
+          if (!COUPLED) Aq[q] *= fmaf(4.0f, Aq[q], S_w);   // A = S_e (4 S_e + S_w)
         }
       };
       float Lq[2], Aq[2];
       if (has_ovr) score(std::true_type{}, Lq, Aq);
       else score(std::false_type{}, Lq, Aq);
 
-      // lane (row gg, column i) now holds codes k_q = 16*(4q+gg) + i + 1 for q = 0, 1
-      const int kq0 = 16 * gg + i + 1, kq1 = 16 * (4 + gg) + i + 1;
-      if (kq1 > 126) Lq[1] = __builtin_inff();
-      float bestL = Lq[0], bestA = Aq[0];
-      int bestK = kq0;
-      if (Lq[1] < bestL) { bestL = Lq[1]; bestA = Aq[1]; bestK = kq1; }
-      // winner k* = a lane holding the wave minimum.  k* is the exact argmin when every other
-      // candidate's lower bound exceeds k*'s upper bound (L_k - cA_k > L* + cA*).
-      const float mL = wave_min(bestL);
-      const int owner = (int)__builtin_ctzll(__ballot(bestL == mL));
-      const int k_best = __builtin_amdgcn_readlane(bestK, owner);
-      const float A_best = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bestA), owner));
-      const float U = fmaf(kErrC, A_best, mL);
+      // lane l now holds codes l + 1 (tiles 0..3) and l + 65 (tiles 4..7); 127 and 128 do not exist
+      if (lane >= 62) Lq[1] = __builtin_inff();
+      // Each candidate's exact loss lies in [L_k - cA_k, L_k + cA_k].  U, the lowest upper end,
+      // is >= the exact minimum, so the exact argmin is one of the candidates whose lower end is
+      // <= U; when there is only one, it is the argmin.
+      const float u0 = fmaf(kErrC, Aq[0], Lq[0]), u1 = fmaf(kErrC, Aq[1], Lq[1]);
+      const float U = wave_min_ordered(u1 < u0 ? u1 : u0);
       const unsigned long long M0 = __ballot(fmaf(-kErrC, Aq[0], Lq[0]) <= U);
       const unsigned long long M1 = __ballot(fmaf(-kErrC, Aq[1], Lq[1]) <= U);
       const int cnt = __popcll(M0) + __popcll(M1);
       if (cnt == 1) {
         // unique winner: emit its codes.  Its scale and reciprocal come from the lane that owns
         // it (tiles >= 1 apply their power of 4 exactly).
+        const int k_best = M0 ? (int)__builtin_ctzll(M0) + 1 : (int)__builtin_ctzll(M1) + 65;
         const int kb0 = k_best - 1;
         const int src = kb0 & 15;
         float iw, sw;
@@ -521,9 +528,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
           iw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(is0), src));
           sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s0), src));
         } else {
-          const float sc = (float)(1u << (2 * ((kb0 >> 4) - 1)));
-          iw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(is1), src)) / sc;
-          sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), src)) * sc;
+          const int sh = 2 * ((kb0 >> 4) - 1);
+          iw = __builtin_amdgcn_ldexpf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(is1), src)), -sh);
+          sw = __builtin_amdgcn_ldexpf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), src)), sh);
         }
         float rw[4];
 #pragma unroll
@@ -546,7 +553,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
           if (lane == 0) L.ws[rr] = sw;
           emitted |= 1u << rr;
         }
-      } else if (cnt <= 4) {
+      } else if (cnt >= 2 && cnt <= 4) {
         // 2..4 contenders: re-score them exactly in float64, 16 lanes (one per element) each
         unsigned long long ma = M0, mb = M1;
         auto next = [&]() -> int {
