@@ -249,7 +249,8 @@ struct FullLds {
   float P[256];
   float w[16][16];     // current 16-row tile: w[row][elem]
   float g[16][16];     // (H w - 2 P w)[row][elem]
-  float pw[16][16];    // (|P| |w|)[row][elem]
+  float pw[16][16];    // bound weights d S_w + 2 |P||w| [row][elem] (coupled form)
+  float sw[16];        // S_w = sum_j d_j |w_j| per row
   float b[16][16];     // (P w)[row][elem]           } the loss of the tile's
   float ws[16];        // winner's scale per row      } filter-decided winners
   unsigned short wn[16][4];   // winner's signed nibbles per row and lane group
@@ -355,8 +356,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     const bool row_on = crow < c_end;
     float wt[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      wt[t] = row_on ? load_w(W, BF16, (g * cout + crow) * cin + n * 16 + 4 * gg + t) : 0.0f;
+    for (int t = 0; t < 4; ++t)   // + 0 turns -0 into +0, so the FP4 converts' sign bit is (w < 0)
+      wt[t] = row_on ? load_w(W, BF16, (g * cout + crow) * cin + n * 16 + 4 * gg + t) + 0.0f : 0.0f;
     v4f hw = zero4, bt = zero4, pwt = zero4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) hw = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], wt[t], hw, 0, 0, 0);
@@ -367,16 +368,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
         pwt = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[t], fabsf(wt[t]), pwt, 0, 0, 0);
       }
     }
+    // S_w of row i (rounded up; the coupled form's dm carries 2 d)
+    float swt = fabsf(wt[0]) * dm[0];
+    swt = fmaf(fabsf(wt[1]), dm[1], swt);
+    swt = fmaf(fabsf(wt[2]), dm[2], swt);
+    swt = fmaf(fabsf(wt[3]), dm[3], swt);
+    const float swr = group_sum(swt) * (COUPLED ? 0.50000025f : 1.0000005f);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {                  // lane holds elements 4gg+t of row i
       L.w[i][4 * gg + t] = wt[t];
       L.g[i][4 * gg + t] = coupled ? fmaf(-2.0f, bt[t], hw[t]) : hw[t];
       if (COUPLED) {
-        L.pw[i][4 * gg + t] = pwt[t];
+        // weight of |e_t| in the linear part of the bound: d_t S_w + 2 (|P||w|)_t
+        L.pw[i][4 * gg + t] = fmaf(dm[t], 0.5f * swr, coupled ? 2.0f * pwt[t] : 0.0f);
         L.b[i][4 * gg + t] = bt[t];
       }
     }
+    if (gg == 0) L.sw[i] = swr;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -390,19 +399,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       for (int t = 0; t < 4; ++t) {
         w[t] = L.w[rr][4 * gg + t];
         gq[t] = L.g[rr][4 * gg + t];
+        om[t] = COUPLED ? L.pw[rr][4 * gg + t] : 0.0f;
       }
-      float swp = fabsf(w[0]) * dm[0];
-      swp = fmaf(fabsf(w[1]), dm[1], swp);
-      swp = fmaf(fabsf(w[2]), dm[2], swp);
-      swp = fmaf(fabsf(w[3]), dm[3], swp);
-      // S_w = sum_j d_j |w_j| (rounded up; the coupled form's dm carries 2 d)
-      const float S_w = group_sum(swp) * (COUPLED ? 0.50000025f : 1.0000005f);
-      if (COUPLED) {
-        // weights of |e_t| in the linear part of the bound: d_t S_w + 2 (|P||w|)_t
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          om[t] = fmaf(dm[t], 0.5f * S_w, coupled ? 2.0f * L.pw[rr][4 * gg + t] : 0.0f);
-      }
+      const float S_w = L.sw[rr];
 
       // quotients within a few ulps of an E2M1 midpoint are decided exactly (fma sign test)
       const float wp0 = L.w[rr][p0 / 7], wp1 = L.w[rr][(p1 < 112 ? p1 : 0) / 7];
@@ -539,11 +538,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
           apply_overrides(m0, 0, kv0, rv0, -1, k_best, i, gg, rw);
           apply_overrides(m1, 64, kv1, rv1, -1, k_best, i, gg, rw);
         }
-        unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, rw[0], rw[1], 1.0f, 0);
-        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, rw[2], rw[3], 1.0f, 1);
-        unsigned nb4 = pk & 0x7777u;                                   // magnitudes
-        nb4 |= (w[0] < 0.0f ? 0x8u : 0u) | (w[1] < 0.0f ? 0x80u : 0u) |
-               (w[2] < 0.0f ? 0x800u : 0u) | (w[3] < 0.0f ? 0x8000u : 0u);
+        // the converts' sign bit is the sign of w, which is (w < 0) since w is never -0
+        unsigned nb4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, rw[0], rw[1], 1.0f, 0);
+        nb4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(nb4, rw[2], rw[3], 1.0f, 1);
         if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
         if (lane == 0) code[oblk] = (uint8_t)k_best;
         if (loss) {

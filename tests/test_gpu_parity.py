@@ -202,6 +202,39 @@ def test_sweep_degenerate_blocks():
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
 
+
+def test_sweep_signed_zeros_bf16():
+    """bf16 weights holding -0 and tiny values that quantize to zero at every candidate: the
+    nibble is (w < 0) << 3 | index, so -0 encodes as 0x0 and a tiny negative as 0x8."""
+    r = np.random.default_rng(21)
+    G, cout, cin = 2, 70, 64
+    W = r.normal(0, 0.02, (G, cout, cin)).astype(np.float32)
+    cls = r.integers(0, 8, size=W.shape)      # disjoint classes of planted values
+    W[cls == 0] = -0.0
+    W[cls == 1] = -1e-9
+    W[cls == 2] = 1e-9
+    W[1, 9, 16:32] = -0.0                     # a block of -0 only
+    cls[1, 9, 16:32] = 0
+    Wb = synth.bf16_bits_from_f32(W)
+    W64 = synth.f32_from_bf16_bits(Wb).astype(np.float64)
+    amax = oracle.absmax(W64).astype(np.float32)
+    A = r.standard_normal((G, cin // 16, 16, 16)).astype(np.float32)
+    H = np.einsum("gnij,gnkj->gnik", A, A).astype(np.float32) / 16
+    P = (0.1 * r.standard_normal(H.shape)).astype(np.float32)
+    imp = np.abs(r.standard_normal((G, cin))).astype(np.float32)
+    note(f"sweep signed zeros bf16 G={G} cout={cout} cin={cin}")
+    Wd, ad = to_dev(Wb, "bf16"), torch.from_numpy(amax).to(DEV)
+    for with_p in (False, True):
+        code, fp4, loss = lh.lh_scale_sweep(Wd, ad, torch.from_numpy(H).to(DEV),
+                                            torch.from_numpy(P).to(DEV) if with_p else None)
+        res = oracle.sweep(W64, amax, H, P if with_p else None)
+        nib = res["nib"].reshape(G, cout, cin)
+        assert (nib[cls == 1] == 8).all() and (nib[cls == 0] == 0).all()
+        assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+    code, fp4, loss = lh.lh_scale_sweep_diag(Wd, ad, torch.from_numpy(imp).to(DEV))
+    res = oracle.sweep_diag(W64, amax, imp)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
 def test_sweep_exact_midpoint_ties():
     """Weights placed exactly on E2M1 midpoints of some candidate scale must round like the oracle."""
     r = np.random.default_rng(4)
