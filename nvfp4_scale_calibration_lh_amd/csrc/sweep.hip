@@ -862,17 +862,12 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
       L1 = fmaf(im[j + 1] * eb1, eb1, L1);
     }
     if (!v1) L1 = __builtin_inff();
-    float bestL = L0;
-    int bestK = k0;
-    if (L1 < bestL) { bestL = L1; bestK = k1; }
-    // the winner is exact when every other candidate's lower bound exceeds its upper bound
-    const float mL = wave_min_nonneg(bestL);     // losses are sums of Imp * e^2 >= 0
-    const int owner = (int)__builtin_ctzll(__ballot(bestL == mL));
-    const int k_best = __builtin_amdgcn_readlane(bestK, owner);
-    const float U = mL * (1.0f + kErrC);
+    // Exact losses lie in [L(1-c), L(1+c)]; U = (1+c) min L bounds the minimum from above, and
+    // only candidates with L(1-c) <= U can be the argmin (losses are sums of Imp e^2 >= 0).
+    const float U = wave_min_nonneg(L1 < L0 ? L1 : L0) * (1.0f + kErrC);
     const unsigned long long M0 = __ballot(L0 * (1.0f - kErrC) <= U), M1 = __ballot(L1 * (1.0f - kErrC) <= U);
     const int cnt = __popcll(M0) + __popcll(M1);
-    int kwin = k_best;
+    int kwin = M0 ? (int)__builtin_ctzll(M0) + 1 : (int)__builtin_ctzll(M1) + 65;
     if (cnt > 1 && cnt <= 4) {
       // 2..4 contenders: exact float64 losses, one contender per 16 lanes (lane: element l%16)
       unsigned long long ma = M0, mb = M1;
@@ -901,8 +896,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     const int wl = (kwin - 1) & 63;               // the lane that holds code kwin
     const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kwin <= 64 ? s0 : s1), wl));
     if (lane == 0) {
-      if (cnt > 4) code[oblk] = 0;                // many contenders: float64 pass
-      win_k[wave][rr] = cnt <= 4 ? kwin : 0;
+      const bool decided = cnt >= 1 && cnt <= 4;
+      if (!decided) code[oblk] = 0;               // many contenders (or none): float64 pass
+      win_k[wave][rr] = decided ? kwin : 0;
       win_s[wave][rr] = sw;
     }
   }
