@@ -7,6 +7,8 @@
 // combine with an unsigned atomicMax on the output word, which an init kernel sets to 0 first.
 #include "lh_internal.hpp"
 
+#include <algorithm>
+
 namespace lh {
 namespace {
 
@@ -30,18 +32,25 @@ __global__ __launch_bounds__(kThreads) void k_absmax_vec(const v4u* __restrict__
                                                          int64_t vec_per_group, unsigned* out) {
   const int g = blockIdx.y;
   const v4u* base = W + (int64_t)g * vec_per_group;
-  unsigned m = 0;
-  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < vec_per_group;
-       i += (int64_t)gridDim.x * kThreads) {
-    const v4u v = __builtin_nontemporal_load(base + i);
+  auto absmax16 = [](const v4u v) -> unsigned {       // largest |x| of the 16 bytes, as bits
     if (BF16) {
-      unsigned a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-      unsigned b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
-      m = max(m, max(a, b) << 16);
-    } else {
-      m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+      const unsigned a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+      const unsigned b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+      return max(a, b) << 16;
     }
+    return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+  };
+  unsigned m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  for (; i + 3 * stride < vec_per_group; i += 4 * stride) {   // four loads in flight
+    const v4u v0 = __builtin_nontemporal_load(base + i);
+    const v4u v1 = __builtin_nontemporal_load(base + i + stride);
+    const v4u v2 = __builtin_nontemporal_load(base + i + 2 * stride);
+    const v4u v3 = __builtin_nontemporal_load(base + i + 3 * stride);
+    m = max(max(m, max(absmax16(v0), absmax16(v1))), max(absmax16(v2), absmax16(v3)));
   }
+  for (; i < vec_per_group; i += stride) m = max(m, absmax16(__builtin_nontemporal_load(base + i)));
   __shared__ unsigned red[kThreads / 64];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -90,10 +99,12 @@ hipError_t launch_absmax(const void* W, bool bf16, int64_t n_groups, int64_t ele
   const int vec = bf16 ? 8 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(W) % 16 == 0) && (elems % vec == 0);
   const int64_t units = aligned ? elems / vec : elems;
-  // about 8 units per thread, at most 256 workgroups per group
+  // about 8 units per thread; at most max(256, 16384 / n_groups) workgroups per group, so one
+  // large group still gets thousands of workgroups and many groups do not get millions
+  const int64_t cap = std::max<int64_t>(256, 16384 / n_groups);
   int64_t bx = (units + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
   if (bx < 1) bx = 1;
-  if (bx > 256) bx = 256;
+  if (bx > cap) bx = cap;
   dim3 grid((unsigned)bx, (unsigned)n_groups);
   if (aligned) {
     if (bf16)
