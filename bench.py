@@ -81,6 +81,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="c2", choices=list(synth.CONFIGS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fq", action="store_true",
+                   help="activation-aware workload: make X_q from X inside the accumulation kernel "
+                        "(lh_accumulate_act_aware_fq) instead of reading a stored X_q")
     p.add_argument("--cpu-sample-blocks", type=int, default=24576,
                    help="blocks of the oracle's sweep timed for the CPU baseline")
     p.add_argument("--rotate-gib", type=float, default=1.0)
@@ -164,7 +167,7 @@ def main():
     nb = cin // 16
     blocks = wl.weight_blocks
     esz = 2 if wl.dtype == "bf16" else 4
-    x_bytes = rows * cin * esz * (2 if wl.mode == "act" else 1)
+    x_bytes = rows * cin * esz * (2 if wl.mode == "act" and not args.fq else 1)   # X (and a stored X_q)
     w_bytes = G * cout * cin * esz
     copies = max(1, min(64, int(np.ceil(args.rotate_gib * 2 ** 30 / max(1, x_bytes + w_bytes)))))
     free = torch.cuda.mem_get_info(dev)[0]
@@ -175,7 +178,7 @@ def main():
     Xq0 = to_dev(torch, wl.Xq, wl.dtype, dev) if wl.Xq is not None else None
     Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
     Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
-    Xqs = ([Xq0] + [Xq0.clone() for _ in range(copies - 1)]) if Xq0 is not None else None
+    Xqs = ([Xq0] + [Xq0.clone() for _ in range(copies - 1)]) if Xq0 is not None and not args.fq else None
     off = torch.from_numpy(wl.offsets).to(dev) if G > 1 else None
 
     amax = torch.empty(G, dtype=torch.float32, device=dev)
@@ -189,8 +192,15 @@ def main():
     def absmax(j):
         lh.lh_absmax(Ws[j], amax)
 
+    fq = args.fq and wl.mode == "act"
+    if fq:   # the input quantizer's amax comes from its own (earlier) max calibration
+        x_amax = torch.stack([Xs[0][int(wl.offsets[g]):int(wl.offsets[g + 1])].abs().max().float()
+                              for g in range(G)])
+
     def accumulate(j):
-        if wl.mode == "act":
+        if fq:
+            lh.lh_accumulate_act_aware_fq(Xs[j], x_amax, H=H, P=P, offsets=off)
+        elif wl.mode == "act":
             lh.lh_accumulate_act_aware(Xs[j], Xqs[j], H=H, P=P, offsets=off)
         elif wl.mode == "diag":
             lh.lh_accumulate(Xs[j], H=None, imp=imp, offsets=off, want_h=False, want_imp=True)
@@ -210,6 +220,7 @@ def main():
         sweep(j)
 
     stream = torch.cuda.current_stream(dev)     # the stream the library launches on
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -239,11 +250,16 @@ def main():
     ms_abs = phase_ms(absmax)
     ms_acc = phase_ms(accumulate)
     ms_sw = phase_ms(sweep)
+    # reference: a device-to-device copy of X (the same rotating sources), bytes read + written
+    xdst = torch.empty_like(Xs[0])
+    ms_copy = phase_ms(lambda j: xdst.copy_(Xs[j]))
+    del xdst
 
     flops_blk = FLOPS_DIAG if wl.mode == "diag" else (FLOPS_COUPLED if wl.mode == "act" else FLOPS_FULL)
     sweep_tflops = flops_blk * blocks / (ms_sw * 1e-3) / 1e12
     acc_bytes = x_bytes + (G * cin * 4 if wl.mode == "diag" else G * nb * 1024 * (2 if wl.mode == "act" else 1))
     acc_gbs = acc_bytes / (ms_acc * 1e-3) / 1e9
+    copy_gbs = 2 * Xs[0].numel() * Xs[0].element_size() / (ms_copy * 1e-3) / 1e9
     abs_gbs = w_bytes / (ms_abs * 1e-3) / 1e9
     if wl.mode == "diag":
         roof = {"bound": "alu", "achieved": sweep_tflops, "peak": VALU_FP32_TFLOPS, "unit": "TFLOP/s",
@@ -271,11 +287,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.description, "name": args.config, "n_groups": G, "cout": cout,
                    "cin": cin, "rows": rows, "blocks": blocks, "input_dtype": wl.dtype,
-                   "mode": wl.mode, "rotating_copies": copies},
+                   "mode": wl.mode, "rotating_copies": copies,
+                   **({"x_q": "made in the accumulation kernel"} if args.fq and wl.mode == "act" else {})},
         "roofline": roof,
         "accumulate": {"avg_launch_ms": ms_acc, "algorithmic_bytes": acc_bytes, "achieved_gbs": acc_gbs,
                        "peak_gbs": HBM_PEAK_GBS, "frac": acc_gbs / HBM_PEAK_GBS,
-                       "traffic": measured_traffic(args.config, "k_acc")},
+                       "traffic": measured_traffic(args.config, "k_acc"),
+                       "copy_gbs": copy_gbs, "frac_of_copy": acc_gbs / copy_gbs},
         "absmax": {"avg_launch_ms": ms_abs, "achieved_gbs": abs_gbs, "frac": abs_gbs / HBM_PEAK_GBS},
         "sweep": {"avg_launch_ms": ms_sw, "blocks_per_s": blocks / (ms_sw * 1e-3), "tflops": sweep_tflops},
     }

@@ -93,6 +93,27 @@ lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype,
                                   float beta, float* H, float* P, void* stream);
 
 /*
+ * The same H and P with X_q made from X inside the kernel, so the activations are read once
+ * (PR #1976, What does this PR do?: X_q is the activation as the layer's NVFP4 input quantizer
+ * emits it; the quantizer below is the NVFP4 recipe of PR #2004, What does this PR do?
+ * (448-normalized), applied to activations per token):
+ *   gX = fp32(x_amax[g] / (6*448)) per group;
+ *   per row and 16-channel block: v = the E4M3 value (0 or one of the 126 positive finite values)
+ *     nearest to max|x| / (6 gX), ties to the even code (so it saturates at 448 and a block whose
+ *     max rounds to 0 becomes 0), s = fp32(v gX);
+ *   x_q = sign(x) * E2M1(|x| / s) * s for each element (nearest of {0,0.5,1,1.5,2,3,4,6}, ties
+ *     to the even grid index, saturating at 6; every rounding decision is the exact one), the
+ *     product taken in fp32 and rounded to nearest-even bf16 when dtype is bf16.
+ * x_amax [n_groups] fp32 device: the input quantizer's amax per group (>= 0 and finite; 0 gives
+ * X_q = 0).  Other arguments, outputs and errors as lh_accumulate_act_aware, plus
+ * INVALID_ARGUMENT for a NULL x_amax.
+ */
+lh_status lh_accumulate_act_aware_fq(const void* X, lh_dtype dtype, int64_t rows, int64_t cin,
+                                     const int64_t* group_offsets, int64_t n_groups,
+                                     const float* x_amax, float beta, float* H, float* P,
+                                     void* stream);
+
+/*
  * Exhaustive FP8 block-scale sweep with the local-Hessian objective (PR #788, review: block loss
  * cnb,nbd,cnd->cn; PR #1976, review: dw = quant(w) - w, coupling term 2 dw^T (P W0) with
  * P.W0 = nbd,cnd->cnb, best_loss = inf so negative losses are handled; PR #2283, How: the 126

@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("LH_LIBRARY") or os.path.join(_PKG, "liblh.so")
 LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 
-EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_scale_sweep", "lh_scale_sweep_diag",
+EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep", "lh_scale_sweep_diag",
             "lh_absmax", "lh_last_error", "lh_version")
 
 
@@ -46,10 +46,12 @@ def lib() -> ctypes.CDLL:
         vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
         h.lh_accumulate.argtypes = [vp, i32, i64, i64, vp, i64, f32, vp, vp, vp]
         h.lh_accumulate_act_aware.argtypes = [vp, vp, i32, i64, i64, vp, i64, f32, vp, vp, vp]
+        h.lh_accumulate_act_aware_fq.argtypes = [vp, i32, i64, i64, vp, i64, vp, f32, vp, vp, vp]
         h.lh_scale_sweep.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_diag.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         h.lh_absmax.argtypes = [vp, i32, i64, i64, vp, vp]
-        for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_scale_sweep", "lh_scale_sweep_diag", "lh_absmax"):
+        for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep",
+                  "lh_scale_sweep_diag", "lh_absmax"):
             getattr(h, f).restype = ctypes.c_int
         h.lh_last_error.argtypes = []
         h.lh_last_error.restype = ctypes.c_char_p
@@ -143,6 +145,27 @@ def lh_accumulate_act_aware(X: torch.Tensor, Xq: torch.Tensor, H: Optional[torch
     _need(P, "P", shape, torch.float32)
     _check(lib().lh_accumulate_act_aware(_ptr(X), _ptr(Xq), _dtype_code(X), rows, cin, _ptr(offsets), G,
                                          float(beta), _ptr(H), _ptr(P), _stream(X.device)))
+    return H, P
+
+
+def lh_accumulate_act_aware_fq(X: torch.Tensor, x_amax: torch.Tensor, H: Optional[torch.Tensor] = None,
+                               P: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None,
+                               beta: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """As lh_accumulate_act_aware, with X_q the NVFP4 fake-quant of X made in the kernel from the
+    input quantizer's amax per group (x_amax [G] fp32)."""
+    _need(X, "X")
+    rows, cin = X.shape
+    offsets, G = _offsets(offsets, X)
+    _need(x_amax, "x_amax", (G,), torch.float32)
+    shape = (G, cin // 16, 16, 16)
+    if H is None:
+        H = torch.empty(shape, dtype=torch.float32, device=X.device)
+    if P is None:
+        P = torch.empty(shape, dtype=torch.float32, device=X.device)
+    _need(H, "H", shape, torch.float32)
+    _need(P, "P", shape, torch.float32)
+    _check(lib().lh_accumulate_act_aware_fq(_ptr(X), _dtype_code(X), rows, cin, _ptr(offsets), G, _ptr(x_amax),
+                                            float(beta), _ptr(H), _ptr(P), _stream(X.device)))
     return H, P
 
 

@@ -12,7 +12,8 @@
 namespace lh {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;       // scalar path
+constexpr int kVecThreads = 1024;   // vector path: 16 waves per workgroup
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __global__ void k_absmax_init(unsigned* out, int64_t n) {
@@ -28,7 +29,7 @@ __device__ inline unsigned wave_max(unsigned v) {
 // Vector path: each thread reads 16 bytes per step (8 bf16 or 4 fp32).  Requires the group's
 // base to be 16-byte aligned and elems to be a multiple of the vector width.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_absmax_vec(const v4u* __restrict__ W,
+__global__ __launch_bounds__(kVecThreads) void k_absmax_vec(const v4u* __restrict__ W,
                                                          int64_t vec_per_group, unsigned* out) {
   const int g = blockIdx.y;
   const v4u* base = W + (int64_t)g * vec_per_group;
@@ -41,8 +42,8 @@ __global__ __launch_bounds__(kThreads) void k_absmax_vec(const v4u* __restrict__
     return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
   };
   unsigned m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kVecThreads;
+  int64_t i = blockIdx.x * (int64_t)kVecThreads + threadIdx.x;
   for (; i + 3 * stride < vec_per_group; i += 4 * stride) {   // four loads in flight
     const v4u v0 = __builtin_nontemporal_load(base + i);
     const v4u v1 = __builtin_nontemporal_load(base + i + stride);
@@ -51,13 +52,13 @@ __global__ __launch_bounds__(kThreads) void k_absmax_vec(const v4u* __restrict__
     m = max(max(m, max(absmax16(v0), absmax16(v1))), max(absmax16(v2), absmax16(v3)));
   }
   for (; i < vec_per_group; i += stride) m = max(m, absmax16(__builtin_nontemporal_load(base + i)));
-  __shared__ unsigned red[kThreads / 64];
+  __shared__ unsigned red[kVecThreads / 64];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned r = red[0];
-    for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+    for (int w = 1; w < kVecThreads / 64; ++w) r = max(r, red[w]);
     if (r) atomicMax(out + g, r);
   }
 }
@@ -99,18 +100,19 @@ hipError_t launch_absmax(const void* W, bool bf16, int64_t n_groups, int64_t ele
   const int vec = bf16 ? 8 : 4;
   const bool aligned = (reinterpret_cast<uintptr_t>(W) % 16 == 0) && (elems % vec == 0);
   const int64_t units = aligned ? elems / vec : elems;
-  // about 8 units per thread; at most max(256, 16384 / n_groups) workgroups per group, so one
-  // large group still gets thousands of workgroups and many groups do not get millions
-  const int64_t cap = std::max<int64_t>(256, 16384 / n_groups);
-  int64_t bx = (units + (int64_t)kThreads * 8 - 1) / ((int64_t)kThreads * 8);
+  // about 8 units per thread, but at least ~1024 workgroups in all when the groups are few (and
+  // at least one unit per thread); at most 256 workgroups (and as many atomics) per group
+  const int64_t tpb = aligned ? kVecThreads : kThreads;
+  int64_t bx = std::max((units + tpb * 8 - 1) / (tpb * 8), (1024 + n_groups - 1) / n_groups);
+  bx = std::min(bx, (units + tpb - 1) / tpb);
   if (bx < 1) bx = 1;
-  if (bx > cap) bx = cap;
+  if (bx > 256) bx = 256;
   dim3 grid((unsigned)bx, (unsigned)n_groups);
   if (aligned) {
     if (bf16)
-      hipLaunchKernelGGL(k_absmax_vec<true>, grid, dim3(kThreads), 0, stream, (const v4u*)W, units, out);
+      hipLaunchKernelGGL(k_absmax_vec<true>, grid, dim3(kVecThreads), 0, stream, (const v4u*)W, units, out);
     else
-      hipLaunchKernelGGL(k_absmax_vec<false>, grid, dim3(kThreads), 0, stream, (const v4u*)W, units, out);
+      hipLaunchKernelGGL(k_absmax_vec<false>, grid, dim3(kVecThreads), 0, stream, (const v4u*)W, units, out);
   } else {
     if (bf16)
       hipLaunchKernelGGL(k_absmax_scalar<true>, grid, dim3(kThreads), 0, stream, W, elems, out);

@@ -19,8 +19,8 @@
 //    high part (truncation) and the exact bf16 remainder, so P = X_q^T D_hi + X_q^T D_lo needs two
 //    more MFMAs and no catastrophic cancellation.
 //  * Dense layer (one group): a workgroup of 16 waves owns a tile of R rows whose chunks the
-//    waves take in turn; the waves add their sums in LDS at the end.  With several tiles, each tile stores
-//    its sums and a second kernel adds them in tile order, one thread per output entry.
+//    waves take in turn; the waves add their sums in LDS at the end.  With several tiles, each
+//    tile stores its sums and the last tile of a slice to finish adds them all in tile order.
 //  * Grouped rows (MoE experts): a small planning kernel cuts every group into pieces of at most
 //    R rows (a group without rows is one empty piece); each wave owns one piece, so a group of at
 //    most R rows is finished by one wave with no synchronization.  Pieces of larger groups leave
@@ -32,12 +32,16 @@
 //  * When only the importance is wanted, partial sums keep just the 16 diagonal entries.
 #include "lh_internal.hpp"
 
+#include <type_traits>
+
 namespace lh {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 32;          // rows per chunk (one 16x16x32 MFMA per block)
@@ -78,10 +82,139 @@ __device__ inline void clear(unsigned* c) {
 __device__ inline float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
 __device__ inline float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
 
+// ---------------------------------------------------------------------------------------------
+// NVFP4 fake-quant of the activations, applied while a chunk streams in (the layer's input
+// quantizer).  Per group: gX = fp32(amax_X / (6*448)).  Per row and 16-channel block: v = the E4M3
+// value (0 or one of the 126 positive finite values) nearest to max|x| / (6 gX), ties to the even
+// code, so it saturates at 448 and flushes small blocks to 0; s = fp32(v gX); each element becomes
+// E2M1(x / s) * s (nearest grid value of |x|/s, ties to the even index, saturating at 6, sign of
+// x) computed in fp32 and stored in the input dtype (rounded to nearest-even bf16 for bf16 data).
+// ---------------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline unsigned dpp_u(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// E4M3 value nearest to y >= 0, ties to the even code, saturating at 448.  y = amax * (1/(6 gX))
+// carries at most 2^-52 relative error; the exact quotient of a bf16 or fp32 amax by 6 gX either
+// equals an E4M3 midpoint or lies more than 2^-31 of itself away from every midpoint, so a y
+// within 2^-40 of a midpoint is that midpoint and every other y is on the exact quotient's side.
+__device__ inline float e4m3_nearest(double y) {
+  if (!(y < 448.0)) return 448.0f;
+  if (y == 0.0) return 0.0f;
+  const int e = max(ilogb(y), -6);                // spacing 2^(e-3); 2^-9 below 2^-6
+  const double t = ldexp(y, 3 - e);               // exact, in [0, 16)
+  const double k = floor(t), f = t - k;
+  const double q = fabs(f - 0.5) <= 0x1p-40 * t ? k + (double)((int)k & 1) : rint(t);
+  return (float)fmin(ldexp(q, e - 3), 448.0);
+}
+
+__device__ inline float e2m1_value(int c) {
+  return c <= 4 ? 0.5f * (float)c : (c == 5 ? 3.0f : (c == 6 ? 4.0f : 6.0f));
+}
+// Exact E2M1 index of |x|/s between grid indices lo and lo + 1: the sign of m s - |x| (m their
+// midpoint, at most 3 significant bits) is exact in one fma; a tie goes to the even index.
+__device__ inline int e2m1_resolve(float ax, float s, int lo) {
+  const float m = lo < 4 ? 0.25f + 0.5f * (float)lo : (lo == 4 ? 2.5f : (lo == 5 ? 3.5f : 5.0f));
+  const float d = fmaf(m, s, -ax);
+  return d < 0.0f ? lo + 1 : (d > 0.0f ? lo : lo + (lo & 1));
+}
+// E2M1 index of r = |x|/s given as an exactly rounded float64 quotient (ties to the even index).
+__device__ inline int e2m1_index_f64(double r) {
+  return (int)(r > 0.25) + (int)(r >= 0.75) + (int)(r > 1.25) + (int)(r >= 1.75) +
+         (int)(r > 2.5) + (int)(r >= 3.5) + (int)(r > 5.0);
+}
+
+// Fake-quantizes the 16 bytes a lane holds of one row: 8 bf16 (half a block; the other half is in
+// lane ^ 1) or 4 fp32 (a quarter; the block is the lane's quad).  gx = gX, inv6g = 1/(6 gX) in
+// float64, fast = gX in [2^-100, 2^100] (all scales and quotients normal).
+template <bool BF16>
+__device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool fast) {
+  constexpr int n = BF16 ? 8 : 4;
+  float xf[n];
+  unsigned am = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if (BF16) {
+      xf[2 * p] = __uint_as_float(x[p] << 16);
+      xf[2 * p + 1] = __uint_as_float(x[p] & 0xFFFF0000u);
+      const unsigned a = x[p] & 0x7FFF7FFFu;
+      am = max(am, max(a << 16, a & 0xFFFF0000u));
+    } else {
+      xf[p] = __uint_as_float(x[p]);
+      am = max(am, x[p] & 0x7FFFFFFFu);
+    }
+  }
+  am = max(am, dpp_u<0xB1>(am));                  // quad_perm [1,0,3,2]: the lane pair
+  if (!BF16) am = max(am, dpp_u<0x4E>(am));       // quad_perm [2,3,0,1]: the whole quad
+  const float v = gx > 0.0f ? e4m3_nearest((double)__uint_as_float(am) * inv6g) : 0.0f;
+  const float s = v * gx;                         // fp32(v gX): one rounding of an exact product
+  float q[n];
+  if (fast) {
+    // Nearest grid values of x * (1/s) pushed up and down by 2^-19 bracket the exact quotient
+    // (the quotient through the 1-ulp hardware reciprocal is within 2^-21 of it) and agree unless
+    // it is within about 2^-18 of a midpoint; those elements take the exact decision.  s = 0
+    // (a block that rounds to 0) uses 1/s = 0, so every element becomes 0.
+    const float is = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+    const float iu = is * 1.0000019073486328125f, id = is * 0.9999980926513671875f;
+    unsigned up = 0u, dn = 0u;
+    auto pack = [&](auto sel) {                   // the convert's byte select is an immediate
+      constexpr int p = decltype(sel)::value;
+      up = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(up, xf[2 * p] * iu, xf[2 * p + 1] * iu, 1.0f, p);
+      dn = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dn, xf[2 * p] * id, xf[2 * p + 1] * id, 1.0f, p);
+    };
+    pack(std::integral_constant<int, 0>{});
+    pack(std::integral_constant<int, 1>{});
+    if constexpr (n == 8) {
+      pack(std::integral_constant<int, 2>{});
+      pack(std::integral_constant<int, 3>{});
+    }
+    if (up != dn) {
+#pragma unroll
+      for (int k = 0; k < n; ++k) {
+        const int cu = (up >> (4 * k)) & 7, cd = (dn >> (4 * k)) & 7;
+        if (cu != cd)
+          up = (up & ~(7u << (4 * k))) | ((unsigned)e2m1_resolve(fabsf(xf[k]), s, cd) << (4 * k));
+      }
+    }
+    auto unpack = [&](auto sel) {
+      constexpr int p = decltype(sel)::value;
+      const v2f g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(up, 1.0f, p);   // signed grid values
+      q[2 * p] = g[0] * s;
+      q[2 * p + 1] = g[1] * s;
+    };
+    unpack(std::integral_constant<int, 0>{});
+    unpack(std::integral_constant<int, 1>{});
+    if constexpr (n == 8) {
+      unpack(std::integral_constant<int, 2>{});
+      unpack(std::integral_constant<int, 3>{});
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < n; ++k) {
+      const int c = s == 0.0f ? 0 : e2m1_index_f64((double)fabsf(xf[k]) / (double)s);
+      q[k] = copysignf(e2m1_value(c) * s, xf[k]);
+    }
+  }
+  v4u out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if (BF16) {
+      const v2bf b = __builtin_convertvector((v2f){q[2 * p], q[2 * p + 1]}, v2bf);   // nearest-even
+      out[p] = __builtin_bit_cast(unsigned, b);
+    } else {
+      out[p] = __float_as_uint(q[p]);
+    }
+  }
+  return out;
+}
+
 // One wave's streaming contraction of rows [r0, r1) of a 64-channel slice into four blocks of
 // accumulators, using the wave's own LDS stage.  Chunks are taken with a stride of `step` chunks
-// starting at chunk `first` (counted from r0), so several waves can share a range.
-template <bool BF16, bool ACT>
+// starting at chunk `first` (counted from r0), so several waves can share a range.  With FQ the
+// activation-aware X_q is not read: it is made from X in registers (act_fake_quant) while the
+// next chunk's loads are in flight.
+template <bool BF16, bool ACT, bool FQ = false>
 struct Streamer {
   using Gm = Geo<BF16>;
   static constexpr int kM = ACT ? 2 : 1;
@@ -91,6 +224,15 @@ struct Streamer {
   int nblk, lane, i, gg;
   unsigned* stage;              // [kM][kWords] of this wave
   v4f accH[4], accP[4];
+  float gx = 0.0f;              // FQ: the group's gX, 1/(6 gX) in float64, gX in the fast range
+  double inv6g = 0.0;
+  bool fq_fast = false;
+
+  __device__ void set_fake_quant(float x_amax) {
+    gx = x_amax / 2688.0f;                       // fp32(amax / (6*448)), correctly rounded
+    inv6g = 1.0 / (6.0 * (double)gx);
+    fq_fast = gx >= 0x1p-100f && gx <= 0x1p100f;
+  }
 
   __device__ void run(int64_t r0, int64_t r1, int first, int step) {
 #pragma unroll
@@ -110,7 +252,7 @@ struct Streamer {
         const int64_t r = min(r0 + (int64_t)j * kChunk + lrow + q * Gm::kRowsPerLoad, r1 - 1);
         const int64_t byte = (r * cin + (col_on ? ch0 + lcol : 0)) * esz;
 #pragma unroll
-        for (int m = 0; m < kM; ++m) {
+        for (int m = FQ ? 1 : 0; m < kM; ++m) {
           const char* base = (m == 0) ? (ACT ? Xq : X) : X;    // act-aware: matrix 0 = X_q, 1 = X
           pre[m][q] = __builtin_nontemporal_load((const v4u*)(base + byte));
         }
@@ -120,6 +262,30 @@ struct Streamer {
     if (j < nchunks) issue(j);
     for (; j < nchunks; j += step) {
       const int64_t c0 = r0 + (int64_t)j * kChunk;
+      if constexpr (FQ) {
+        // X goes to its stage first and the next chunk's loads are issued; each lane then reads
+        // back its own 16 bytes to make X_q (an X of zeros stays zero)
+#pragma unroll
+        for (int q = 0; q < Gm::kLoads; ++q) {
+          const int row = lrow + q * Gm::kRowsPerLoad;
+          const bool on = col_on && c0 + row < r1;
+          const int word = BF16 ? (row * kPitchH + lcol) / 2 : row * kPitchF + lcol;
+          *(v4u*)&stage[Gm::kWords + word] = on ? pre[1][q] : v4u{0u, 0u, 0u, 0u};
+        }
+        if (j + step < nchunks) issue(j + step);
+#pragma unroll
+        for (int q = 0; q < Gm::kLoads; ++q) {
+          const int row = lrow + q * Gm::kRowsPerLoad;
+          const int word = BF16 ? (row * kPitchH + lcol) / 2 : row * kPitchF + lcol;
+          const v4u xv = *(const v4u*)&stage[Gm::kWords + word];
+          *(v4u*)&stage[word] = act_fake_quant<BF16>(xv, gx, inv6g, fq_fast);   // every lane: uses its pair/quad
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        contract();
+        continue;
+      }
 #pragma unroll
       for (int q = 0; q < Gm::kLoads; ++q) {
         const int row = lrow + q * Gm::kRowsPerLoad;
@@ -294,17 +460,18 @@ __device__ inline v4f sum_partials(const float* w0, int64_t stride, int64_t n, i
 template <bool BF16>
 constexpr int dense_waves() { return BF16 ? 16 : 4; }
 
-template <bool BF16, bool ACT, bool DIAG, int NW>
+template <bool BF16, bool ACT, bool DIAG, int NW, bool FQ>
 __global__ __launch_bounds__(NW * 64) void k_acc_dense(
-    const void* __restrict__ Xv, const void* __restrict__ Xqv, int64_t rows, int64_t cin,
-    int64_t R, float beta, float* __restrict__ H, float* __restrict__ P, float* __restrict__ imp,
-    float* __restrict__ ws, int64_t nb) {
-  using St = Streamer<BF16, ACT>;
+    const void* __restrict__ Xv, const void* __restrict__ Xqv, const float* __restrict__ x_amax,
+    int64_t rows, int64_t cin, int64_t R, float beta, float* __restrict__ H, float* __restrict__ P,
+    float* __restrict__ imp, float* __restrict__ ws, unsigned* __restrict__ counters, int64_t nb) {
+  using St = Streamer<BF16, ACT, FQ>;
   constexpr int kM = St::kM;
   constexpr int kPart = DIAG ? 16 : 256;
   constexpr int kStage = NW * kM * Geo<BF16>::kWords;
   constexpr int kComb = NW * 4 * 64 * 4;      // [wave][block][lane] v4f, in words
   __shared__ __attribute__((aligned(16))) unsigned smem[kStage > kComb ? kStage : kComb];
+  __shared__ int last_tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, gg = lane >> 4;
   const int64_t tiles = gridDim.x, tile = blockIdx.x, slice = blockIdx.y;
@@ -314,6 +481,7 @@ __global__ __launch_bounds__(NW * 64) void k_acc_dense(
 
   St st{(const char*)Xv, (const char*)Xqv, cin, slice * kCh, nblk, lane, i, gg,
         smem + wave * kM * Geo<BF16>::kWords, {}, {}};
+  if (FQ) st.set_fake_quant(x_amax[0]);
   st.run(t0, t1, wave, NW);
 
   const bool mine = wave < nblk;              // waves 0..3 own the slice's four blocks
@@ -339,62 +507,26 @@ __global__ __launch_bounds__(NW * 64) void k_acc_dense(
       for (int m = 0; m < kM; ++m) emit_block<DIAG>(m, tot[m], rows, blk, beta, H, P, imp_blk, i, gg);
     return;
   }
-  // several tiles: plain stores of this tile's sums; k_acc_dense_sum adds them after this kernel
+  // several tiles: each stores its sums; the slice's last tile to finish adds all of them in
+  // tile order and writes the outputs
+  float* part = ws + slice * tiles * kM * 4 * kPart;          // [tile][m][block][kPart]
   if (mine) {
 #pragma unroll
-    for (int m = 0; m < kM; ++m) {
-      float* w = ws + (((slice * tiles + tile) * kM + m) * 4 + wave) * kPart;
+    for (int m = 0; m < kM; ++m)
+      store_partial<DIAG>(part + ((tile * kM + m) * 4 + wave) * kPart, tot[m], lane, i, gg);
+  }
+  __builtin_amdgcn_s_waitcnt(0);              // this wave's partial stores have completed
+  __syncthreads();                            // ... and every other wave's
+  if (tid == 0) last_tile = arrive(&counters[slice]) == (unsigned)(tiles - 1);
+  __syncthreads();
+  if (!last_tile) return;
+  if (mine) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (DIAG) {
-          if (4 * gg + r == i) w[i] = tot[m][r];
-        } else {
-          w[4 * lane + r] = tot[m][r];
-        }
-      }
-    }
+    for (int m = 0; m < kM; ++m)
+      emit_block<DIAG>(m, sum_partials<DIAG>(part + (m * 4 + wave) * kPart, kM * 4 * kPart, tiles, lane, i, gg),
+                       rows, blk, beta, H, P, imp_blk, i, gg);
   }
-}
-
-// Dense layer with several tiles: one thread per output entry adds the tiles' sums in tile order
-// (eight loads in flight) and writes H, P (sum / rows, beta) and the importance.
-template <bool ACT, bool DIAG>
-__global__ __launch_bounds__(kThreads) void k_acc_dense_sum(
-    const float* __restrict__ ws, int64_t tiles, int64_t slices, int64_t nb, int64_t rows,
-    float beta, float* __restrict__ H, float* __restrict__ P, float* __restrict__ imp) {
-  constexpr int kM = ACT ? 2 : 1;
-  constexpr int kPart = DIAG ? 16 : 256;
-  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // over [slice][m][block][kPart]
-  if (e >= slices * kM * 4 * kPart) return;
-  const int64_t q = e % kPart, b = (e / kPart) % 4, m = (e / (4 * kPart)) % kM, slice = e / (kM * 4 * kPart);
-  const int64_t n = slice * 4 + b;
-  if (n >= nb) return;
-  const float* w0 = ws + ((slice * tiles * kM + m) * 4 + b) * kPart + q;
-  const int64_t stride = (int64_t)kM * 4 * kPart;
-  float s = 0.0f;
-  int64_t t = 0;
-  for (; t + 8 <= tiles; t += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = w0[(t + u) * stride];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
-  }
-  for (; t < tiles; ++t) s += w0[t * stride];
-  if (DIAG) {
-    float* o = imp + n * 16 + q;
-    *o = beta != 0.0f ? beta * *o + s : s;
-    return;
-  }
-  // entry q of the lane-major layout: lane l = q / 4 holds row 4 * (l / 16) + q % 4, column l % 16
-  const int64_t l = q / 4, row = 4 * (l / 16) + q % 4, col = l % 16;
-  if (m == 0 && imp && row == col) {
-    float* o = imp + n * 16 + col;
-    *o = beta != 0.0f ? beta * *o + s : s;
-  }
-  float* o = (m == 0 ? H : P) + n * 256 + row * 16 + col;
-  const float v = rows > 0 ? s / (float)rows : 0.0f;
-  *o = beta != 0.0f ? beta * *o + v : v;
+  if (tid == 0) clear(&counters[slice]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -463,13 +595,13 @@ __global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict
 // Grouped rows: a 1-D grid of ceil(capacity / 4) x slices workgroups, slice fastest (the slices of
 // the same rows run together); wave w of workgroup x owns the piece in schedule slot 4x + w.
 // Partial layout: [piece][slice][m][block][kPart]; counters: [group][slice].
-template <bool BF16, bool ACT, bool DIAG>
+template <bool BF16, bool ACT, bool DIAG, bool FQ>
 __global__ __launch_bounds__(kThreads) void k_acc_pieces(
-    const void* __restrict__ Xv, const void* __restrict__ Xqv, int64_t cin,
-    const int64_t* __restrict__ table, int64_t cap, float beta, float* __restrict__ H,
+    const void* __restrict__ Xv, const void* __restrict__ Xqv, const float* __restrict__ x_amax,
+    int64_t cin, const int64_t* __restrict__ table, int64_t cap, float beta, float* __restrict__ H,
     float* __restrict__ P, float* __restrict__ imp, float* __restrict__ ws,
     unsigned* __restrict__ counters, int64_t nb) {
-  using St = Streamer<BF16, ACT>;
+  using St = Streamer<BF16, ACT, FQ>;
   constexpr int kM = St::kM;
   constexpr int kPart = DIAG ? 16 : 256;
   __shared__ __attribute__((aligned(16))) unsigned smem[4 * kM * Geo<BF16>::kWords];
@@ -487,6 +619,7 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
 
   St st{(const char*)Xv, (const char*)Xqv, cin, slice * kCh, nblk, lane, i, gg,
         smem + wave * kM * Geo<BF16>::kWords, {}, {}};
+  if (FQ) st.set_fake_quant(x_amax[g]);
   st.run(r0, r1, 0, 1);
 
   const int64_t gbeg = table[kEntry + (p - k) * kEntry + 1];
@@ -551,24 +684,18 @@ int64_t piece_rows(int64_t rows, int64_t nb) {
 
 bool is_dense(const int64_t* offsets, int64_t n_groups) { return !offsets || n_groups == 1; }
 
-template <bool BF16, bool ACT, bool DIAG>
+template <bool BF16, bool ACT, bool DIAG, bool FQ = false>
 hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off, int64_t G,
-                       const void* X, const void* Xq, float beta, float* H, float* P, float* imp,
-                       void* work, unsigned* counters, hipStream_t stream) {
+                       const void* X, const void* Xq, const float* x_amax, float beta, float* H,
+                       float* P, float* imp, void* work, unsigned* counters, hipStream_t stream) {
   const int64_t nb = cin / 16, slices = (nb + 3) / 4;
   if (dense) {
     constexpr int NW = dense_waves<BF16>();
     const int64_t R = dense_tile_rows(rows, nb, BF16, DIAG);
     const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
-    hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG, NW>), dim3((unsigned)tiles, (unsigned)slices),
-                       dim3(NW * 64), 0, stream, X, Xq, rows, cin, R, beta, H, P, imp,
-                       (float*)work, nb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || tiles == 1) return e;
-    const int64_t outs = slices * (ACT ? 2 : 1) * 4 * (DIAG ? 16 : 256);
-    hipLaunchKernelGGL((k_acc_dense_sum<ACT, DIAG>), dim3((unsigned)((outs + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, (const float*)work, tiles, slices, nb, rows, beta,
-                       H, P, imp);
+    hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG, NW, FQ>), dim3((unsigned)tiles, (unsigned)slices),
+                       dim3(NW * 64), 0, stream, X, Xq, x_amax, rows, cin, R, beta, H, P, imp,
+                       (float*)work, counters, nb);
     return hipGetLastError();
   }
   const int64_t R = piece_rows(rows, nb);
@@ -578,12 +705,25 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
   hipLaunchKernelGGL(k_acc_plan, dim3(1), dim3(kThreads), 0, stream, off, G, rows, R, cap, table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG>), dim3((unsigned)(((cap + 3) / 4) * slices)),
-                     dim3(kThreads), 0, stream, X, Xq, cin, table, cap, beta, H, P, imp, ws, counters, nb);
+  hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG, FQ>), dim3((unsigned)(((cap + 3) / 4) * slices)),
+                     dim3(kThreads), 0, stream, X, Xq, x_amax, cin, table, cap, beta, H, P, imp, ws,
+                     counters, nb);
   return hipGetLastError();
 }
 
 }  // namespace
+
+__global__ void k_zero_fill(unsigned* p, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_fill(unsigned* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     p, (int64_t)n);
+  return hipGetLastError();
+}
 
 AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, int64_t n_groups,
                               bool bf16, bool act_aware, bool imp_only) {
@@ -604,23 +744,24 @@ AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, 
   return s;
 }
 
-hipError_t launch_accumulate(const void* X, const void* Xq, bool bf16, int64_t rows, int64_t cin,
-                             const int64_t* offsets, int64_t n_groups, float beta, float* H,
-                             float* P, float* imp, void* work, size_t work_bytes,
-                             unsigned* counters, size_t n_counters, hipStream_t stream) {
-  const bool act = Xq != nullptr;
+hipError_t launch_accumulate(const void* X, const void* Xq, const float* x_amax, bool bf16,
+                             int64_t rows, int64_t cin, const int64_t* offsets, int64_t n_groups,
+                             float beta, float* H, float* P, float* imp, void* work,
+                             size_t work_bytes, unsigned* counters, size_t n_counters,
+                             hipStream_t stream) {
+  const bool fq = x_amax != nullptr;
+  const bool act = Xq != nullptr || fq;
   const bool diag = !act && H == nullptr;
   const bool dense = is_dense(offsets, n_groups);
   const AccScratch need = accumulate_scratch(rows, cin / 16, offsets, n_groups, bf16, act, diag);
   if (work_bytes < need.work_bytes || n_counters < need.counters) return hipErrorInvalidValue;
-  if (act)
-    return bf16 ? launch_kind<true, true, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream)
-                : launch_kind<false, true, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream);
-  if (diag)
-    return bf16 ? launch_kind<true, false, true>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream)
-                : launch_kind<false, false, true>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream);
-  return bf16 ? launch_kind<true, false, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream)
-              : launch_kind<false, false, false>(dense, rows, cin, offsets, n_groups, X, Xq, beta, H, P, imp, work, counters, stream);
+#define LH_ACC_KIND(B, A, D, F) \
+  launch_kind<B, A, D, F>(dense, rows, cin, offsets, n_groups, X, Xq, x_amax, beta, H, P, imp, work, counters, stream)
+  if (fq) return bf16 ? LH_ACC_KIND(true, true, false, true) : LH_ACC_KIND(false, true, false, true);
+  if (act) return bf16 ? LH_ACC_KIND(true, true, false, false) : LH_ACC_KIND(false, true, false, false);
+  if (diag) return bf16 ? LH_ACC_KIND(true, false, true, false) : LH_ACC_KIND(false, false, true, false);
+  return bf16 ? LH_ACC_KIND(true, false, false, false) : LH_ACC_KIND(false, false, false, false);
+#undef LH_ACC_KIND
 }
 
 }  // namespace lh

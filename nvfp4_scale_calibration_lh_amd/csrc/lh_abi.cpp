@@ -183,14 +183,14 @@ hipError_t grow(void** buf, size_t* have, size_t need, size_t elem, hipMemPool_t
   hipError_t e = hipMallocFromPoolAsync(buf, need * elem, pool, s);
   if (e != hipSuccess) return e;
   *have = need;
-  return zero ? hipMemsetAsync(*buf, 0, need * elem, s) : hipSuccess;
+  return zero ? lh::launch_zero_fill(static_cast<unsigned*>(*buf), need * elem / sizeof(unsigned), s) : hipSuccess;
 }
 
-lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t rows, int64_t cin,
-                         const int64_t* offsets, int64_t n_groups, float beta, float* H, float* P,
-                         float* imp, void* stream) {
+lh_status run_accumulate(const void* X, const void* Xq, const float* x_amax, lh_dtype dt, int64_t rows,
+                         int64_t cin, const int64_t* offsets, int64_t n_groups, float beta, float* H,
+                         float* P, float* imp, void* stream) {
   int dev = -1;
-  lh_status st = check_pointers({{X, "X"}, {Xq, "Xq"}, {offsets, "group_offsets"}, {H, "H"}, {P, "P"}, {imp, "imp"}}, &dev);
+  lh_status st = check_pointers({{X, "X"}, {Xq, "Xq"}, {x_amax, "x_amax"}, {offsets, "group_offsets"}, {H, "H"}, {P, "P"}, {imp, "imp"}}, &dev);
   if (st != LH_OK) return st;
   if ((st = check_aligned(X, "X")) != LH_OK) return st;
   if ((st = check_aligned(Xq, "Xq")) != LH_OK) return st;
@@ -198,7 +198,7 @@ lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t row
   if ((st = guard.enter(dev)) != LH_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t nb = cin / 16;
-  const bool act = Xq != nullptr;
+  const bool act = Xq != nullptr || x_amax != nullptr;
   const lh::AccScratch need = lh::accumulate_scratch(rows, nb, offsets, n_groups, dt == LH_DTYPE_BF16, act,
                                                     !act && H == nullptr);
   hipMemPool_t pool;
@@ -221,7 +221,7 @@ lh_status run_accumulate(const void* X, const void* Xq, lh_dtype dt, int64_t row
     (void)hipEventRecord(sc.ready, s);
     return hip_fail(e, "accumulation scratch");
   }
-  e = lh::launch_accumulate(X, Xq, dt == LH_DTYPE_BF16, rows, cin, offsets, n_groups, beta, H, P, imp,
+  e = lh::launch_accumulate(X, Xq, x_amax, dt == LH_DTYPE_BF16, rows, cin, offsets, n_groups, beta, H, P, imp,
                             sc.work, sc.work_bytes, sc.counters, sc.n_counters, s);
   hipError_t e2 = hipEventRecord(sc.ready, s);
   if (e != hipSuccess) return hip_fail(e, "accumulate launch");
@@ -249,7 +249,7 @@ lh_status lh_accumulate(const void* X, lh_dtype x_dtype, int64_t rows, int64_t c
   if (st != LH_OK) return st;
   if (!H && !imp) return fail(LH_ERR_INVALID_ARGUMENT, "at least one of H, imp must be given");
   if (!X && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X is NULL");
-  return run_accumulate(X, nullptr, x_dtype, rows, cin, group_offsets, n_groups, beta, H, nullptr, imp, stream);
+  return run_accumulate(X, nullptr, nullptr, x_dtype, rows, cin, group_offsets, n_groups, beta, H, nullptr, imp, stream);
 }
 
 lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype, int64_t rows,
@@ -262,9 +262,23 @@ lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype,
   if ((!X || !Xq) && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X and Xq are required");
   if (rows == 0) {
     // nothing to read: only the beta term remains; run the generic path with an alias for Xq
-    return run_accumulate(X ? X : H, Xq ? Xq : H, dtype, 0, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
+    return run_accumulate(X ? X : H, Xq ? Xq : H, nullptr, dtype, 0, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
   }
-  return run_accumulate(X, Xq, dtype, rows, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
+  return run_accumulate(X, Xq, nullptr, dtype, rows, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
+}
+
+lh_status lh_accumulate_act_aware_fq(const void* X, lh_dtype dtype, int64_t rows, int64_t cin,
+                                     const int64_t* group_offsets, int64_t n_groups,
+                                     const float* x_amax, float beta, float* H, float* P,
+                                     void* stream) {
+  if (!dtype_ok(dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  lh_status st = check_shapes_x(rows, cin, group_offsets, n_groups);
+  if (st != LH_OK) return st;
+  if (!H || !P) return fail(LH_ERR_INVALID_ARGUMENT, "H and P are both required");
+  if (!x_amax) return fail(LH_ERR_INVALID_ARGUMENT, "x_amax is required");
+  if (!X && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X is NULL");
+  // with no rows nothing is read: only the beta term remains (X may then be NULL)
+  return run_accumulate(X ? X : H, nullptr, x_amax, dtype, rows, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
 }
 
 lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,

@@ -17,14 +17,19 @@ struct AccScratch {
 AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, int64_t n_groups,
                               bool bf16, bool act_aware, bool imp_only);
 
+// Sets n words at p to zero (a kernel, so that graph capture records no memset node).
+hipError_t launch_zero_fill(unsigned* p, size_t n, hipStream_t stream);
+
 hipError_t launch_absmax(const void* W, bool bf16, int64_t n_groups, int64_t elems, float* amax,
                          hipStream_t stream);
 
-// act_aware: X and Xq given; H and P required.  Otherwise Xq == nullptr and H and/or imp given.
-hipError_t launch_accumulate(const void* X, const void* Xq, bool bf16, int64_t rows, int64_t cin,
-                             const int64_t* offsets, int64_t n_groups, float beta, float* H,
-                             float* P, float* imp, void* work, size_t work_bytes,
-                             unsigned* counters, size_t n_counters, hipStream_t stream);
+// Activation-aware: X and Xq given, or X and x_amax (X_q made from X in the kernel, Xq ==
+// nullptr); H and P required.  Otherwise Xq == x_amax == nullptr and H and/or imp given.
+hipError_t launch_accumulate(const void* X, const void* Xq, const float* x_amax, bool bf16,
+                             int64_t rows, int64_t cin, const int64_t* offsets, int64_t n_groups,
+                             float beta, float* H, float* P, float* imp, void* work,
+                             size_t work_bytes, unsigned* counters, size_t n_counters,
+                             hipStream_t stream);
 
 hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout, int64_t cin,
                         const float* amax, const float* H, const float* P, uint8_t* code,

@@ -14,9 +14,11 @@ from .lh_oracle import (  # noqa: F401
     candidate_losses,
     accumulate,
     accumulate_act_aware,
+    activation_fake_quant,
     candidate_scales,
     e2m1_index,
     e4m3_ladder,
+    e4m3_nearest,
     exempt_mask,
     fake_quant,
     global_scale,

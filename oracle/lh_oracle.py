@@ -12,6 +12,8 @@ What it computes, in the order and notation of the pages:
   accumulated as x.square().sum(-1) into an [n_blocks, block_size] buffer).
 * ``accumulate_act_aware``: ``H = X_q^T X_q / B`` and ``P = X_q^T (X_q - X) / B`` per block.
   Page: "Add activation-aware local Hessian scale calibration" (PR #1976), What does this PR do?
+* ``activation_fake_quant``: the X_q those use when the layer's NVFP4 input quantizer is applied
+  to X (per-token 16-channel E4M3 block scales under the 448-normalized global scale).
 * ``sweep``: for every 16-element weight block try each of the 126 positive finite E4M3 block
   scales, fake-quantize to E2M1, score ``dw^T H_n dw + 2 dw^T (P_n w0)`` with ``dw = quant(w) - w``
   and keep the argmin, starting from best = +inf.  Pages: PR #1976 review assessment (sign of dw,
@@ -187,6 +189,62 @@ def accumulate_act_aware(X, Xq, offsets, beta: float = 0.0, H_prev=None, P_prev=
         H = beta * np.asarray(H_prev, dtype=np.float64) + H
         P = beta * np.asarray(P_prev, dtype=np.float64) + P
     return H, P
+
+
+def e4m3_nearest(y) -> np.ndarray:
+    """The E4M3 value (0 or one of the 126 positive finite values) nearest to y >= 0, ties to the
+    even code; values above 448 are nearest to 448 (saturation).  Brute force over all 127.
+
+    y is a float64 quotient of a bf16/fp32 amax by 6 gX (at most 26 significant bits): it lies on
+    the exact quotient's side of every E4M3 midpoint (at most 5 bits) and equals one only when the
+    exact quotient does, and its distances to the two nearest values are exact (Sterbenz)."""
+    y = np.asarray(y, dtype=np.float64)
+    values = np.concatenate([[0.0], e4m3_ladder()])                 # index = E4M3 code 0..126
+    d = np.abs(y[..., None] - values)
+    is_min = d == d.min(axis=-1, keepdims=True)
+    even_min = is_min & (np.arange(127) % 2 == 0)
+    code = np.where(even_min.any(axis=-1), np.argmax(even_min, axis=-1), np.argmax(is_min, axis=-1))
+    return values[code]
+
+
+def _bf16_round(x32) -> np.ndarray:
+    """Nearest-even bf16 of float32 values, returned as float64 (torch's conversion)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+
+
+def activation_fake_quant(X, x_amax, offsets, bf16: bool, rows_per_chunk: int = 256) -> np.ndarray:
+    """X_q: the NVFP4 fake-quant the layer's input quantizer applies to its activations, which the
+    activation-aware Hessian is built from ("Add activation-aware local Hessian scale
+    calibration", What does this PR do?), with the 448-normalized NVFP4 scaling ("Add composable
+    scale calibration to GPTQ", What does this PR do?) applied per token.
+
+    Group g has the global scale gX = fp32(x_amax[g] / (6*448)).  Each row's 16-channel block gets
+    the block scale v = the E4M3 value nearest to max|x| / (6 gX) (ties to the even code, so 448 at
+    most and 0 for a block whose max rounds to 0), s = fp32(v gX); each element becomes
+    sign(x) * E2M1(|x|/s) * s, the product rounded to fp32 and then, for bf16 activations, to bf16.
+    x_amax = 0 gives X_q = 0."""
+    X = np.asarray(X, dtype=np.float64)
+    x_amax = np.asarray(x_amax, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows, cin = X.shape
+    nb = cin // BLOCK
+    out = np.zeros_like(X)
+    for g in range(len(offsets) - 1):
+        gx = float(global_scale(x_amax[g]))
+        r0, r1 = _group_rows(offsets, g)
+        if gx == 0.0:
+            continue
+        for a in range(r0, r1, rows_per_chunk):
+            b = min(r1, a + rows_per_chunk)
+            xb = X[a:b].reshape(b - a, nb, BLOCK)
+            v = e4m3_nearest(np.abs(xb).max(axis=-1) / (6.0 * gx))
+            s = (v * gx).astype(np.float32).astype(np.float64)       # v gX is exact in float64
+            _, wq, _ = fake_quant(xb, s[..., None])                  # sign(x) E2M1(|x|/s) s, exact
+            q32 = wq.astype(np.float32)                              # the product in fp32
+            out[a:b] = (_bf16_round(q32) if bf16 else q32.astype(np.float64)).reshape(b - a, cin)
+    return out
 
 
 # ----------------------------------------------------------------------------- sweep

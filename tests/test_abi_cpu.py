@@ -59,6 +59,12 @@ def test_validation_errors_without_device():
     assert L.lh_accumulate(None, 1, 10, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     # act-aware needs both outputs
     assert L.lh_accumulate_act_aware(FAKE, FAKE, 1, 10, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    # act-aware with X_q made in the kernel: x_amax, H and P required
+    c, m = _err(L.lh_accumulate_act_aware_fq(FAKE, 1, 10, 32, None, 1, None, 0.0, FAKE, FAKE, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "x_amax" in m
+    assert L.lh_accumulate_act_aware_fq(FAKE, 1, 10, 32, None, 1, FAKE, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_accumulate_act_aware_fq(FAKE, 1, 10, 40, None, 1, FAKE, 0.0, FAKE, FAKE, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_accumulate_act_aware_fq(FAKE, 5, 10, 32, None, 1, FAKE, 0.0, FAKE, FAKE, None) == lh.LH_ERR_UNSUPPORTED
     # sweep
     assert L.lh_scale_sweep(FAKE, 1, 0, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_scale_sweep(FAKE, 1, 1, 4, 33, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT

@@ -158,3 +158,18 @@ def test_fullsize_codes_and_nibbles_consistent(run):
             ref = oracle.pack_nibbles(nib)
             bad = (fp4[r0:r1] != ref).any(-1)
             assert not bad.any(), f"group {g}: {bad.sum()} blocks whose FP4 bytes are not the encoding at their scale"
+
+
+def test_fullsize_fused_fake_quant_matches_two_input_path():
+    """Activation-aware up_proj 12288x4096 (X [8192,4096] bf16): H and P with X_q made in the
+    kernel equal, value for value, those of the two-input kernel fed the generator's X_q (the
+    same quantizer recipe, pinned against the oracle's), so every X_q element is bit-exact."""
+    wl = synth.make("c3")
+    note("full-size c3: fused fake-quant accumulation against the two-input path")
+    X = to_dev(wl.X, "bf16")
+    Xq = to_dev(wl.Xq, "bf16")
+    amax = torch.tensor([float(np.abs(wl.X_f64()).max())], dtype=torch.float32, device=DEV)
+    H1, P1 = lh.lh_accumulate_act_aware(X, Xq)
+    H2, P2 = lh.lh_accumulate_act_aware_fq(X, amax)
+    torch.cuda.synchronize()
+    assert torch.equal(H1, H2) and torch.equal(P1, P2)

@@ -138,6 +138,46 @@ def test_accumulate_act_aware(name):
     assert_p_close(P.cpu().numpy(), P_ref, H_ref, R_ref)
 
 
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c5"])
+def test_accumulate_act_aware_fused_fake_quant(name):
+    """X_q made in the kernel from X and the input quantizer's amax: H and P against the oracle
+    (its own activation fake-quant), and identical to the two-input kernel fed the oracle's X_q
+    (same summation order), which holds only if every X_q element matches bit for bit."""
+    wl = synth.make(name, **SMALL[name])
+    G, bf16 = wl.n_groups, wl.dtype == "bf16"
+    X64 = wl.X_f64()
+    amax = np.array([np.abs(X64[wl.offsets[g]:wl.offsets[g + 1]]).max(initial=0.0) for g in range(G)])
+    if G > 2:
+        amax[1] *= 0.25                     # blocks of this group saturate at 448
+        amax[2] = 0.0                       # X_q = 0 for this group
+    amax = amax.astype(np.float32)
+    note(f"fused fake-quant accumulate {name} X{wl.X.shape} G={G} dtype={wl.dtype}")
+    _, X, _, off = upload(wl)
+    H, P = lh.lh_accumulate_act_aware_fq(X, torch.from_numpy(amax).to(DEV), offsets=off)
+    Xq64 = oracle.activation_fake_quant(X64, amax.astype(np.float64), wl.offsets, bf16=bf16)
+    H_ref, P_ref = oracle.accumulate_act_aware(X64, Xq64, wl.offsets)
+    R_ref = cross_gram(X64, Xq64, wl.offsets)
+    assert_h_close(H.cpu().numpy(), H_ref)
+    assert_p_close(P.cpu().numpy(), P_ref, H_ref, R_ref)
+    Xq_store = synth.bf16_bits_from_f32(Xq64.astype(np.float32)) if bf16 else Xq64.astype(np.float32)
+    H2, P2 = lh.lh_accumulate_act_aware(X, to_dev(Xq_store, wl.dtype), offsets=off)
+    assert torch.equal(H, H2) and torch.equal(P, P2)
+
+
+def test_accumulate_fused_fake_quant_beta_and_zero_rows():
+    wl = synth.make("c3", **SMALL["c3"])
+    _, X, _, _ = upload(wl)
+    amax = torch.tensor([float(np.abs(wl.X_f64()).max())], dtype=torch.float32, device=DEV)
+    note("fused fake-quant accumulate: beta and zero rows")
+    H, P = lh.lh_accumulate_act_aware_fq(X, amax)
+    H0, P0 = H.clone(), P.clone()
+    H, P = lh.lh_accumulate_act_aware_fq(X, amax, H=H, P=P, beta=1.0)
+    torch.testing.assert_close(H, 2 * H0, rtol=1e-6, atol=0)
+    torch.testing.assert_close(P, 2 * P0, rtol=1e-6, atol=0)
+    lh.lh_accumulate_act_aware_fq(X[:0], amax, H=H, P=P, beta=0.5)
+    torch.testing.assert_close(H, H0, rtol=1e-6, atol=0)
+
 # ------------------------------------------------------------------------------------ sweep
 def _oracle_h32(wl):
     """fp32 Hessians computed by the oracle: the identical input both sweeps receive."""

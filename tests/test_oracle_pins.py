@@ -384,3 +384,95 @@ def test_generator_is_deterministic_and_shaped():
     assert a.sha256()["W"] == want["c1.W"] and a.sha256()["X"] == want["c1.X"]
     c = synth.make("c5", n_groups=8, cout=4, cin=32, tokens=100, topk=3)
     assert c.offsets[-1] == 300 and np.all(np.diff(c.offsets) >= 0)
+
+
+# ------------------------------------------------------------------ activation fake-quant (X_q)
+def test_e4m3_nearest_matches_library_encoder_and_saturates():
+    """Block scales round like torch's float8_e4m3fn encoder (nearest, ties to even) on fp32
+    inputs covering every binade, every midpoint and its float neighbours; above 448 they stay
+    at 448 and below 2^-10 they flush to 0."""
+    import torch
+    values = np.concatenate([[0.0], oracle.e4m3_ladder()])
+    mids = (values[:-1] + values[1:]) / 2
+    r = np.random.default_rng(5)
+    y = np.concatenate([np.exp2(r.uniform(-12, np.log2(448.0), 4000)), mids,
+                        np.nextafter(mids.astype(np.float32), np.float32(0)),
+                        np.nextafter(mids.astype(np.float32), np.float32(1e9)), values])
+    y = y.astype(np.float32).astype(np.float64)
+    y = y[y <= 448.0]
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_nearest(y), ref)
+    assert np.all(oracle.e4m3_nearest(np.array([448.0, 450.0, 464.0, 1e6])) == 448.0)
+    assert oracle.e4m3_nearest(np.array([2.0 ** -10]))[0] == 0.0          # tie to even code 0
+    assert oracle.e4m3_nearest(np.array([2.0 ** -10 * 1.0001]))[0] == 2.0 ** -9
+
+
+def _exact_act_fq(x, amax, bf16):
+    """One row's X_q by exact rational arithmetic (brute force over every E4M3 and E2M1 value)."""
+    import torch
+    gx = Fraction(float(np.float32(Fraction(amax) / 2688)))
+    vals = [Fraction(0)] + [Fraction(v) for v in oracle.e4m3_ladder()]
+    grid = [Fraction(v) for v in oracle.E2M1_GRID]
+    out = []
+    for blk in np.asarray(x).reshape(-1, 16):
+        am = max(abs(Fraction(float(t))) for t in blk)
+        y = am / (6 * gx) if gx else Fraction(0)
+        d = [abs(y - v) for v in vals]
+        best = min(d)
+        code = [k for k in range(127) if d[k] == best]
+        code = [k for k in code if k % 2 == 0] or code
+        s = Fraction(float(np.float32(vals[code[0]] * gx)))
+        for t in blk:
+            if s == 0:
+                out.append(0.0)
+                continue
+            rr = abs(Fraction(float(t))) / s
+            dg = [abs(rr - gv) for gv in grid]
+            m = min(dg)
+            c = [k for k in range(8) if dg[k] == m]
+            c = [k for k in c if k % 2 == 0] or c
+            q = float(np.float32(float(grid[c[0]] * s)))
+            out.append(-q if t < 0 else q)
+    out = np.array(out, dtype=np.float32)
+    if bf16:
+        out = torch.from_numpy(out).to(torch.bfloat16).to(torch.float32).numpy()
+    return out.astype(np.float64)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_activation_fake_quant_matches_exact_rationals(bf16):
+    r = np.random.default_rng(9 + bf16)
+    x = (r.standard_t(4, size=(6, 64)) * 0.7).astype(np.float32)
+    x[1, :16] = 0.0                                  # zero block
+    x[2, 16:32] *= 1e-4                              # block far below the global scale
+    x[3, 32:48] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5] * 2, dtype=np.float32)
+    x[4] = -x[4]
+    if bf16:
+        x = synth.f32_from_bf16_bits(synth.bf16_bits_from_f32(x))
+    amax = float(np.abs(x).max())
+    for a in (amax, amax / 3.0):                      # the second saturates some blocks at 448
+        got = oracle.activation_fake_quant(x.astype(np.float64), [a], np.array([0, 6]), bf16=bf16)
+        for row in range(6):
+            np.testing.assert_array_equal(got[row], _exact_act_fq(x[row], a, bf16))
+    assert np.all(oracle.activation_fake_quant(x.astype(np.float64), [0.0], np.array([0, 6]), bf16) == 0.0)
+
+
+def test_activation_fake_quant_agrees_with_generator_recipe():
+    """The generator's own quantizer (which makes the activation-aware workload's X_q input) and
+    the oracle's, written independently, give the same X_q."""
+    wl = synth.make("c3", cout=8, cin=96, rows=530)
+    X = wl.X_f64()
+    got = oracle.activation_fake_quant(X, [np.abs(X).max()], np.array([0, X.shape[0]]), bf16=True)
+    np.testing.assert_array_equal(got, wl.Xq_f64())
+
+
+def test_activation_fake_quant_is_on_the_grid_and_per_group():
+    r = np.random.default_rng(4)
+    X = r.normal(0, 1, (40, 32)).astype(np.float32).astype(np.float64)
+    off = np.array([0, 10, 10, 40])
+    amax = np.array([np.abs(X[:10]).max(), 1.0, 0.5 * np.abs(X[10:]).max()])
+    Q = oracle.activation_fake_quant(X, amax, off, bf16=False)
+    for g in range(3):
+        sub = oracle.activation_fake_quant(X[off[g]:off[g + 1]], amax[g:g + 1], np.array([0, off[g + 1] - off[g]]), False)
+        np.testing.assert_array_equal(Q[off[g]:off[g + 1]], sub)
+    assert np.all(np.sign(Q) * np.sign(X) >= 0)      # never flips a sign
