@@ -84,7 +84,7 @@ def parse():
     p.add_argument("--fq", action="store_true",
                    help="activation-aware workload: make X_q from X inside the accumulation kernel "
                         "(lh_accumulate_act_aware_fq) instead of reading a stored X_q")
-    p.add_argument("--cpu-sample-blocks", type=int, default=24576,
+    p.add_argument("--cpu-sample-blocks", type=int, default=65536,
                    help="blocks of the oracle's sweep timed for the CPU baseline")
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -267,7 +267,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": sweep_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": sweep_tflops / FP32_PEAK_TFLOPS, "traffic": None}
-    roof["traffic"] = measured_traffic(args.config, "k_sweep")
+    rec = args.config + ("fq" if args.fq and wl.mode == "act" else "")   # key of the counter record
+    roof["traffic"] = measured_traffic(rec, "k_sweep")
     roof.update({"kernel": "sweep", "flops_per_block": flops_blk, "blocks_per_launch": blocks,
                  "avg_launch_ms": ms_sw})
 
@@ -292,7 +293,7 @@ def main():
         "roofline": roof,
         "accumulate": {"avg_launch_ms": ms_acc, "algorithmic_bytes": acc_bytes, "achieved_gbs": acc_gbs,
                        "peak_gbs": HBM_PEAK_GBS, "frac": acc_gbs / HBM_PEAK_GBS,
-                       "traffic": measured_traffic(args.config, "k_acc"),
+                       "traffic": measured_traffic(rec, "k_acc"),
                        "copy_gbs": copy_gbs, "frac_of_copy": acc_gbs / copy_gbs},
         "absmax": {"avg_launch_ms": ms_abs, "achieved_gbs": abs_gbs, "frac": abs_gbs / HBM_PEAK_GBS},
         "sweep": {"avg_launch_ms": ms_sw, "blocks_per_s": blocks / (ms_sw * 1e-3), "tflops": sweep_tflops},
