@@ -250,6 +250,12 @@ def main():
     ms_abs = phase_ms(absmax)
     ms_acc = phase_ms(accumulate)
     ms_sw = phase_ms(sweep)
+    # after the path: the fake-quantized bf16 weights and block amax the chosen codes define
+    wq_buf = torch.empty((G, cout, cin), dtype=torch.bfloat16, device=dev)
+    bam_buf = torch.empty((G, cout, nb), dtype=torch.float32, device=dev)
+    ms_dq = phase_ms(lambda j: lh.lh_dequantize(code, fp4, amax, dtype=torch.bfloat16, Wq=wq_buf, block_amax=bam_buf))
+    del wq_buf, bam_buf
+    dq_bytes = blocks * (1 + 8 + 32 + 4) + G * 4
     # reference: a device-to-device copy of X (the same rotating sources), bytes read + written
     xdst = torch.empty_like(Xs[0])
     ms_copy = phase_ms(lambda j: xdst.copy_(Xs[j]))
@@ -296,6 +302,9 @@ def main():
                        "traffic": measured_traffic(rec, "k_acc"),
                        "copy_gbs": copy_gbs, "frac_of_copy": acc_gbs / copy_gbs},
         "absmax": {"avg_launch_ms": ms_abs, "achieved_gbs": abs_gbs, "frac": abs_gbs / HBM_PEAK_GBS},
+        "dequantize": {"avg_launch_ms": ms_dq, "algorithmic_bytes": dq_bytes,
+                       "achieved_gbs": dq_bytes / (ms_dq * 1e-3) / 1e9,
+                       "frac": dq_bytes / (ms_dq * 1e-3) / 1e9 / HBM_PEAK_GBS, "outside_step": True},
         "sweep": {"avg_launch_ms": ms_sw, "blocks_per_s": blocks / (ms_sw * 1e-3), "tflops": sweep_tflops},
     }
     if not args.no_cpu_baseline and G == 1:

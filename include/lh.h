@@ -24,10 +24,10 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null stream of
  *     the pointers' device).  The library never synchronizes the host, launches on the device that
  *     owns the pointers and restores the caller's current device.
- *   - Scratch memory, when an entry point needs it (accumulation partial sums), comes from a
- *     library-owned memory pool of the device, allocated and freed stream-ordered on `stream`
- *     within the call; the pool keeps the memory for reuse, so steady-state calls do not reach
- *     the driver's allocator.
+ *   - Scratch memory, when an entry point needs it (accumulation partial sums and arrival
+ *     counters), is a library-owned buffer per device, grown on demand in stream order from a
+ *     device memory pool and kept between calls, so steady-state calls allocate nothing; calls
+ *     on different streams are ordered through an event, so two calls never use it at once.
  *   - Return: LH_OK, or an error code with a message available from lh_last_error().  Argument
  *     checks run before any launch.  Faults inside kernels surface at the caller's next
  *     synchronization, as usual in HIP.  NaN or Inf in any input gives undefined results.
@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LH_VERSION 1
+#define LH_VERSION 2
 
 typedef enum {
   LH_OK = 0,
@@ -151,6 +151,25 @@ lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int6
 lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
                               int64_t cin, const float* global_amax, const float* imp,
                               uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream);
+
+/*
+ * Fake-quantized weights and per-block amax from a sweep's result: the calibrated quantizer state
+ * ("Add WMSE weight scale search calibration": the shared-path check fingerprints the quantizers'
+ * amax and scales and the final fake-quantized weights):
+ *   s_k  = fp32(v_k * fp32(global_amax[g] / (6*448)))  for the block's code k (the sweep's scale)
+ *   Wq[g][c][16n+j] = sign * E2M1 value of nibble j * s_k, rounded to fp32 and, for a bf16
+ *                     out_dtype, to nearest-even bf16 (a negative value that quantized to 0
+ *                     gives -0)
+ *   block_amax[g][c][n] = fp32(6 * s_k)
+ * scale_code [n_groups, cout, cin/16] u8 and fp4 [n_groups, cout, cin/2] u8 as lh_scale_sweep
+ * writes them (codes 0x01..0x7E); global_amax [n_groups] fp32; Wq [n_groups, cout, cin] in
+ * out_dtype or NULL (16-byte aligned); block_amax [n_groups, cout, cin/16] fp32 or NULL.
+ * Errors: INVALID_ARGUMENT for shapes as lh_scale_sweep, NULL scale_code or global_amax, both
+ * outputs NULL, NULL fp4 with Wq, misaligned pointers, non-device or mixed-device pointers.
+ */
+lh_status lh_dequantize(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
+                        int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
+                        void* Wq, float* block_amax, void* stream);
 
 /*
  * Per-group absolute maximum amax_out[g] = max |W_g| over elems_per_group elements: the max

@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("LH_LIBRARY") or os.path.join(_PKG, "liblh.so")
 LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 
-EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep", "lh_scale_sweep_diag",
+EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_dequantize", "lh_scale_sweep", "lh_scale_sweep_diag",
             "lh_absmax", "lh_last_error", "lh_version")
 
 
@@ -50,8 +50,9 @@ def lib() -> ctypes.CDLL:
         h.lh_scale_sweep.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_diag.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         h.lh_absmax.argtypes = [vp, i32, i64, i64, vp, vp]
+        h.lh_dequantize.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep",
-                  "lh_scale_sweep_diag", "lh_absmax"):
+                  "lh_scale_sweep_diag", "lh_absmax", "lh_dequantize"):
             getattr(h, f).restype = ctypes.c_int
         h.lh_last_error.argtypes = []
         h.lh_last_error.restype = ctypes.c_char_p
@@ -220,6 +221,33 @@ def lh_scale_sweep_diag(W: torch.Tensor, amax: torch.Tensor, imp: torch.Tensor,
     _check(lib().lh_scale_sweep_diag(_ptr(W), _dtype_code(W), G, cout, cin, _ptr(amax), _ptr(imp),
                                      _ptr(code), _ptr(fp4), _ptr(loss), _stream(W.device)))
     return code, fp4, loss
+
+
+def lh_dequantize(code: torch.Tensor, fp4: torch.Tensor, amax: torch.Tensor, dtype: torch.dtype = torch.bfloat16,
+                  Wq: Optional[torch.Tensor] = None, block_amax: Optional[torch.Tensor] = None,
+                  want_wq: bool = True, want_block_amax: bool = True):
+    """Fake-quantized weights Wq [G, cout, cin] (bf16 or fp32) and per-block amax [G, cout, cin/16]
+    from the sweep's scale codes and FP4 nibbles."""
+    if code.dim() != 3:
+        raise ValueError("code must be [G, cout, cin/16]")
+    G, cout, nb = code.shape
+    cin = nb * 16
+    _need(code, "code", (G, cout, nb), torch.uint8)
+    _need(fp4, "fp4", (G, cout, cin // 2), torch.uint8)
+    _need(amax, "amax", (G,), torch.float32)
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dtype must be torch.bfloat16 or torch.float32")
+    if Wq is None and want_wq:
+        Wq = torch.empty((G, cout, cin), dtype=dtype, device=code.device)
+    if block_amax is None and want_block_amax:
+        block_amax = torch.empty((G, cout, nb), dtype=torch.float32, device=code.device)
+    if Wq is not None:
+        _need(Wq, "Wq", (G, cout, cin), dtype)
+    if block_amax is not None:
+        _need(block_amax, "block_amax", (G, cout, nb), torch.float32)
+    _check(lib().lh_dequantize(_ptr(code), _ptr(fp4), 1 if dtype == torch.bfloat16 else 0, G, cout, cin,
+                               _ptr(amax), _ptr(Wq), _ptr(block_amax), _stream(code.device)))
+    return Wq, block_amax
 
 
 def lh_absmax(W: torch.Tensor, amax: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "liblh.so")
-SOURCES = ["absmax.hip", "accumulate.hip", "sweep.hip", "lh_abi.cpp"]
+SOURCES = ["absmax.hip", "accumulate.hip", "sweep.hip", "dequant.hip", "lh_abi.cpp"]
 ARCH = "gfx950"
 # Packed fp32 ALU instructions are kept out of the generated code; MFMA results live in VGPRs
 # (no accumulator-register copies in the sweep loop).

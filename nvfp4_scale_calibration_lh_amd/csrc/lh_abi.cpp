@@ -322,6 +322,28 @@ lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups,
   return ok();
 }
 
+lh_status lh_dequantize(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
+                        int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
+                        void* Wq, float* block_amax, void* stream) {
+  if (!dtype_ok(out_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)out_dtype);
+  lh_status st = check_sweep_shapes(n_groups, cout, cin);
+  if (st != LH_OK) return st;
+  if (!scale_code || !global_amax) return fail(LH_ERR_INVALID_ARGUMENT, "scale_code and global_amax are required");
+  if (!Wq && !block_amax) return fail(LH_ERR_INVALID_ARGUMENT, "at least one of Wq, block_amax must be given");
+  if (Wq && !fp4) return fail(LH_ERR_INVALID_ARGUMENT, "fp4 is required for Wq");
+  int dev = -1;
+  st = check_pointers({{scale_code, "scale_code"}, {fp4, "fp4"}, {global_amax, "global_amax"}, {Wq, "Wq"}, {block_amax, "block_amax"}}, &dev);
+  if (st != LH_OK) return st;
+  if ((st = check_aligned(Wq, "Wq")) != LH_OK) return st;
+  if (fp4 && (reinterpret_cast<uintptr_t>(fp4) % 8) != 0) return fail(LH_ERR_INVALID_ARGUMENT, "fp4 must be 8-byte aligned");
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipError_t e = lh::launch_dequantize(scale_code, fp4, global_amax, n_groups, cout, cin, out_dtype == LH_DTYPE_BF16,
+                                       Wq, block_amax, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return ok();
+}
+
 lh_status lh_absmax(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t elems_per_group,
                     float* amax_out, void* stream) {
   if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lh {
 
 // Scratch of one launch_accumulate call: a work area (piece table of grouped rows and partial
@@ -38,5 +40,10 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
 hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t cout,
                              int64_t cin, const float* amax, const float* imp, uint8_t* code,
                              uint8_t* fp4, float* loss, hipStream_t stream);
+
+// Wq (bf16 or fp32, may be NULL) and block_amax (may be NULL) from scale codes and FP4 nibbles.
+hipError_t launch_dequantize(const uint8_t* code, const uint8_t* fp4, const float* amax, int64_t n_groups,
+                             int64_t cout, int64_t cin, bool bf16, void* Wq, float* block_amax,
+                             hipStream_t stream);
 
 }  // namespace lh

@@ -16,6 +16,7 @@ from .lh_oracle import (  # noqa: F401
     accumulate_act_aware,
     activation_fake_quant,
     candidate_scales,
+    dequantize,
     e2m1_index,
     e4m3_ladder,
     e4m3_nearest,

@@ -14,6 +14,7 @@ What it computes, in the order and notation of the pages:
   Page: "Add activation-aware local Hessian scale calibration" (PR #1976), What does this PR do?
 * ``activation_fake_quant``: the X_q those use when the layer's NVFP4 input quantizer is applied
   to X (per-token 16-channel E4M3 block scales under the 448-normalized global scale).
+* ``dequantize``: the fake-quantized weights and per-block amax that the chosen codes define.
 * ``sweep``: for every 16-element weight block try each of the 126 positive finite E4M3 block
   scales, fake-quantize to E2M1, score ``dw^T H_n dw + 2 dw^T (P_n w0)`` with ``dw = quant(w) - w``
   and keep the argmin, starting from best = +inf.  Pages: PR #1976 review assessment (sign of dw,
@@ -245,6 +246,29 @@ def activation_fake_quant(X, x_amax, offsets, bf16: bool, rows_per_chunk: int = 
             q32 = wq.astype(np.float32)                              # the product in fp32
             out[a:b] = (_bf16_round(q32) if bf16 else q32.astype(np.float64)).reshape(b - a, cin)
     return out
+
+
+def dequantize(code, fp4, amax, bf16: bool):
+    """Fake-quantized weights and per-block amax from scale codes [G, cout, nb] (bytes 1..126)
+    and packed nibbles [G, cout, cin/2] -- the calibrated quantizer state whose amax, scales and
+    final fake-quantized weights "Add WMSE weight scale search calibration" fingerprints.
+
+    s = fp32(v_code * g) with g = fp32(amax / (6*448)); Wq = sign * E2M1 value * s rounded to fp32
+    (then to bf16 for bf16 weights), a set sign bit giving -0 for a zero value; block amax =
+    fp32(6 s).  Returns (Wq float64 values [G, cout, cin], block_amax float64 [G, cout, nb])."""
+    code = np.asarray(code, dtype=np.int64)
+    fp4 = np.asarray(fp4, dtype=np.uint8)
+    G, cout, nb = code.shape
+    g = global_scale(np.asarray(amax, dtype=np.float64))
+    v = e4m3_ladder()[code - 1]
+    s = (v * g[:, None, None]).astype(np.float32).astype(np.float64)
+    nib = np.empty((G, cout, nb * BLOCK), dtype=np.uint8)
+    nib[..., 0::2] = fp4 & 15
+    nib[..., 1::2] = fp4 >> 4
+    mag = E2M1_GRID[nib & 7] * np.repeat(s, BLOCK, axis=-1)
+    wq = np.where(nib >= 8, -mag, mag).astype(np.float32)
+    Wq = _bf16_round(wq) if bf16 else wq.astype(np.float64)
+    return Wq, (6.0 * s).astype(np.float32).astype(np.float64)
 
 
 # ----------------------------------------------------------------------------- sweep

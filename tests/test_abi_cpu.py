@@ -20,8 +20,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_scale_sweep", "lh_scale_sweep_diag",
-              "lh_absmax", "lh_last_error", "lh_version"):
+    for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep",
+              "lh_scale_sweep_diag", "lh_dequantize", "lh_absmax", "lh_last_error", "lh_version"):
         assert n in names
     assert set(names) == set(lh.EXPORTED)
 
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = lh.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert lh.lh_version() == 1
+    assert lh.lh_version() == 2
 
 
 VP = ctypes.c_void_p
@@ -65,6 +65,13 @@ def test_validation_errors_without_device():
     assert L.lh_accumulate_act_aware_fq(FAKE, 1, 10, 32, None, 1, FAKE, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_accumulate_act_aware_fq(FAKE, 1, 10, 40, None, 1, FAKE, 0.0, FAKE, FAKE, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_accumulate_act_aware_fq(FAKE, 5, 10, 32, None, 1, FAKE, 0.0, FAKE, FAKE, None) == lh.LH_ERR_UNSUPPORTED
+    # dequantize: codes and amax required, at least one output, fp4 with Wq
+    c, m = _err(L.lh_dequantize(None, FAKE, 1, 1, 4, 32, FAKE, FAKE, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "scale_code" in m
+    assert L.lh_dequantize(FAKE, FAKE, 1, 1, 4, 32, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_dequantize(FAKE, None, 1, 1, 4, 32, FAKE, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_dequantize(FAKE, FAKE, 1, 1, 4, 40, FAKE, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_dequantize(FAKE, FAKE, 7, 1, 4, 32, FAKE, FAKE, None, None) == lh.LH_ERR_UNSUPPORTED
     # sweep
     assert L.lh_scale_sweep(FAKE, 1, 0, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_scale_sweep(FAKE, 1, 1, 4, 33, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT

@@ -160,6 +160,32 @@ def test_fullsize_codes_and_nibbles_consistent(run):
             assert not bad.any(), f"group {g}: {bad.sum()} blocks whose FP4 bytes are not the encoding at their scale"
 
 
+
+def test_fullsize_dequantize(run):
+    """Fake-quantized bf16 weights and block amax of every block (8 sampled experts for the MoE
+    layer) from the full-size sweep's codes, bit for bit against the oracle's decoding."""
+    name, wl, out = run
+    G = wl.n_groups
+    groups = np.arange(G) if G == 1 else np.sort(np.random.default_rng(6).choice(G, size=8, replace=False))
+    note(f"full-size {name}: dequantize {len(groups)} group(s)")
+    code = np.ascontiguousarray(out["code"][groups])
+    fp4 = np.ascontiguousarray(out["fp4"][groups])
+    amax = np.ascontiguousarray(out["amax"][groups])
+    Wq, bam = lh.lh_dequantize(torch.from_numpy(code).to(DEV), torch.from_numpy(fp4).to(DEV),
+                               torch.from_numpy(amax).to(DEV), dtype=torch.bfloat16)
+    got_w = Wq.view(torch.int16).cpu().numpy()
+    got_a = bam.cpu().numpy()
+    del Wq, bam
+    torch.cuda.empty_cache()
+    step = max(1, (1 << 22) // wl.cin)
+    for k in range(len(groups)):
+        for r0 in range(0, wl.cout, step):
+            r1 = min(wl.cout, r0 + step)
+            ref_w, ref_a = oracle.dequantize(code[k:k + 1, r0:r1], fp4[k:k + 1, r0:r1], amax[k:k + 1], bf16=True)
+            ref_bits = synth.bf16_bits_from_f32(ref_w.astype(np.float32)).view(np.int16)
+            np.testing.assert_array_equal(got_w[k, r0:r1], ref_bits[0])
+            np.testing.assert_array_equal(got_a[k, r0:r1].astype(np.float64), ref_a[0])
+
 def test_fullsize_fused_fake_quant_matches_two_input_path():
     """Activation-aware up_proj 12288x4096 (X [8192,4096] bf16): H and P with X_q made in the
     kernel equal, value for value, those of the two-input kernel fed the generator's X_q (the

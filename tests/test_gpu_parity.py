@@ -275,6 +275,27 @@ def test_sweep_signed_zeros_bf16():
     res = oracle.sweep_diag(W64, amax, imp)
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
+
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_dequantize_matches_oracle(name):
+    """Fake-quantized weights and block amax from the GPU sweep's own codes and nibbles, bit for
+    bit against the oracle's decoding, in bf16 and fp32."""
+    wl = synth.make(name, **SMALL[name])
+    note(f"dequantize {name} W{wl.W.shape}")
+    W, _, _, _ = upload(wl)
+    H32, P32 = _oracle_h32(wl)
+    amax = torch.from_numpy(oracle.absmax(wl.W_f64()).astype(np.float32)).to(DEV)
+    code, fp4, _ = lh.lh_scale_sweep(W, amax, torch.from_numpy(H32).to(DEV), None)
+    for dt, bf16 in ((torch.bfloat16, True), (torch.float32, False)):
+        Wq, bam = lh.lh_dequantize(code, fp4, amax, dtype=dt)
+        ref_w, ref_a = oracle.dequantize(code.cpu().numpy(), fp4.cpu().numpy(), amax.cpu().numpy(), bf16=bf16)
+        got = Wq.float().cpu().numpy().astype(np.float64)
+        np.testing.assert_array_equal(got, ref_w)
+        assert np.array_equal(np.signbit(got), np.signbit(ref_w))
+        np.testing.assert_array_equal(bam.cpu().numpy().astype(np.float64), ref_a)
+    Wq2, none = lh.lh_dequantize(code, fp4, amax, want_block_amax=False)
+    assert none is None and torch.equal(Wq2, lh.lh_dequantize(code, fp4, amax)[0])
+
 def test_sweep_exact_midpoint_ties():
     """Weights placed exactly on E2M1 midpoints of some candidate scale must round like the oracle."""
     r = np.random.default_rng(4)

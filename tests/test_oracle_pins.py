@@ -476,3 +476,31 @@ def test_activation_fake_quant_is_on_the_grid_and_per_group():
         sub = oracle.activation_fake_quant(X[off[g]:off[g + 1]], amax[g:g + 1], np.array([0, off[g + 1] - off[g]]), False)
         np.testing.assert_array_equal(Q[off[g]:off[g + 1]], sub)
     assert np.all(np.sign(Q) * np.sign(X) >= 0)      # never flips a sign
+
+
+# ------------------------------------------------------------------ dequantized weights
+@pytest.mark.parametrize("bf16", [True, False])
+def test_dequantize_reproduces_fake_quant_of_the_chosen_scale(bf16):
+    """Decoding codes and packed nibbles gives back, element for element, the fake-quantized
+    block that the search scored (fake_quant at the chosen scale, rounded to the storage type);
+    block amax is 6 s and bounds every |Wq| of the block."""
+    import torch
+    r = np.random.default_rng(13)
+    G, cout, cin = 2, 5, 48
+    W = r.normal(0, 0.02, (G, cout, cin))
+    W[0, 1, :16] = 0.0
+    W[1, 2, 3] = -1e-12                            # quantizes to -0
+    amax = oracle.absmax(W).astype(np.float32)
+    code = r.integers(1, 127, size=(G, cout, cin // 16)).astype(np.uint8)
+    s = oracle.candidate_scales(oracle.global_scale(amax.astype(np.float64)))       # [G, 126]
+    sb = np.take_along_axis(s, code.reshape(G, -1).astype(np.int64) - 1, axis=1).reshape(G, cout, -1)
+    nib, wq, _ = oracle.fake_quant(W.reshape(G, cout, -1, 16), sb[..., None])
+    fp4 = oracle.pack_nibbles(nib.reshape(G, cout, cin))
+    Wq, bam = oracle.dequantize(code, fp4, amax, bf16=bf16)
+    ref = wq.reshape(G, cout, cin).astype(np.float32)
+    if bf16:
+        ref = torch.from_numpy(ref).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(Wq, ref.astype(np.float64))
+    assert np.signbit(Wq[1, 2, 3]) and Wq[1, 2, 3] == 0.0
+    np.testing.assert_array_equal(bam, (6.0 * sb).astype(np.float32).astype(np.float64))
+    assert np.all(np.abs(Wq).reshape(G, cout, -1, 16).max(axis=-1) <= bam * (1 + 2 ** -7))
