@@ -253,7 +253,9 @@ struct FullLds {
   float sw[16];        // S_w = sum_j d_j |w_j| per row
   float b[16][16];     // (P w)[row][elem]           } the loss of the tile's
   float ws[16];        // winner's scale per row      } filter-decided winners
-  unsigned short wn[16][4];   // winner's signed nibbles per row and lane group
+  float wi[16];        // winner's 1/scale per row    }
+  int kw[16];          // winner's code per row       }
+  unsigned short wn[16][4];   // winner's signed nibbles per row and lane group (override rows)
   double ex[4][16];    // float64 refinement: e of up to 4 contenders
 };
 
@@ -390,7 +392,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
     const int rows_here = (int)min((int64_t)16, c_end - c0);
-    unsigned emitted = 0u;                           // rows whose winner came from the filter
+    unsigned batched = 0u;   // rows whose unique winner is emitted by the per-tile pass below
+    unsigned emitted = 0u;   // rows with midpoint overrides, emitted at once (loss per tile)
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
       const int64_t oblk = (g * cout + c) * nb + n;
@@ -531,24 +534,30 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
           iw = __builtin_amdgcn_ldexpf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(is1), src)), -sh);
           sw = __builtin_amdgcn_ldexpf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), src)), sh);
         }
-        float rw[4];
+        if (!has_ovr) {
+          // codes, nibbles and loss come from the per-tile pass, 16 rows at once
+          if (lane == 0) {
+            L.ws[rr] = sw;
+            L.wi[rr] = iw;
+            L.kw[rr] = k_best;
+          }
+          batched |= 1u << rr;
+        } else {
+          float rw[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) rw[t] = w[t] * iw;
-        if (has_ovr) {
+          for (int t = 0; t < 4; ++t) rw[t] = w[t] * iw;
           apply_overrides(m0, 0, kv0, rv0, -1, k_best, i, gg, rw);
           apply_overrides(m1, 64, kv1, rv1, -1, k_best, i, gg, rw);
-        }
-        // the converts' sign bit is the sign of w, which is (w < 0) since w is never -0
-        unsigned nb4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, rw[0], rw[1], 1.0f, 0);
-        nb4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(nb4, rw[2], rw[3], 1.0f, 1);
-        if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
-        if (lane == 0) code[oblk] = (uint8_t)k_best;
-        if (loss) {
-          // The filter's mL carries the cancellation error of s(Hq) - Hw; the reported loss is
-          // re-evaluated from the winner's codes once per tile (below).
-          if (i == 0) L.wn[rr][gg] = (unsigned short)nb4;
-          if (lane == 0) L.ws[rr] = sw;
-          emitted |= 1u << rr;
+          // the converts' sign bit is the sign of w, which is (w < 0) since w is never -0
+          unsigned nb4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, rw[0], rw[1], 1.0f, 0);
+          nb4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(nb4, rw[2], rw[3], 1.0f, 1);
+          if (i == 0 && fp4) *(unsigned short*)(fp4 + (g * cout + c) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nb4;
+          if (lane == 0) code[oblk] = (uint8_t)k_best;
+          if (loss) {
+            if (i == 0) L.wn[rr][gg] = (unsigned short)nb4;
+            if (lane == 0) L.ws[rr] = sw;
+            emitted |= 1u << rr;
+          }
         }
       } else if (cnt >= 2 && cnt <= 4) {
         // 2..4 contenders: re-score them exactly in float64, 16 lanes (one per element) each
@@ -604,30 +613,45 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
         if (lane == 0) code[oblk] = 0;              // many contenders: float64 pass
       }
     }
-    if (emitted) {
-      // Loss of the filter-decided winners of this tile from their codes: e* = q s* - w, then
-      // (H e*) on fp32 MFMA in the layout of H w (lane: row i, elements 4gg..4gg+3) and
-      // e*^T (H e* + 2 P w).
+    if (batched | emitted) {
+      // The filter-decided winners of this tile, lane (row i, elements 4gg..4gg+3): nibbles of
+      // the batched rows (w * (1/s*) through the FP4 converts; no midpoint is near), code and
+      // nibble stores, then the loss from the codes -- the filter's value carries the
+      // cancellation of s(Hq) - Hw -- as e* = q s* - w, (H e*) on fp32 MFMA in the layout of
+      // H w and e*^T (H e* + 2 P w).
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      const bool on = (emitted >> i) & 1u;
-      const unsigned nbits = on ? (unsigned)L.wn[i][gg] : 0u;
-      const float sw = on ? L.ws[i] : 0.0f;
-      const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nbits, 1.0f, 0);
-      const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nbits, 1.0f, 1);
-      const float qv[4] = {q01[0], q01[1], q23[0], q23[1]};
-      float ev[4];
+      const bool on_b = (batched >> i) & 1u;
+      const bool on = on_b || ((emitted >> i) & 1u);
+      unsigned nbits = 0u;
+      if (on_b) {
+        const float iw = L.wi[i];
+        nbits = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, L.w[i][4 * gg] * iw, L.w[i][4 * gg + 1] * iw, 1.0f, 0);
+        nbits = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(nbits, L.w[i][4 * gg + 2] * iw, L.w[i][4 * gg + 3] * iw, 1.0f, 1);
+        nbits &= 0xFFFFu;
+        if (fp4) *(unsigned short*)(fp4 + (g * cout + c0 + i) * (cin / 2) + n * 8 + 2 * gg) = (unsigned short)nbits;
+        if (gg == 0) code[(g * cout + c0 + i) * nb + n] = (uint8_t)L.kw[i];
+      } else if (on) {
+        nbits = (unsigned)L.wn[i][gg];
+      }
+      if (loss) {
+        const float sw = on ? L.ws[i] : 0.0f;
+        const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nbits, 1.0f, 0);
+        const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nbits, 1.0f, 1);
+        const float qv[4] = {q01[0], q01[1], q23[0], q23[1]};
+        float ev[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) ev[t] = on ? fmaf(qv[t], sw, -L.w[i][4 * gg + t]) : 0.0f;
-      v4f he = zero4;
+        for (int t = 0; t < 4; ++t) ev[t] = on ? fmaf(qv[t], sw, -L.w[i][4 * gg + t]) : 0.0f;
+        v4f he = zero4;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) he = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], ev[t], he, 0, 0, 0);
-      float part = 0.0f;
+        for (int t = 0; t < 4; ++t) he = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], ev[t], he, 0, 0, 0);
+        float part = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        part = fmaf(ev[t], coupled ? fmaf(2.0f, L.b[i][4 * gg + t], he[t]) : he[t], part);
-      const float Lrow = group_sum(part);
-      if (gg == 0 && on) loss[((g * cout + c0 + i) * nb) + n] = Lrow;
+        for (int t = 0; t < 4; ++t)
+          part = fmaf(ev[t], coupled ? fmaf(2.0f, L.b[i][4 * gg + t], he[t]) : he[t], part);
+        const float Lrow = group_sum(part);
+        if (gg == 0 && on) loss[((g * cout + c0 + i) * nb) + n] = Lrow;
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
