@@ -237,9 +237,12 @@ def main():
 
     # per-phase launch durations: the same calls back to back (rotating inputs), between two
     # events on the library's stream, so each average is the kernel's steady-state duration
+    # (a ~2 ms spin first keeps the GPU busy while the calls are queued, so for phases of a few
+    # microseconds the events time the kernels rather than the host's launch rate)
     def phase_ms(fn):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        torch.cuda._sleep(4_000_000)
         a.record(stream)
         for i in range(args.steps):
             fn(i % copies)
