@@ -430,6 +430,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       // q' = q * 4^(tau-1) (exact in bf16), e = fma(q', s, -w), y = H q' on bf16 MFMA (H in
       // two pieces, products exact, fp32 accumulation), (H e + 2b)_i = s y_i - (H w - 2b)_i,
       // L = sum_i e_i (H e + 2b)_i.  Instantiated twice so the common case has no override code.
+      unsigned pkc = 0u;
       auto score = [&](auto ovr_tag, float Lq[2], float Aq[2]) {
         constexpr bool OVR = decltype(ovr_tag)::value;
         auto tile_err = [&](int tau, float e[4], unsigned& p01, unsigned& p23) {
@@ -445,8 +446,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
             for (int t = 0; t < 4; ++t) r[t] = o[t] * sc;
           }
-          unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], sc, 0);
-          pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, r[2], r[3], sc, 1);
+          // bytes 0 and 1 of the pack register are written and read; its other bytes never
+          // are, so the register carried from the previous tile serves as the old value
+          pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, r[0], r[1], sc, 0);
+          pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, r[2], r[3], sc, 1);
+          const unsigned pk = pkc;
           const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc, 0);
           const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc, 1);
           const float sb = tau == 0 ? s0 : s1;
@@ -855,6 +859,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
   const float s0 = cand_scale(k0, gsc), s1 = cand_scale(v1 ? k1 : 126, gsc);
   const float is0 = inv_scale(s0), is1 = inv_scale(s1);
 
+  unsigned pkc = 0u;                              // FP4 pack register carried between uses
   for (int64_t c = c_begin; c < c_end; ++c) {
     const int64_t oblk = (g * cout + c) * nb + n;
     const int rr = (int)(c - c_begin);
@@ -874,8 +879,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
     float L0 = 0.0f, L1 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
-      unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, w[j] * is0, w[j + 1] * is0, 1.0f, 0);
-      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, w[j] * is1, w[j + 1] * is1, 1.0f, 1);
+      // bytes 0 and 1 are written and read; the other bytes of the carried register never are
+      pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, w[j] * is0, w[j + 1] * is0, 1.0f, 0);
+      pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, w[j] * is1, w[j + 1] * is1, 1.0f, 1);
+      const unsigned pk = pkc;
       const v2f qa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
       const v2f qb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 1);
       const float ea0 = fmaf(qa[0], s0, -w[j]), ea1 = fmaf(qa[1], s0, -w[j + 1]);
