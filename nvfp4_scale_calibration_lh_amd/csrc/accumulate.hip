@@ -457,8 +457,10 @@ __device__ inline v4f sum_partials(const float* w0, int64_t stride, int64_t n, i
 // (many waves per tile: few tiles, so few partial sums, yet enough loads in flight).
 // Partial layout: [slice][tile][m][block][kPart].
 // ---------------------------------------------------------------------------------------------
-template <bool BF16>
-constexpr int dense_waves() { return BF16 ? 16 : 4; }
+// Waves per dense workgroup (measured on MI355X): 8 for bf16 H alone, so two workgroups share a
+// compute unit; 16 for bf16 H and P (both forms: X_q read or made in the kernel, which therefore
+// tile alike and sum in the same order) and for importance only; 4 for fp32.
+constexpr int dense_waves(bool bf16, bool imp_only, bool act) { return bf16 ? ((imp_only || act) ? 16 : 8) : 4; }
 
 template <bool BF16, bool ACT, bool DIAG, int NW, bool FQ>
 __global__ __launch_bounds__(NW * 64) void k_acc_dense(
@@ -661,12 +663,12 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
 }
 
 // Rows per tile of a dense layer: NW waves x 32 rows x c chunks per wave, with the largest c of
-// 1, 2, 4, 8 that still gives 256 workgroups (one per compute unit; the 16-wave workgroups of
-// H and P fill a compute unit's LDS), or 1024 when only the importance is produced (smaller
-// workgroups, several per compute unit).  Measured on MI355X for the dense shapes.
-int64_t dense_tile_rows(int64_t rows, int64_t nb, bool bf16, bool imp_only) {
+// 1, 2, 4, 8 that still gives 256 workgroups, or 1024 when only the importance is produced
+// (small partials, several workgroups per compute unit).  Measured on MI355X for the dense
+// shapes.
+int64_t dense_tile_rows(int64_t rows, int64_t nb, bool bf16, bool imp_only, bool act) {
   const int64_t slices = (nb + 3) / 4;
-  const int64_t base = (bf16 ? dense_waves<true>() : dense_waves<false>()) * kChunk;
+  const int64_t base = dense_waves(bf16, imp_only, act) * kChunk;
   const int64_t want = imp_only ? 1024 : 256;
   int64_t R = base;
   while (R < 8 * base && ((rows + 2 * R - 1) / (2 * R)) * slices >= want) R *= 2;
@@ -690,8 +692,8 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
                        float* P, float* imp, void* work, unsigned* counters, hipStream_t stream) {
   const int64_t nb = cin / 16, slices = (nb + 3) / 4;
   if (dense) {
-    constexpr int NW = dense_waves<BF16>();
-    const int64_t R = dense_tile_rows(rows, nb, BF16, DIAG);
+    constexpr int NW = dense_waves(BF16, DIAG, ACT);
+    const int64_t R = dense_tile_rows(rows, nb, BF16, DIAG, ACT);
     const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
     hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG, NW, FQ>), dim3((unsigned)tiles, (unsigned)slices),
                        dim3(NW * 64), 0, stream, X, Xq, x_amax, rows, cin, R, beta, H, P, imp,
@@ -731,7 +733,7 @@ AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, 
   const size_t part = (size_t)(act_aware ? 2 : 1) * 4 * (imp_only ? 16 : 256) * sizeof(float);
   AccScratch s;
   if (is_dense(offsets, n_groups)) {
-    const int64_t R = dense_tile_rows(rows, nb, bf16, imp_only);
+    const int64_t R = dense_tile_rows(rows, nb, bf16, imp_only, act_aware);
     const int64_t tiles = (rows + R - 1) / R;
     s.work_bytes = (size_t)slices * tiles * part;
     s.counters = (size_t)slices;
