@@ -26,13 +26,15 @@
 //    the 4 lane groups with permlane swaps; the argmin over lanes uses DPP row rotations and
 //    permlane swaps.  Quantization of the next tile is issued before the current tile's MFMA
 //    result is consumed.
-//  * Diagonal form: VALU only (there is no contraction to map onto MFMA); lane l scores
-//    candidates l+1 and l+65 over all 16 elements, whose weights are wave-uniform.
+//  * Diagonal form: VALU only (there is no contraction to map onto MFMA); a lane scores two
+//    candidates of one E4M3 mantissa class over all 16 elements, whose weights are wave-uniform,
+//    in the frame scaled by sqrt(Imp) (see k_sweep_diag).
 //  * Exactness.  The float32 pass is a filter: each candidate carries a rigorous bound c*A_k on
 //    its rounding error, with A_k >= S_e^2 + S_e S_w + 2|e|^T(|P||w|), S_e = sum_i |e_i| d_i,
 //    S_w = sum_i |w_i| d_i and d_i^2 = max_j max(|H_ij|, |H_ji|) (A_k = S_e (4 S_e + S_w)
 //    without P; with P the 4 S_e^2 is taken as 4 times the sum of the squared parts of S_e over
-//    the four lane groups, which is >= S_e^2; L_k itself in the diagonal form).  Every exact
+//    the four lane groups, which is >= S_e^2; the diagonal form has a bound of its own, see
+//    k_sweep_diag).  Every exact
 //    L_k lies in [L_k - cA_k, L_k + cA_k]; the candidates whose interval starts below the
 //    lowest upper end are the only ones that can be the minimum.  If there is one, it is
 //    the exact argmin; with 2 to 4 contenders the wave re-scores them in
@@ -60,7 +62,7 @@ constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
 constexpr int kExactRows = 16;       // rows per wave of the float64 passes
 // Filter error bound factor.  Full form: the fp32 arithmetic and the two-piece bf16 split of H
 // together contribute at most about 2^-17.2 (S_e^2 + S_e S_w + 2|e|^T(|P||w|)) <= 2^-17.2 A
-// (A_k as in the header), so 2^-16 leaves a margin above 2x; diagonal form: under 5e-6 L.
+// (A_k as in the header), so 2^-16 leaves a margin above 2x.
 constexpr float kErrC = 0x1p-16f;
 constexpr int kNearUlps = 16;        // midpoint proximity test, in ulps of |w|/(m g)
 
@@ -186,29 +188,27 @@ __device__ inline float load_w(const void* W, bool bf16, int64_t idx) {
   return ((const float*)W)[idx];
 }
 
-// Minimum over all 64 lanes of a value >= 0 (or +inf): the bit patterns of such floats are
-// ordered like unsigned integers, so the reduction needs no float canonicalization.
-template <int CTRL>
-__device__ inline unsigned dppu(unsigned v) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-__device__ inline float wave_min_nonneg(float x) {
-  unsigned v = __float_as_uint(x);
-  v = min(v, dppu<0x128>(v));
-  v = min(v, dppu<0x124>(v));
-  v = min(v, dppu<0x122>(v));
-  v = min(v, dppu<0x121>(v));
-  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = min((unsigned)a[0], (unsigned)a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __uint_as_float(min((unsigned)b[0], (unsigned)b[1]));
-}
-// Minimum over all 64 lanes of a float that is not NaN, taken on integer keys whose signed
-// order is the float order (negative values have their magnitude bits flipped).
+// Wave minima, returned wave-uniform: rotations inside each 16-lane row leave the row minimum in
+// every lane, then the row broadcasts carry rows 0 and 2 into rows 1 and 3 and lane 31 into
+// rows 2 and 3 (the masked-off rows take the identity), so lane 63 ends with the minimum.
 template <int CTRL>
 __device__ inline int dppi(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
+// Of a value >= 0 (or +inf): the bit patterns of such floats are ordered like unsigned
+// integers, so the reduction needs no float canonicalization.
+__device__ inline float wave_min_nonneg(float x) {
+  unsigned v = __float_as_uint(x);
+  v = min(v, (unsigned)dppi<0x128>((int)v));
+  v = min(v, (unsigned)dppi<0x124>((int)v));
+  v = min(v, (unsigned)dppi<0x122>((int)v));
+  v = min(v, (unsigned)dppi<0x121>((int)v));
+  v = min(v, (unsigned)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xA, 0xF, false));
+  v = min(v, (unsigned)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xC, 0xF, false));
+  return __uint_as_float((unsigned)__builtin_amdgcn_readlane((int)v, 63));
+}
+// Of a float that is not NaN, taken on integer keys whose signed order is the float order
+// (negative values have their magnitude bits flipped).
 __device__ inline int order_key(int b) { return b ^ ((b >> 31) & 0x7FFFFFFF); }   // an involution
 __device__ inline float wave_min_ordered(float x) {
   int v = order_key(__float_as_int(x));
@@ -216,10 +216,9 @@ __device__ inline float wave_min_ordered(float x) {
   v = min(v, dppi<0x124>(v));
   v = min(v, dppi<0x122>(v));
   v = min(v, dppi<0x121>(v));
-  auto a = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
-  v = min((int)a[0], (int)a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
-  return __int_as_float(order_key(min((int)b[0], (int)b[1])));
+  v = min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x142, 0xA, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x143, 0xC, 0xF, false));
+  return __int_as_float(order_key(__builtin_amdgcn_readlane(v, 63)));
 }
 // Lowest (loss, code) over the wave in float64 (exact re-scoring).
 __device__ inline void wave_argmin_d(double& L, int& k) {
@@ -789,22 +788,82 @@ __device__ inline float e2m1_valf(int c) {
   return c <= 4 ? 0.5f * (float)c : (c == 5 ? 3.0f : (c == 6 ? 4.0f : 6.0f));
 }
 
-// Diagonal form.  Every candidate is scored with the fp32 quotient and the gfx950 FP4 converts.
-// No midpoint correction is needed here: at a rounding midpoint both neighbours are equally far,
-// so a quotient on the wrong side by its rounding error (|r' - r| <= 2^-23 r) changes that
-// element's e^2 by at most 4 (m / h) 2^-23 <= 28 * 2^-23 of itself (m a midpoint, h the half
-// spacing around it); with the fp32 arithmetic (under 19 * 2^-24) every L_k is within 5e-6 of
-// its exact value, inside the filter's 2^-16 bound.  Only the winner's nibbles and loss are then
-// recomputed with exact rounding decisions.
+// Diagonal form.  The loss L_k = sum_j Imp_j e_j^2 is scored in a weighted frame: with
+// a_j = sqrt(Imp_j) (float64 root rounded to fp32), t_kj = s_k a_j and u_j = w_j a_j, a lane forms
+// e'_j = fma(q_j, t_kj, -u_j) ~ a_j e_j and L'_k = sum_j e'_j^2 (two VALU operations per element
+// and candidate after the quantization).  Error bound, with delta = 2^-24 and W = sum_j Imp_j w_j^2:
+//  * quantization: a quotient r' = w (1/s) on the wrong side of an E2M1 midpoint by its rounding
+//    error (|r' - r| <= 2^-23 r) picks the other neighbour, which changes that element's e^2 by at
+//    most 4 (m/h) 2^-23 <= 56 delta of itself (m a midpoint, h the half spacing around it), so
+//    the loss L of the codes the converts pick lies in [L*, (1 + 56 delta) L*], L* the exact one;
+//  * arithmetic: q t - u = a (e + eta) with |eta| <= delta (|q| s + |w|) <= delta (2|w| + |e|)
+//    (|q s| <= |w| + |e| and |e| <= |w|: 0 is on the grid), so with the roundings of a, of the fma
+//    and of the 16-term sum, |L' - L| <= 22 delta L + 4 delta sqrt(L W) + 9 delta^2 W; moving
+//    from L to L' on the right costs under 2% plus 400 delta^2 W.
+// Hence L* lies within B(L') = C1 L' + C2 sqrt(L' W) + C3 W of L' (C1 = 2^-17 >= 80 delta,
+// C2 = 2^-21 >= 4.1 delta, C3 = 2^-38), provided nothing overflows or leaves the normal range:
+// the filter runs only for 2^-100 <= g <= 2^100, 448 g max_j a_j <= 2^120 and, per row,
+// 2^-100 <= W <= 2^100 (then |e'| <= 3 |u| and L' stays finite; underflowed products are covered
+// by C3 W); other rows go to the float64 kernel.  The square root is linearized once per wave:
+// for any lam > 0, C2 sqrt(L' W) <= C2/2 (lam L' + W/lam), so B(L') <= alpha L' + beta with
+// alpha = C1 + C2 lam/2 and beta = (C2/(2 lam) + C3) W; lam = sqrt(W/m) from the first row's
+// lowest L' makes the line tangent where it matters.  U = (1 + alpha) min L' + beta bounds the
+// exact minimum from above, and only candidates with (1 - alpha) L' - beta <= U can be the
+// argmin (the tests are written so a NaN or infinite L' counts as a contender).  Only the
+// winner's nibbles and loss are then recomputed with exact rounding decisions.
+//
+// Candidate pairs: a lane scores two codes that share one E4M3 mantissa, so s_b = 2^p s_a exactly
+// and one quotient w (1/s_a) serves both: the FP4 convert divides it by 2^p through its
+// exponent-only scale operand, exactly.  Lanes 7..61 hold codes (l+1, l+65) (p = 8); the
+// subnormal codes 1..7 and codes 63..71 are paired by hand.  Four mantissa classes hold an odd
+// number of codes, so one code (69) is left without a partner: it is scored in a separate pass
+// over the wave's rows and its loss stands in lane 5's second slot.  Lanes 6 and 63 hold one code.
+constexpr float kDiagC1 = 0x1p-17f;
+constexpr float kDiagC2h = 0x1p-22f;      // C2 / 2
+constexpr float kDiagC3 = 0x1p-38f;
+constexpr int kDiagLoneCode = 69;
+constexpr int kDiagLoneLane = 5;
+
+struct DiagPair {
+  int k0, k1;        // codes of the two slots (k1 = 0: no second code)
+  float sc1;         // s_k1 / s_k0, a power of two
+};
+__device__ inline DiagPair diag_pair(int lane) {
+  switch (lane) {
+    case 0: return {1, 2, 2.0f};
+    case 1: return {3, 6, 2.0f};
+    case 2: return {5, 66, 256.0f};
+    case 3: return {7, 70, 256.0f};
+    case 4: return {4, 64, 256.0f};
+    case 5: return {65, kDiagLoneCode, 1.0f};   // second slot: the separate pass
+    case 6: return {67, 0, 1.0f};
+    case 62: return {63, 71, 2.0f};
+    case 63: return {68, 0, 1.0f};
+    default: return {lane + 1, lane + 65, 256.0f};
+  }
+}
+
+// A wave-uniform float kept in a scalar register.
+__device__ inline float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+
+// 6 waves per SIMD (80 registers; a few values outside the row loop go to scratch) measured
+// about 1% faster than 5 waves without the cap.
 template <bool BF16>
-__global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_sweep_diag(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ imp, uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
     float* __restrict__ loss) {
-  __shared__ __attribute__((aligned(16))) float wt_all[kWaves][kRowsPerWave][16];
+  __shared__ __attribute__((aligned(16))) float wt_all[kWaves][kRowsPerWave][16];   // w (+0 for -0)
+  __shared__ __attribute__((aligned(16))) float ut_all[kWaves][kRowsPerWave][16];   // w a
+  __shared__ __attribute__((aligned(16))) float sa_all[kWaves][16];                 // a = sqrt(Imp)
   __shared__ float im_all[kWaves][16];
-  __shared__ float win_s[kWaves][kRowsPerWave];   // winner's scale per row (0: no winner here)
-  __shared__ int win_k[kWaves][kRowsPerWave];
+  __shared__ float wr_all[kWaves][kRowsPerWave];      // W of the row (-1: not filtered)
+  __shared__ float lone_all[kWaves][kRowsPerWave];    // L' of the unpaired code
+  __shared__ float win_s[kWaves][kRowsPerWave];       // winner's scale per row
+  __shared__ int win_k[kWaves][kRowsPerWave];         // winner's code per row (0: no winner)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = cin / 16;
   const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
@@ -812,159 +871,260 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag(
   const int64_t c_begin = (int64_t)blockIdx.y * kRowsPerWave;
   if (n >= nb || c_begin >= cout) return;
   const int64_t c_end = min(cout, c_begin + kRowsPerWave);
+  const int nrows = (int)(c_end - c_begin);
 
-  // The wave's 32 blocks (rows c_begin.., column n) come in with one coalesced load per lane
-  // (lane l: row l/2, elements 8*(l%2)..+7) and wait in LDS as fp32.
-  float (*wt)[16] = wt_all[wave];
-  {
-    const int rr = lane >> 1, h = lane & 1;
-    const int64_t c = c_begin + rr;
-    const int64_t e0 = (g * cout + min(c, c_end - 1)) * cin + n * 16 + 8 * h;
-    float v[8];
-    if (BF16) {
-      const v4u u = *(const v4u*)((const unsigned short*)W + e0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(u[q] << 16);
-        v[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
-      }
-    } else {
-      const v4f u0 = *(const v4f*)((const float*)W + e0), u1 = *(const v4f*)((const float*)W + e0 + 4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { v[q] = u0[q]; v[4 + q] = u1[q]; }
-    }
-    *(v4f*)&wt[rr][8 * h] = v4f{v[0], v[1], v[2], v[3]};
-    *(v4f*)&wt[rr][8 * h + 4] = v4f{v[4], v[5], v[6], v[7]};
-  }
-  float im[16];
+  // importance of the block column (all ones when it sums to zero), a_j = sqrt(Imp_j)
+  const float* ip = imp + g * cin + n * 16;
   double isum = 0.0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    im[j] = imp[g * cin + n * 16 + j];
-    isum += (double)im[j];
+  for (int j = 0; j < 16; ++j) isum += (double)ip[j];
+  if (lane < 16) {
+    const float v = isum == 0.0 ? 1.0f : ip[lane];
+    im_all[wave][lane] = v;
+    sa_all[wave][lane] = (float)sqrt((double)v);
   }
-  if (isum == 0.0) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) im[j] = 1.0f;
-  }
-  if (lane < 16) im_all[wave][lane] = im[lane & 15];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  const float gsc = global_scale(amax[g]);
-  const bool fast = filter_ok(gsc);
-  const int k0 = lane + 1, k1 = lane + 65;
-  const bool v1 = k1 <= 126;
-  const float s0 = cand_scale(k0, gsc), s1 = cand_scale(v1 ? k1 : 126, gsc);
-  const float is0 = inv_scale(s0), is1 = inv_scale(s1);
+  const float gsc = uniform(global_scale(amax[g]));
+  float a[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v4f t = *(const v4f*)&sa_all[wave][4 * q];
+    a[4 * q] = t[0]; a[4 * q + 1] = t[1]; a[4 * q + 2] = t[2]; a[4 * q + 3] = t[3];
+  }
+  float amx = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) amx = fmaxf(amx, a[j]);
+  const bool fast = filter_ok(gsc) && 448.0 * (double)gsc * (double)amx <= 0x1p120;
 
-  unsigned pkc = 0u;                              // FP4 pack register carried between uses
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    const int64_t oblk = (g * cout + c) * nb + n;
-    const int rr = (int)(c - c_begin);
-    if (!fast) {
+  const DiagPair pr = diag_pair(lane);
+  const bool lone = lane == kDiagLoneLane, single = pr.k1 == 0;
+  const float s0 = cand_scale(pr.k0, gsc), s1 = cand_scale(single ? pr.k0 : pr.k1, gsc);
+  const float is0 = inv_scale(s0), sc1 = pr.sc1;
+  const float sl = uniform(cand_scale(kDiagLoneCode, gsc)), isl = uniform(inv_scale(sl));
+  // t_k1,j = sc1 t_k0,j exactly; the second slot's grid values come back from the convert
+  // already multiplied by sc1, so one set of products serves both slots
+  float t0[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t0[j] = s0 * a[j];
+
+  bool have_line = false;                         // alpha, beta set from the first filtered row
+  float oma = 0.0f, A1 = 0.0f, K2 = 0.0f;
+  unsigned pkc[4] = {0u, 0u, 0u, 0u};             // FP4 pack registers carried between rows
+  float (*wt)[16] = wt_all[wave];
+  float (*ut)[16] = ut_all[wave];
+
+  {
+    const int sub = lane & 7, el0 = 2 * sub, el1 = el0 + 1;
+
+    // The wave's 32 blocks (rows c_begin.., column n) come in with one coalesced load per lane (lane l: row
+    // l/2, elements 8*(l%2)..+7) and wait in LDS as w and w a, with the row's W; the same lane
+    // scores the unpaired code over its 8 elements.
+    {
+      const int rr = lane >> 1, h = lane & 1;
+      const int64_t c = c_begin + rr;
+      const int64_t e0 = (g * cout + min(c, c_end - 1)) * cin + n * 16 + 8 * h;
+      float v[8];
+      if (BF16) {
+        const v4u u = *(const v4u*)((const unsigned short*)W + e0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = __uint_as_float(u[q] << 16) + 0.0f;           // + 0 turns -0 into +0
+          v[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u) + 0.0f;
+        }
+      } else {
+        const v4f u0 = *(const v4f*)((const float*)W + e0), u1 = *(const v4f*)((const float*)W + e0 + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { v[q] = u0[q] + 0.0f; v[4 + q] = u1[q] + 0.0f; }
+      }
+      const v4f a0 = *(const v4f*)&sa_all[wave][8 * h], a1 = *(const v4f*)&sa_all[wave][8 * h + 4];
+      const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      float uv[8];
+      float wp = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uv[q] = v[q] * av[q];
+        wp = fmaf(uv[q], uv[q], wp);
+      }
+      *(v4f*)&wt[rr][8 * h] = v4f{v[0], v[1], v[2], v[3]};
+      *(v4f*)&wt[rr][8 * h + 4] = v4f{v[4], v[5], v[6], v[7]};
+      *(v4f*)&ut[rr][8 * h] = v4f{uv[0], uv[1], uv[2], uv[3]};
+      *(v4f*)&ut[rr][8 * h + 4] = v4f{uv[4], uv[5], uv[6], uv[7]};
+      float lp = 0.0f;
+      unsigned pk = 0u;
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, v[q] * isl, v[q + 1] * isl, 1.0f, 0);
+        const v2f qq = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
+        const float ea = fmaf(qq[0], sl * av[q], -uv[q]), eb = fmaf(qq[1], sl * av[q + 1], -uv[q + 1]);
+        lp = fmaf(ea, ea, lp);
+        lp = fmaf(eb, eb, lp);
+      }
+      const float wrow = wp + __shfl_xor(wp, 1, 64);
+      lp += __shfl_xor(lp, 1, 64);
+      if (h == 0) {
+        wr_all[wave][rr] = (wrow >= 0x1p-100f && wrow <= 0x1p+100f) ? wrow : -1.0f;
+        lone_all[wave][rr] = lp;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    for (int rr = 0; rr < nrows; ++rr) {
+      const int64_t oblk = (g * cout + c_begin + rr) * nb + n;
+      const float wrow = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wr_all[wave][rr])));
+      if (!fast || !(wrow >= 0.0f)) {
+        if (lane == 0) {
+          code[oblk] = 0;                         // resolved by the float64 pass
+          win_k[wave][rr] = 0;
+          win_s[wave][rr] = 1.0f;
+        }
+        continue;
+      }
+      float w[16], u[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f t = *(const v4f*)&wt[rr][4 * q];
+        const v4f z = *(const v4f*)&ut[rr][4 * q];
+        w[4 * q] = t[0]; w[4 * q + 1] = t[1]; w[4 * q + 2] = t[2]; w[4 * q + 3] = t[3];
+        u[4 * q] = z[0]; u[4 * q + 1] = z[1]; u[4 * q + 2] = z[2]; u[4 * q + 3] = z[3];
+      }
+      float L0 = 0.0f, L1 = 0.0f;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        // elements 4 j4..+3: bytes 0/1 hold the first pair for the two slots, bytes 2/3 the
+        // second; all four bytes are rewritten before they are read
+        const int j = 4 * j4;
+        const float x0 = w[j] * is0, x1 = w[j + 1] * is0, x2 = w[j + 2] * is0, x3 = w[j + 3] * is0;
+        unsigned pk = pkc[j4];
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, x0, x1, 1.0f, 0);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, x0, x1, sc1, 1);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, x2, x3, 1.0f, 2);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, x2, x3, sc1, 3);
+        pkc[j4] = pk;
+        const v2f qa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
+        const v2f qb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc1, 1);
+        const v2f qc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 2);
+        const v2f qd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc1, 3);
+        const float ea0 = fmaf(qa[0], t0[j], -u[j]), ea1 = fmaf(qa[1], t0[j + 1], -u[j + 1]);
+        const float eb0 = fmaf(qb[0], t0[j], -u[j]), eb1 = fmaf(qb[1], t0[j + 1], -u[j + 1]);
+        const float ec0 = fmaf(qc[0], t0[j + 2], -u[j + 2]), ec1 = fmaf(qc[1], t0[j + 3], -u[j + 3]);
+        const float ed0 = fmaf(qd[0], t0[j + 2], -u[j + 2]), ed1 = fmaf(qd[1], t0[j + 3], -u[j + 3]);
+        L0 = fmaf(ea0, ea0, L0);
+        L0 = fmaf(ea1, ea1, L0);
+        L1 = fmaf(eb0, eb0, L1);
+        L1 = fmaf(eb1, eb1, L1);
+        L0 = fmaf(ec0, ec0, L0);
+        L0 = fmaf(ec1, ec1, L0);
+        L1 = fmaf(ed0, ed0, L1);
+        L1 = fmaf(ed1, ed1, L1);
+      }
+      const float lone_L = lone_all[wave][rr];
+      L1 = single ? __builtin_inff() : (lone ? lone_L : L1);
+      const float m = wave_min_nonneg(L1 < L0 ? L1 : L0);
+      if (!have_line) {
+        // lam = sqrt(W/m), kept within [1, 4096]; any lam > 0 gives a valid line.  The factors
+        // (1 + 2^-18) cover the roundings of alpha and beta, (1 + 2^-16) those of W and the test.
+        const float mm = m > wrow * 0x1p-40f ? m : wrow * 0x1p-40f;
+        const float lam = fminf(fmaxf(__builtin_amdgcn_rsqf(mm / wrow), 1.0f), 4096.0f);
+        const float alpha = fmaf(kDiagC2h, lam, kDiagC1) * (1.0f + 0x1p-18f);
+        const float bet = fmaf(kDiagC2h * (1.0f + 0x1p-18f), 1.0f / lam, kDiagC3);
+        oma = uniform(1.0f - alpha);
+        A1 = uniform((1.0f + alpha) * (1.0f + 0x1p-16f));
+        K2 = uniform(2.0f * bet * (1.0f + 0x1p-16f));
+        have_line = true;
+      }
+      // U + beta; the exact argmin is among the slots with (1 - alpha) L' <= (1 + alpha) m + 2 beta
+      const float rhs = fmaf(A1, m, K2 * wrow);
+      const unsigned long long M0 = __ballot(!(L0 * oma > rhs)), M1 = __ballot(!(L1 * oma > rhs));
+      const int cnt = __popcll(M0) + __popcll(M1);
+      int kwin = 0;
+      float sw = 1.0f;
+      if (cnt == 1) {
+        const bool in0 = M0 != 0ull;
+        const int b = (int)__builtin_ctzll(in0 ? M0 : M1);
+        const DiagPair pb = diag_pair(b);
+        kwin = in0 ? pb.k0 : pb.k1;
+        sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in0 ? s0 : s1), b));
+      } else if (cnt > 1 && cnt <= 4) {
+        // 2..4 contenders: exact float64 losses, one contender per 16 lanes (lane: element l%16)
+        unsigned long long ma = M0, mb = M1;
+        auto next = [&]() -> int {
+          if (ma) { const int bb = __builtin_ctzll(ma); ma &= ma - 1; return diag_pair(bb).k0; }
+          if (mb) { const int bb = __builtin_ctzll(mb); mb &= mb - 1; return diag_pair(bb).k1; }
+          return 0;
+        };
+        const int kc0 = next(), kc1 = next(), kc2 = next(), kc3 = next();
+        const int q = lane >> 4, j = lane & 15;
+        const int my_k = q == 0 ? kc0 : (q == 1 ? kc1 : (q == 2 ? kc2 : kc3));
+        int nib;
+        const double e = exact_err(wt[rr][j], cand_scale(my_k > 0 ? my_k : 1, gsc), &nib);
+        double z = (double)im_all[wave][j] * e * e;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+        double bestD = __builtin_inf();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kr = r == 0 ? kc0 : (r == 1 ? kc1 : (r == 2 ? kc2 : kc3));
+          const double Lr = __shfl(z, 16 * r, 64);
+          if (kr > 0 && (Lr < bestD || (Lr == bestD && kr < kwin))) { bestD = Lr; kwin = kr; }
+        }
+        sw = cand_scale(kwin, gsc);
+      }
       if (lane == 0) {
-        code[oblk] = 0;                           // resolved by the float64 pass
-        win_k[wave][rr] = 0;
-      }
-      continue;
-    }
-    float w[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const v4f t = *(const v4f*)&wt[rr][4 * q];
-      w[4 * q] = t[0]; w[4 * q + 1] = t[1]; w[4 * q + 2] = t[2]; w[4 * q + 3] = t[3];
-    }
-    float L0 = 0.0f, L1 = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      // bytes 0 and 1 are written and read; the other bytes of the carried register never are
-      pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, w[j] * is0, w[j + 1] * is0, 1.0f, 0);
-      pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, w[j] * is1, w[j + 1] * is1, 1.0f, 1);
-      const unsigned pk = pkc;
-      const v2f qa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
-      const v2f qb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 1);
-      const float ea0 = fmaf(qa[0], s0, -w[j]), ea1 = fmaf(qa[1], s0, -w[j + 1]);
-      const float eb0 = fmaf(qb[0], s1, -w[j]), eb1 = fmaf(qb[1], s1, -w[j + 1]);
-      L0 = fmaf(im[j] * ea0, ea0, L0);
-      L0 = fmaf(im[j + 1] * ea1, ea1, L0);
-      L1 = fmaf(im[j] * eb0, eb0, L1);
-      L1 = fmaf(im[j + 1] * eb1, eb1, L1);
-    }
-    if (!v1) L1 = __builtin_inff();
-    // Exact losses lie in [L(1-c), L(1+c)]; U = (1+c) min L bounds the minimum from above, and
-    // only candidates with L(1-c) <= U can be the argmin (losses are sums of Imp e^2 >= 0).
-    const float U = wave_min_nonneg(L1 < L0 ? L1 : L0) * (1.0f + kErrC);
-    const unsigned long long M0 = __ballot(L0 * (1.0f - kErrC) <= U), M1 = __ballot(L1 * (1.0f - kErrC) <= U);
-    const int cnt = __popcll(M0) + __popcll(M1);
-    int kwin = M0 ? (int)__builtin_ctzll(M0) + 1 : (int)__builtin_ctzll(M1) + 65;
-    if (cnt > 1 && cnt <= 4) {
-      // 2..4 contenders: exact float64 losses, one contender per 16 lanes (lane: element l%16)
-      unsigned long long ma = M0, mb = M1;
-      auto next = [&]() -> int {
-        if (ma) { const int bb = __builtin_ctzll(ma); ma &= ma - 1; return bb + 1; }
-        if (mb) { const int bb = __builtin_ctzll(mb); mb &= mb - 1; return bb + 65; }
-        return 0;
-      };
-      const int kc0 = next(), kc1 = next(), kc2 = next(), kc3 = next();
-      const int q = lane >> 4, j = lane & 15;
-      const int my_k = q == 0 ? kc0 : (q == 1 ? kc1 : (q == 2 ? kc2 : kc3));
-      int nib;
-      const double e = exact_err(wt[rr][j], cand_scale(my_k > 0 ? my_k : 1, gsc), &nib);
-      double z = (double)im_all[wave][j] * e * e;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
-      double bestD = __builtin_inf();
-      kwin = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kr = r == 0 ? kc0 : (r == 1 ? kc1 : (r == 2 ? kc2 : kc3));
-        const double Lr = __shfl(z, 16 * r, 64);
-        if (kr > 0 && (Lr < bestD || (Lr == bestD && kr < kwin))) { bestD = Lr; kwin = kr; }
+        const bool decided = cnt >= 1 && cnt <= 4;
+        if (!decided) code[oblk] = 0;             // many contenders (or none): float64 pass
+        win_k[wave][rr] = decided ? kwin : 0;
+        win_s[wave][rr] = sw;
       }
     }
-    const int wl = (kwin - 1) & 63;               // the lane that holds code kwin
-    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kwin <= 64 ? s0 : s1), wl));
-    if (lane == 0) {
-      const bool decided = cnt >= 1 && cnt <= 4;
-      if (!decided) code[oblk] = 0;               // many contenders (or none): float64 pass
-      win_k[wave][rr] = decided ? kwin : 0;
-      win_s[wave][rr] = sw;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // exact nibbles and loss of every row's winner, eight rows at a time: lane l takes row
-  // 8*pass + l/8 and its elements 2*(l%8), 2*(l%8)+1
-  const int sub = lane & 7, el0 = 2 * sub, el1 = el0 + 1;
-  const float ima = im_all[wave][el0], imb = im_all[wave][el1];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // Exact nibbles and loss of every row's winner, eight rows at a time: lane l takes row
+    // 8*pass + l/8 and its elements 2*(l%8), 2*(l%8)+1.  The hardware reciprocal is within one
+    // ulp, so |w| (1/s)(1 -+ 2^-19) fall strictly below and above the exact quotient |w|/s; the
+    // FP4 convert is monotone in its input, so when the two give the same code that is the exact
+    // rounding (an exact midpoint gives two different codes).  Otherwise the element is within
+    // about 2^-18 of a midpoint and the sign of fma(m, s, -|w|) decides each midpoint.
 #pragma unroll
-  for (int pass = 0; pass < kRowsPerWave / 8; ++pass) {
-    const int rr = 8 * pass + (lane >> 3);
-    const int64_t c = c_begin + rr;
-    const bool row_on = c < c_end;
-    const int kw = row_on ? win_k[wave][rr] : 0;
-    const float sw = row_on ? win_s[wave][rr] : 1.0f;
-    const float wa = wt[rr][el0], wb = wt[rr][el1];
-    const int ca = e2m1_index_fma(fabsf(wa), sw), cb = e2m1_index_fma(fabsf(wb), sw);
-    const float qa = e2m1_valf(ca), qb = e2m1_valf(cb);
-    const float ea = fmaf(wa < 0.0f ? -qa : qa, sw, -wa), eb = fmaf(wb < 0.0f ? -qb : qb, sw, -wb);
-    float part = fmaf(imb * eb, eb, ima * ea * ea);
-    part += __shfl_xor(part, 1, 64);
-    part += __shfl_xor(part, 2, 64);
-    part += __shfl_xor(part, 4, 64);
-    if (kw != 0) {
-      if (fp4) {
-        const unsigned byte = (unsigned)(ca | (wa < 0.0f ? 8 : 0)) | ((unsigned)(cb | (wb < 0.0f ? 8 : 0)) << 4);
-        fp4[(g * cout + c) * (cin / 2) + n * 8 + sub] = (uint8_t)byte;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rr = 8 * pass + (lane >> 3);
+      const int64_t c = c_begin + rr;
+      const bool row_on = rr < nrows;
+      const int kw = row_on ? win_k[wave][rr] : 0;
+      const float sw = row_on ? win_s[wave][rr] : 1.0f;
+      const float wa = wt[rr][el0], wb = wt[rr][el1];
+      const float ima = im_all[wave][el0], imb = im_all[wave][el1];
+      const float is = __builtin_amdgcn_rcpf(sw);
+      const float isp = is * (1.0f + 0x1p-19f), ism = is * (1.0f - 0x1p-19f);
+      unsigned byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, wa * isp, wb * isp, 1.0f, 0);
+      const unsigned blo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, wa * ism, wb * ism, 1.0f, 0);
+      if (byte != blo) {
+        const int ca = e2m1_index_fma(fabsf(wa), sw), cb = e2m1_index_fma(fabsf(wb), sw);
+        byte = (unsigned)(ca | (wa < 0.0f ? 8 : 0)) | ((unsigned)(cb | (wb < 0.0f ? 8 : 0)) << 4);
       }
-      if (sub == 0) {
-        code[(g * cout + c) * nb + n] = (uint8_t)kw;
-        if (loss) loss[(g * cout + c) * nb + n] = part;
+      const v2f qv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);   // signed grid values
+      const float ea = fmaf(qv[0], sw, -wa), eb = fmaf(qv[1], sw, -wb);
+      float part = fmaf(imb * eb, eb, ima * ea * ea);
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      part += __shfl_xor(part, 4, 64);
+      if (kw != 0) {
+        if (fp4) fp4[(g * cout + c) * (cin / 2) + n * 8 + sub] = (uint8_t)byte;
+        if (sub == 0) {
+          code[(g * cout + c) * nb + n] = (uint8_t)kw;
+          if (loss) loss[(g * cout + c) * nb + n] = part;
+        }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 

@@ -355,6 +355,63 @@ def test_sweep_power_of_two_fractions_of_amax(diag):
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
 
+def _every_code_weights(r, cout, cin):
+    """Blocks whose max |w| is 6 s_k (within 3%) for k cycling over all 126 codes, global amax 1:
+    the argmin lands on every code, the subnormal ones included."""
+    nb = cin // 16
+    s = oracle.candidate_scales(oracle.global_scale(np.float32(1.0)))
+    W = r.standard_normal((1, cout, nb, 16))
+    W /= np.abs(W).max(-1, keepdims=True)
+    k = (np.arange(cout * nb) % 126).reshape(cout, nb)
+    W *= (6.0 * s[k] * r.uniform(0.97, 1.03, (cout, nb)))[None, :, :, None]
+    W = W.reshape(1, cout, cin).astype(np.float32)
+    W[0, 0, 0] = 1.0
+    return W
+
+
+@pytest.mark.parametrize("diag", [False, True])
+def test_sweep_every_code_wins(diag):
+    """Each of the 126 E4M3 codes is the winner of some block (the oracle's choice), so every
+    lane and slot of the filter's candidate layout decides a winner at least once."""
+    r = np.random.default_rng(31)
+    cout, cin = 504, 64
+    W = _every_code_weights(r, cout, cin)
+    a = oracle.absmax(W.astype(np.float64)).astype(np.float32)
+    note(f"sweep every code wins, diag={diag}")
+    Wd, ad = torch.from_numpy(W).to(DEV), torch.from_numpy(a).to(DEV)
+    if diag:
+        imp = (np.abs(r.standard_normal((1, cin))) + 0.1).astype(np.float32)
+        code, fp4, loss = lh.lh_scale_sweep_diag(Wd, ad, torch.from_numpy(imp).to(DEV))
+        res = oracle.sweep_diag(W.astype(np.float64), a, imp)
+    else:
+        A = r.standard_normal((1, cin // 16, 16, 16)).astype(np.float32)
+        H = (np.einsum("gnij,gnkj->gnik", A, A) / 16 + 0.5 * np.eye(16)).astype(np.float32)
+        code, fp4, loss = lh.lh_scale_sweep(Wd, ad, torch.from_numpy(H).to(DEV))
+        res = oracle.sweep(W.astype(np.float64), a, H)
+    assert set(np.unique(res["code"]).tolist()) == set(range(1, 127))
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
+def test_sweep_diag_importance_and_weight_ranges():
+    """Rows outside the diagonal filter's range and wide importance spreads: tiny weights (the
+    row's sum Imp w^2 under 2^-100), huge importance (over 2^100), importance spanning 1e-30..1e30
+    inside a block, and importance with exact zeros.  All must give the oracle's argmin."""
+    r = np.random.default_rng(33)
+    G, cout, cin = 4, 40, 64
+    W = r.normal(0, 0.02, (G, cout, cin)).astype(np.float32)
+    W[0] *= np.float32(1e-25)
+    imp = (np.abs(r.standard_normal((G, cin))) + 0.1).astype(np.float32)
+    imp[1] *= np.float32(1e36)
+    imp[2] = (10.0 ** r.uniform(-30, 30, cin)).astype(np.float32)
+    imp[3, r.random(cin) < 0.25] = 0.0
+    a = oracle.absmax(W.astype(np.float64)).astype(np.float32)
+    note(f"diag sweep importance and weight ranges G={G} cout={cout} cin={cin}")
+    code, fp4, loss = lh.lh_scale_sweep_diag(torch.from_numpy(W).to(DEV), torch.from_numpy(a).to(DEV),
+                                             torch.from_numpy(imp).to(DEV))
+    res = oracle.sweep_diag(W.astype(np.float64), a, imp)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
 def test_sweep_deterministic():
     wl = synth.make("c2", cout=100, cin=64, rows=300)
     note("sweep determinism")
