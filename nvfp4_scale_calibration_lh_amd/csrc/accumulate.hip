@@ -532,6 +532,130 @@ __global__ __launch_bounds__(NW * 64) void k_acc_dense(
 }
 
 // ---------------------------------------------------------------------------------------------
+// Dense layer, importance alone (no H): every lane squares and adds the channels it loads, in
+// fp32 registers (the square of a bf16 value is exact in fp32), with no staging and no matrix
+// instructions; the lanes that share channels, then the waves, then the tiles are added in a
+// fixed order.  Grid (tiles, slices) and partial layout [slice][tile][64 channels] as above.
+// ---------------------------------------------------------------------------------------------
+template <bool BF16, int NW>
+__global__ __launch_bounds__(NW * 64) void k_imp_dense(const void* __restrict__ Xv, int64_t rows,
+                                                        int64_t cin, int64_t R, float beta,
+                                                        float* __restrict__ imp, float* __restrict__ ws,
+                                                        unsigned* __restrict__ counters) {
+  using Gm = Geo<BF16>;
+  constexpr int kVals = BF16 ? 8 : 4;            // channels per lane (one 16-byte load per row)
+  __shared__ float comb[NW][kCh];
+  __shared__ int last_tile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t tiles = gridDim.x, tile = blockIdx.x, slice = blockIdx.y;
+  const int64_t ch0 = slice * kCh;
+  const int64_t t0 = tile * R, t1 = min(rows, t0 + R);
+  const int lrow = BF16 ? (lane >> 3) : (lane >> 4);
+  const int lcol = BF16 ? (lane & 7) * 8 : (lane & 15) * 4;
+  const bool col_on = ch0 + lcol < cin;
+  const char* X = (const char*)Xv;
+  const int nchunks = t1 > t0 ? (int)((t1 - t0 + kChunk - 1) / kChunk) : 0;
+  float acc[kVals];
+#pragma unroll
+  for (int e = 0; e < kVals; ++e) acc[e] = 0.0f;
+  // Every lane issues the same loads on every path (rows past the range re-read its last row and
+  // are not added; channels past cin read channel 0 and land in channels that are not written).
+  auto issue = [&](v4u (&p)[Gm::kLoads], int j) {
+#pragma unroll
+    for (int q = 0; q < Gm::kLoads; ++q) {
+      const int64_t r = min(t0 + (int64_t)j * kChunk + lrow + q * Gm::kRowsPerLoad, t1 - 1);
+      const int64_t byte = (r * cin + (col_on ? ch0 + lcol : 0)) * (BF16 ? 2 : 4);
+      p[q] = __builtin_nontemporal_load((const v4u*)(X + byte));
+    }
+  };
+  auto add = [&](const v4u (&p)[Gm::kLoads], int j) {
+    const int64_t c0 = t0 + (int64_t)j * kChunk;
+    const bool full = c0 + kChunk <= t1;
+#pragma unroll
+    for (int q = 0; q < Gm::kLoads; ++q) {
+      const float f = (full || c0 + lrow + q * Gm::kRowsPerLoad < t1) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (BF16) {
+          const float lo = __uint_as_float(p[q][u] << 16), hi = __uint_as_float(p[q][u] & 0xFFFF0000u);
+          if (full) {
+            acc[2 * u] = fmaf(lo, lo, acc[2 * u]);
+            acc[2 * u + 1] = fmaf(hi, hi, acc[2 * u + 1]);
+          } else {
+            acc[2 * u] = fmaf(lo * f, lo, acc[2 * u]);
+            acc[2 * u + 1] = fmaf(hi * f, hi, acc[2 * u + 1]);
+          }
+        } else {
+          const float x = __uint_as_float(p[q][u]);
+          acc[u] = full ? fmaf(x, x, acc[u]) : fmaf(x * f, x, acc[u]);
+        }
+      }
+    }
+  };
+  // two register sets: a chunk's loads complete, the next chunk's are issued, then the chunk is
+  // added while they are in flight (the empty asm takes the loaded registers, so the wait for
+  // them comes before the next issue and never covers it)
+  auto ready = [](const v4u (&p)[Gm::kLoads]) {
+#pragma unroll
+    for (int q = 0; q < Gm::kLoads; ++q) asm volatile("" : : "v"(p[q]));
+  };
+  v4u pa[Gm::kLoads], pb[Gm::kLoads];
+  int j = wave;
+  if (j < nchunks) issue(pa, j);
+  while (j < nchunks) {
+    ready(pa);
+    if (j + NW < nchunks) issue(pb, j + NW);
+    add(pa, j);
+    j += NW;
+    if (j >= nchunks) break;
+    ready(pb);
+    if (j + NW < nchunks) issue(pa, j + NW);
+    add(pb, j);
+    j += NW;
+  }
+  // lanes with the same channels: bf16 lanes l, l+8, .., l+56; fp32 lanes l, l+16, l+32, l+48
+#pragma unroll
+  for (int o = BF16 ? 8 : 16; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < kVals; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  if (lrow == 0)
+#pragma unroll
+    for (int e = 0; e < kVals; ++e) comb[wave][lcol + e] = acc[e];
+  __syncthreads();
+  float tot = 0.0f;
+  if (wave == 0)
+#pragma unroll
+    for (int v = 0; v < NW; ++v) tot += comb[v][lane];          // wave order
+  const int64_t ch = ch0 + lane;
+  if (tiles == 1) {
+    if (wave == 0 && ch < cin) imp[ch] = beta != 0.0f ? beta * imp[ch] + tot : tot;
+    return;
+  }
+  // several tiles: each stores its sums; the slice's last tile to finish adds all of them in
+  // tile order and writes the outputs
+  float* part = ws + slice * tiles * kCh;
+  if (wave == 0) {
+    st_agent(part + tile * kCh + lane, tot);
+    __builtin_amdgcn_s_waitcnt(0);            // the partial stores have completed
+    if (lane == 0) last_tile = arrive(&counters[slice]) == (unsigned)(tiles - 1);
+  }
+  __syncthreads();
+  if (!last_tile || wave != 0) return;
+  float s = 0.0f;
+  int64_t t = 0;
+  for (; t + 8 <= tiles; t += 8) {
+    float p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = ld_agent(part + (t + u) * kCh + lane);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += p[u];
+  }
+  for (; t < tiles; ++t) s += ld_agent(part + t * kCh + lane);
+  if (ch < cin) imp[ch] = beta != 0.0f ? beta * imp[ch] + s : s;
+  if (lane == 0) clear(&counters[slice]);
+}
+
+// ---------------------------------------------------------------------------------------------
 // Grouped rows: planning.  One workgroup cuts every group into pieces of at most R rows and
 // writes the piece table: word 0 = number of pieces; entry p (at 4 + 4p) = {group, first row,
 // end row, piece index in group << 32 | pieces in group}, pieces of one group consecutive; then,
@@ -695,6 +819,11 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
     constexpr int NW = dense_waves(BF16, DIAG, ACT);
     const int64_t R = dense_tile_rows(rows, nb, BF16, DIAG, ACT);
     const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
+    if constexpr (DIAG && !ACT) {
+      hipLaunchKernelGGL((k_imp_dense<BF16, NW>), dim3((unsigned)tiles, (unsigned)slices), dim3(NW * 64), 0,
+                         stream, X, rows, cin, R, beta, imp, (float*)work, counters);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG, NW, FQ>), dim3((unsigned)tiles, (unsigned)slices),
                        dim3(NW * 64), 0, stream, X, Xq, x_amax, rows, cin, R, beta, H, P, imp,
                        (float*)work, counters, nb);
