@@ -862,7 +862,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
   __shared__ float im_all[kWaves][16];
   __shared__ float wr_all[kWaves][kRowsPerWave];      // W of the row (-1: not filtered)
   __shared__ float lone_all[kWaves][kRowsPerWave];    // L' of the unpaired code
-  __shared__ float win_s[kWaves][kRowsPerWave];       // winner's scale per row
   __shared__ int win_k[kWaves][kRowsPerWave];         // winner's code per row (0: no winner)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = cin / 16;
@@ -901,8 +900,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
 
   const DiagPair pr = diag_pair(lane);
   const bool lone = lane == kDiagLoneLane, single = pr.k1 == 0;
-  const float s0 = cand_scale(pr.k0, gsc), s1 = cand_scale(single ? pr.k0 : pr.k1, gsc);
-  const float is0 = inv_scale(s0), sc1 = pr.sc1;
+  const float s0 = cand_scale(pr.k0, gsc), is0 = inv_scale(s0), sc1 = pr.sc1;
   const float sl = uniform(cand_scale(kDiagLoneCode, gsc)), isl = uniform(inv_scale(sl));
   // t_k1,j = sc1 t_k0,j exactly; the second slot's grid values come back from the convert
   // already multiplied by sc1, so one set of products serves both slots
@@ -911,7 +909,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
   for (int j = 0; j < 16; ++j) t0[j] = s0 * a[j];
 
   bool have_line = false;                         // alpha, beta set from the first filtered row
-  float oma = 0.0f, A1 = 0.0f, K2 = 0.0f;
+  float A1 = 0.0f, K2 = 0.0f;
   unsigned pkc[4] = {0u, 0u, 0u, 0u};             // FP4 pack registers carried between rows
   float (*wt)[16] = wt_all[wave];
   float (*ut)[16] = ut_all[wave];
@@ -980,7 +978,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
         if (lane == 0) {
           code[oblk] = 0;                         // resolved by the float64 pass
           win_k[wave][rr] = 0;
-          win_s[wave][rr] = 1.0f;
         }
         continue;
       }
@@ -1024,31 +1021,32 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
       }
       const float lone_L = lone_all[wave][rr];
       L1 = single ? __builtin_inff() : (lone ? lone_L : L1);
-      const float m = wave_min_nonneg(L1 < L0 ? L1 : L0);
+      // losses are >= 0 or +inf, ordered like their bit patterns
+      const float m = wave_min_nonneg(__uint_as_float(min(__float_as_uint(L0), __float_as_uint(L1))));
       if (!have_line) {
         // lam = sqrt(W/m), kept within [1, 4096]; any lam > 0 gives a valid line.  The factors
-        // (1 + 2^-18) cover the roundings of alpha and beta, (1 + 2^-16) those of W and the test.
+        // (1 + 2^-18) cover the roundings of alpha and beta, (1 + 2^-16) those of W, of the
+        // division by 1 - alpha folded into A1 and K2, and of the test.
         const float mm = m > wrow * 0x1p-40f ? m : wrow * 0x1p-40f;
         const float lam = fminf(fmaxf(__builtin_amdgcn_rsqf(mm / wrow), 1.0f), 4096.0f);
         const float alpha = fmaf(kDiagC2h, lam, kDiagC1) * (1.0f + 0x1p-18f);
         const float bet = fmaf(kDiagC2h * (1.0f + 0x1p-18f), 1.0f / lam, kDiagC3);
-        oma = uniform(1.0f - alpha);
-        A1 = uniform((1.0f + alpha) * (1.0f + 0x1p-16f));
-        K2 = uniform(2.0f * bet * (1.0f + 0x1p-16f));
+        const float ioma = 1.0f / (1.0f - alpha);
+        A1 = uniform((1.0f + alpha) * ioma * (1.0f + 0x1p-16f));
+        K2 = uniform(2.0f * bet * ioma * (1.0f + 0x1p-16f));
         have_line = true;
       }
-      // U + beta; the exact argmin is among the slots with (1 - alpha) L' <= (1 + alpha) m + 2 beta
+      // the exact argmin is among the slots with (1 - alpha) L' - beta <= U = (1 + alpha) m + beta,
+      // i.e. L' <= ((1 + alpha) m + 2 beta) / (1 - alpha)
       const float rhs = fmaf(A1, m, K2 * wrow);
-      const unsigned long long M0 = __ballot(!(L0 * oma > rhs)), M1 = __ballot(!(L1 * oma > rhs));
+      const unsigned long long M0 = __ballot(!(L0 > rhs)), M1 = __ballot(!(L1 > rhs));
       const int cnt = __popcll(M0) + __popcll(M1);
       int kwin = 0;
-      float sw = 1.0f;
       if (cnt == 1) {
         const bool in0 = M0 != 0ull;
         const int b = (int)__builtin_ctzll(in0 ? M0 : M1);
         const DiagPair pb = diag_pair(b);
         kwin = in0 ? pb.k0 : pb.k1;
-        sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(in0 ? s0 : s1), b));
       } else if (cnt > 1 && cnt <= 4) {
         // 2..4 contenders: exact float64 losses, one contender per 16 lanes (lane: element l%16)
         unsigned long long ma = M0, mb = M1;
@@ -1072,13 +1070,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
           const double Lr = __shfl(z, 16 * r, 64);
           if (kr > 0 && (Lr < bestD || (Lr == bestD && kr < kwin))) { bestD = Lr; kwin = kr; }
         }
-        sw = cand_scale(kwin, gsc);
       }
       if (lane == 0) {
         const bool decided = cnt >= 1 && cnt <= 4;
         if (!decided) code[oblk] = 0;             // many contenders (or none): float64 pass
         win_k[wave][rr] = decided ? kwin : 0;
-        win_s[wave][rr] = sw;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1097,7 +1093,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
       const int64_t c = c_begin + rr;
       const bool row_on = rr < nrows;
       const int kw = row_on ? win_k[wave][rr] : 0;
-      const float sw = row_on ? win_s[wave][rr] : 1.0f;
+      const float sw = cand_scale(kw > 0 ? kw : 1, gsc);        // as the filter formed it
       const float wa = wt[rr][el0], wb = wt[rr][el1];
       const float ima = im_all[wave][el0], imb = im_all[wave][el1];
       const float is = __builtin_amdgcn_rcpf(sw);
