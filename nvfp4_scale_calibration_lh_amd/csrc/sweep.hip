@@ -670,6 +670,21 @@ struct ExactLds {
   double b[16];
 };
 
+// Bit r: block (row c0 + r, column myn) was left undecided (code 0) by the filter.  The rows are
+// read all at once (addresses clamped into the array, so every lane issues every load); rows past
+// cout and columns past nb read as decided.
+__device__ inline unsigned undecided_rows(const uint8_t* code, int64_t g, int64_t cout, int64_t nb,
+                                          int64_t c0, int64_t myn) {
+  uint8_t v[kExactRows];
+  const int64_t n = min(myn, nb - 1);
+#pragma unroll
+  for (int r = 0; r < kExactRows; ++r) v[r] = code[(g * cout + min(c0 + r, cout - 1)) * nb + n];
+  unsigned m = 0u;
+#pragma unroll
+  for (int r = 0; r < kExactRows; ++r) m |= (unsigned)(v[r] == 0 && c0 + r < cout && myn < nb) << r;
+  return m;
+}
+
 template <bool BF16, bool COUPLED>
 __global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
@@ -686,8 +701,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
   const int64_t g = blockIdx.z;
   const float gsc = global_scale(amax[g]);
   const int64_t myn = n0 + lane;
-  for (int64_t c = c0; c < min(cout, c0 + kExactRows); ++c) {
-    unsigned long long todo = __ballot(myn < nb && code[(g * cout + c) * nb + myn] == 0);
+  const unsigned undecided = undecided_rows(code, g, cout, nb, c0, myn);
+  for (int r = 0; r < kExactRows; ++r) {
+    const int64_t c = c0 + r;
+    if (c >= cout) break;
+    unsigned long long todo = __ballot((undecided >> r) & 1u);
     while (todo) {
       const int64_t n = n0 + __builtin_ctzll(todo);
       todo &= todo - 1;
@@ -1137,8 +1155,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
   const int64_t g = blockIdx.z;
   const float gsc = global_scale(amax[g]);
   const int64_t myn = n0 + lane;
-  for (int64_t c = c0; c < min(cout, c0 + kExactRows); ++c) {
-    unsigned long long todo = __ballot(myn < nb && code[(g * cout + c) * nb + myn] == 0);
+  const unsigned undecided = undecided_rows(code, g, cout, nb, c0, myn);
+  for (int r = 0; r < kExactRows; ++r) {
+    const int64_t c = c0 + r;
+    if (c >= cout) break;
+    unsigned long long todo = __ballot((undecided >> r) & 1u);
     while (todo) {
       const int64_t n = n0 + __builtin_ctzll(todo);
       todo &= todo - 1;
