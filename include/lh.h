@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LH_VERSION 2
+#define LH_VERSION 3
 
 typedef enum {
   LH_OK = 0,
@@ -151,6 +151,17 @@ lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int6
 lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
                               int64_t cin, const float* global_amax, const float* imp,
                               uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream);
+
+/*
+ * Same sweep scored by the plain squared error L_k = sum_i e_{k,i}^2 (H = I, no activations): the
+ * weight-only "mse" calibration that "Add WMSE weight scale search calibration" runs as its control
+ * arm (verification: mse control; Ablation table: mse rows).  Equal to lh_scale_sweep_diag with
+ * every importance 1 and to lh_scale_sweep with H_n = I, P = NULL.  Arguments and errors as
+ * lh_scale_sweep_diag without imp.
+ */
+lh_status lh_scale_sweep_mse(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                             int64_t cin, const float* global_amax, uint8_t* scale_code, uint8_t* fp4,
+                             float* best_loss, void* stream);
 
 /*
  * Fake-quantized weights and per-block amax from a sweep's result: the calibrated quantizer state

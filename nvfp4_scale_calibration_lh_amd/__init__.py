@@ -22,7 +22,7 @@ LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_dequantize", "lh_scale_sweep", "lh_scale_sweep_diag",
-            "lh_absmax", "lh_last_error", "lh_version")
+            "lh_scale_sweep_mse", "lh_absmax", "lh_last_error", "lh_version")
 
 
 class LHError(RuntimeError):
@@ -49,10 +49,11 @@ def lib() -> ctypes.CDLL:
         h.lh_accumulate_act_aware_fq.argtypes = [vp, i32, i64, i64, vp, i64, vp, f32, vp, vp, vp]
         h.lh_scale_sweep.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_diag.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        h.lh_scale_sweep_mse.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
         h.lh_absmax.argtypes = [vp, i32, i64, i64, vp, vp]
         h.lh_dequantize.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep",
-                  "lh_scale_sweep_diag", "lh_absmax", "lh_dequantize"):
+                  "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_absmax", "lh_dequantize"):
             getattr(h, f).restype = ctypes.c_int
         h.lh_last_error.argtypes = []
         h.lh_last_error.restype = ctypes.c_char_p
@@ -220,6 +221,20 @@ def lh_scale_sweep_diag(W: torch.Tensor, amax: torch.Tensor, imp: torch.Tensor,
     code, fp4, loss = _sweep_outputs(W, code, fp4, loss, want_fp4, want_loss)
     _check(lib().lh_scale_sweep_diag(_ptr(W), _dtype_code(W), G, cout, cin, _ptr(amax), _ptr(imp),
                                      _ptr(code), _ptr(fp4), _ptr(loss), _stream(W.device)))
+    return code, fp4, loss
+
+
+def lh_scale_sweep_mse(W: torch.Tensor, amax: torch.Tensor, code: Optional[torch.Tensor] = None,
+                       fp4: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None, *,
+                       want_fp4: bool = True, want_loss: bool = True):
+    """126-candidate E4M3 scale sweep scored by the plain sum_i e_i^2: (code, fp4, loss)."""
+    W = _as3d(W)
+    _need(W, "W")
+    G, cout, cin = W.shape
+    _need(amax, "amax", (G,), torch.float32)
+    code, fp4, loss = _sweep_outputs(W, code, fp4, loss, want_fp4, want_loss)
+    _check(lib().lh_scale_sweep_mse(_ptr(W), _dtype_code(W), G, cout, cin, _ptr(amax),
+                                    _ptr(code), _ptr(fp4), _ptr(loss), _stream(W.device)))
     return code, fp4, loss
 
 

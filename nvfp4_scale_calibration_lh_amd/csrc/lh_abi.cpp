@@ -322,6 +322,26 @@ lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups,
   return ok();
 }
 
+lh_status lh_scale_sweep_mse(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                             int64_t cin, const float* global_amax, uint8_t* scale_code, uint8_t* fp4,
+                             float* best_loss, void* stream) {
+  if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);
+  lh_status st = check_sweep_shapes(n_groups, cout, cin);
+  if (st != LH_OK) return st;
+  if (!global_amax || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax and scale_code are required");
+  if (!W && cout > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
+  int dev = -1;
+  st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
+  if (st != LH_OK) return st;
+  if ((st = check_aligned(W, "W")) != LH_OK) return st;
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipError_t e = lh::launch_sweep_diag(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, nullptr,
+                                       scale_code, fp4, best_loss, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "plain-MSE sweep launch");
+  return ok();
+}
+
 lh_status lh_dequantize(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
                         int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
                         void* Wq, float* block_amax, void* stream) {

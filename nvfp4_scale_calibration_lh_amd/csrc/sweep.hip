@@ -890,11 +890,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
   const int64_t c_end = min(cout, c_begin + kRowsPerWave);
   const int nrows = (int)(c_end - c_begin);
 
-  // importance of the block column (all ones when it sums to zero), a_j = sqrt(Imp_j)
-  const float* ip = imp + g * cin + n * 16;
+  // importance of the block column (all ones when it sums to zero or none is given: plain MSE),
+  // a_j = sqrt(Imp_j)
+  const float* ip = imp ? imp + g * cin + n * 16 : nullptr;
   double isum = 0.0;
+  if (ip) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) isum += (double)ip[j];
+    for (int j = 0; j < 16; ++j) isum += (double)ip[j];
+  }
   if (lane < 16) {
     const float v = isum == 0.0 ? 1.0f : ip[lane];
     im_all[wave][lane] = v;
@@ -1167,7 +1170,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
       double isum = 0.0;
   #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        im[j] = imp[g * cin + n * 16 + j];
+        im[j] = imp ? imp[g * cin + n * 16 + j] : 1.0f;
         isum += (double)im[j];
       }
       if (isum == 0.0) {

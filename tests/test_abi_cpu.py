@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep",
-              "lh_scale_sweep_diag", "lh_dequantize", "lh_absmax", "lh_last_error", "lh_version"):
+              "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_dequantize", "lh_absmax", "lh_last_error",
+              "lh_version"):
         assert n in names
     assert set(names) == set(lh.EXPORTED)
 
@@ -30,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = lh.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert lh.lh_version() == 2
+    assert lh.lh_version() == 3
 
 
 VP = ctypes.c_void_p
@@ -81,6 +82,13 @@ def test_validation_errors_without_device():
     assert L.lh_scale_sweep(FAKE, 1, 1, 4, 32, None, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_scale_sweep(FAKE, 9, 1, 4, 32, FAKE, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_UNSUPPORTED
     assert L.lh_scale_sweep_diag(FAKE, 1, 1, 4, 32, FAKE, None, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    # plain-MSE sweep: no importance argument; amax and codes required, shapes as the others
+    c, m = _err(L.lh_scale_sweep_mse(FAKE, 1, 1, 4, 32, None, FAKE, None, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "global_amax" in m
+    assert L.lh_scale_sweep_mse(FAKE, 1, 1, 4, 32, FAKE, None, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep_mse(FAKE, 1, 1, 4, 40, FAKE, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep_mse(FAKE, 1, 0, 4, 32, FAKE, FAKE, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    assert L.lh_scale_sweep_mse(FAKE, 9, 1, 4, 32, FAKE, FAKE, None, None, None) == lh.LH_ERR_UNSUPPORTED
     assert L.lh_absmax(FAKE, 1, 0, 10, FAKE, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_absmax(FAKE, 1, 1, -1, FAKE, None) == lh.LH_ERR_INVALID_ARGUMENT
 

@@ -220,6 +220,32 @@ def test_sweep_diag_parity():
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
 
+@pytest.mark.parametrize("bf16", [True, False])
+def test_sweep_mse_parity(bf16):
+    """Plain-MSE mode (no importance): the oracle's diagonal form with Imp = 1, and bit for bit the
+    diagonal entry point given an all-ones importance; zero blocks and a ragged row count included."""
+    r = np.random.default_rng(41)
+    G, cout, cin = 2, 77, 96
+    W = r.normal(0, 0.02, (G, cout, cin)).astype(np.float32)
+    W[0, 3, 16:32] = 0.0
+    W[1, :, :] *= 10.0
+    if bf16:
+        Wb = synth.bf16_bits_from_f32(W)
+        W64 = synth.f32_from_bf16_bits(Wb).astype(np.float64)
+        Wd = to_dev(Wb, "bf16")
+    else:
+        W64 = W.astype(np.float64)
+        Wd = torch.from_numpy(W).to(DEV)
+    amax = oracle.absmax(W64).astype(np.float32)
+    ad = torch.from_numpy(amax).to(DEV)
+    note(f"plain-MSE sweep bf16={bf16} G={G} cout={cout} cin={cin}")
+    code, fp4, loss = lh.lh_scale_sweep_mse(Wd, ad)
+    res = oracle.sweep_diag(W64, amax, np.ones((G, cin)))
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+    c2, f2, l2 = lh.lh_scale_sweep_diag(Wd, ad, torch.ones((G, cin), device=DEV))
+    assert torch.equal(code, c2) and torch.equal(fp4, f2) and torch.equal(loss, l2)
+
+
 def test_sweep_degenerate_blocks():
     """All-zero blocks, zero-trace Hessians, an all-zero matrix (amax 0), ragged shapes."""
     r = np.random.default_rng(3)

@@ -264,6 +264,11 @@ def test_identity_hessian_is_plain_weight_mse():
                     best, bk = err, k
             assert res["code"][0, c, n] == bk + 1
             assert np.isclose(res["loss"][0, c, n], best, rtol=1e-12)
+    # the diagonal form with unit importance is the same plain MSE (the lh_scale_sweep_mse mode)
+    d = oracle.sweep_diag(W, oracle.absmax(W), np.ones((1, cin)))
+    np.testing.assert_array_equal(d["code"], res["code"])
+    np.testing.assert_array_equal(d["fp4"], res["fp4"])
+    np.testing.assert_allclose(d["loss"], res["loss"], rtol=1e-12)
 
 
 # ------------------------------------------------------------------ P6: invariances
