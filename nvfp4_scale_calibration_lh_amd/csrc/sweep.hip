@@ -240,6 +240,19 @@ __device__ inline float quad_sum(const float p[4]) {
   return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
+// Issue priority by progress.  The SIMD's arbiter favours the oldest wave, so waves that share
+// a SIMD and carry the same work finish far apart and the last one runs alone, which one wave
+// cannot keep busy.  A wave that has done fewer of its rows gets a higher priority (3 .. 0 over
+// the four quarters), so the waves on a SIMD advance together and finish together.
+__device__ inline void wave_priority_by_progress(int done, int total) {
+  const int q = 4 * done / total;
+  if (4 * done % total >= 4) return;              // only at the start of a quarter
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // ------------------------------------------------------------------------------------------
 // Full-Hessian sweep: float32 filter
 // ------------------------------------------------------------------------------------------
@@ -278,7 +291,7 @@ __device__ inline float group_sum(float v) {
 
 // 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
 // more and drop to 3 waves, which costs about 10%; the cap spills two values outside the row loop).
-template <bool BF16, bool COUPLED>
+template <bool BF16, bool COUPLED, bool EQUALIZE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
@@ -396,6 +409,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
       const int64_t oblk = (g * cout + c) * nb + n;
+      if constexpr (EQUALIZE) wave_priority_by_progress((int)(c - c_begin), kRowsPerWave);
       float w[4], gq[4], om[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -1221,12 +1235,19 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + kRowsPerWave - 1) / kRowsPerWave),
             (unsigned)n_groups);
   dim3 block(kWaves * 64);
+  // a launch of at most four rounds of resident waves ends in a tail that the progress-based
+  // priority shortens; longer launches keep the arbiter's own order, which mixes phases better
+  const bool equalize = (int64_t)grid.x * grid.y * grid.z * kWaves <= 16384;
   // float64 pass: a wave per (kExactRows rows, 64 block columns)
   const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
                    (unsigned)((nb + 63) / 64), (unsigned)n_groups);
 #define LH_SWEEP_PAIR(B, C)                                                                        \
-  hipLaunchKernelGGL((k_sweep_full<B, C>), grid, block, 0, stream, W, cout, cin, amax, H, P, code, \
-                     fp4, loss);                                                                   \
+  if (equalize)                                                                                   \
+    hipLaunchKernelGGL((k_sweep_full<B, C, true>), grid, block, 0, stream, W, cout, cin, amax, H, P, \
+                       code, fp4, loss);                                                           \
+  else                                                                                             \
+    hipLaunchKernelGGL((k_sweep_full<B, C, false>), grid, block, 0, stream, W, cout, cin, amax, H,  \
+                       P, code, fp4, loss);                                                        \
   hipLaunchKernelGGL((k_sweep_full_exact<B, C>), xgrid, block, 0, stream, W, cout, cin, amax, H, P, \
                      code, fp4, loss)
   if (bf16 && P) {
