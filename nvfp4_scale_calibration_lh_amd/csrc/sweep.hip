@@ -295,7 +295,7 @@ template <bool BF16, bool COUPLED, bool EQUALIZE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
-    uint8_t* __restrict__ fp4, float* __restrict__ loss) {
+    uint8_t* __restrict__ fp4, float* __restrict__ loss, int rows_per_wave) {
   __shared__ FullLds lds_all[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   FullLds& L = lds_all[wave];
@@ -303,9 +303,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const int64_t nb = cin / 16;
   const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
   const int64_t g = blockIdx.z;
-  const int64_t c_begin = (int64_t)blockIdx.y * kRowsPerWave;
+  const int64_t c_begin = (int64_t)blockIdx.y * rows_per_wave;
   if (n >= nb || c_begin >= cout) return;          // whole wave leaves; no workgroup barriers below
-  const int64_t c_end = min(cout, c_begin + kRowsPerWave);
+  const int64_t c_end = min(cout, c_begin + rows_per_wave);
 
   // ---- column set-up: H_n (and P_n) through LDS into registers
   const float* Hn = Hg + (g * nb + n) * 256;
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
       const int64_t oblk = (g * cout + c) * nb + n;
-      if constexpr (EQUALIZE) wave_priority_by_progress((int)(c - c_begin), kRowsPerWave);
+      if constexpr (EQUALIZE) wave_priority_by_progress((int)(c - c_begin), rows_per_wave);
       float w[4], gq[4], om[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -1232,22 +1232,24 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
                         uint8_t* fp4, float* loss, hipStream_t stream) {
   const int64_t nb = cin / 16;
   if (cout == 0) return hipSuccess;
-  dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + kRowsPerWave - 1) / kRowsPerWave),
-            (unsigned)n_groups);
+  // a launch of at most four rounds of resident waves (4096 at a time) ends in a tail that the
+  // progress-based priority shortens; longer launches keep the arbiter's own order, which mixes
+  // phases better.  A launch of at most two rounds takes 64 rows per wave and runs as one.
+  const int64_t waves32 = (nb + kWaves - 1) / kWaves * kWaves * ((cout + kRowsPerWave - 1) / kRowsPerWave) * n_groups;
+  const bool equalize = waves32 <= 16384;
+  const int rpw = (waves32 <= 8192 && cout > kRowsPerWave) ? 2 * kRowsPerWave : kRowsPerWave;
+  dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + rpw - 1) / rpw), (unsigned)n_groups);
   dim3 block(kWaves * 64);
-  // a launch of at most four rounds of resident waves ends in a tail that the progress-based
-  // priority shortens; longer launches keep the arbiter's own order, which mixes phases better
-  const bool equalize = (int64_t)grid.x * grid.y * grid.z * kWaves <= 16384;
   // float64 pass: a wave per (kExactRows rows, 64 block columns)
   const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
                    (unsigned)((nb + 63) / 64), (unsigned)n_groups);
 #define LH_SWEEP_PAIR(B, C)                                                                        \
   if (equalize)                                                                                   \
     hipLaunchKernelGGL((k_sweep_full<B, C, true>), grid, block, 0, stream, W, cout, cin, amax, H, P, \
-                       code, fp4, loss);                                                           \
+                       code, fp4, loss, rpw);                                                      \
   else                                                                                             \
     hipLaunchKernelGGL((k_sweep_full<B, C, false>), grid, block, 0, stream, W, cout, cin, amax, H,  \
-                       P, code, fp4, loss);                                                        \
+                       P, code, fp4, loss, rpw);                                                   \
   hipLaunchKernelGGL((k_sweep_full_exact<B, C>), xgrid, block, 0, stream, W, cout, cin, amax, H, P, \
                      code, fp4, loss)
   if (bf16 && P) {
