@@ -290,7 +290,8 @@ __device__ inline float group_sum(float v) {
 }
 
 // 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
-// more and drop to 3 waves, which costs about 10%; the cap spills two values outside the row loop).
+// more and drop to 3 waves, which costs about 10%).  EQUALIZE: wave priority by progress (short
+// launches, see wave_priority_by_progress); rows_per_wave: 32, or 64 when one round holds them all.
 template <bool BF16, bool COUPLED, bool EQUALIZE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
@@ -952,9 +953,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
   {
     const int sub = lane & 7, el0 = 2 * sub, el1 = el0 + 1;
 
-    // The wave's 32 blocks (rows c_begin.., column n) come in with one coalesced load per lane (lane l: row
-    // l/2, elements 8*(l%2)..+7) and wait in LDS as w and w a, with the row's W; the same lane
-    // scores the unpaired code over its 8 elements.
+    // The wave's 32 blocks (rows c_begin.., column n) come in with one coalesced load per lane
+    // (lane l: row l/2, elements 8*(l%2)..+7) and wait in LDS as w and w a, with the row's W; the
+    // same lane scores the unpaired code over its 8 elements.
     {
       const int rr = lane >> 1, h = lane & 1;
       const int64_t c = c_begin + rr;
