@@ -242,15 +242,18 @@ __device__ inline float quad_sum(const float p[4]) {
 
 // Issue priority by progress.  The SIMD's arbiter favours the oldest wave, so waves that share
 // a SIMD and carry the same work finish far apart and the last one runs alone, which one wave
-// cannot keep busy.  A wave that has done fewer of its rows gets a higher priority (3 .. 0 over
-// the four quarters), so the waves on a SIMD advance together and finish together.
+// cannot keep busy.  A wave that has done less of its rows gets a higher priority, so the waves
+// on a SIMD advance together: 3 for the first half, 2 to three quarters, 1 to fifteen
+// sixteenths, 0 for the rest.  Within one level the oldest wave still goes first; the geometric
+// steps leave only the last sixteenth to that order, and a wave that runs ahead drops a level
+// and waits for the others.
 __device__ inline void wave_priority_by_progress(int done, int total) {
-  const int q = 4 * done / total;
-  if (4 * done % total >= 4) return;              // only at the start of a quarter
-  if (q <= 0) __builtin_amdgcn_s_setprio(3);
-  else if (q == 1) __builtin_amdgcn_s_setprio(2);
-  else if (q == 2) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
+  if (16 * done % total >= 16) return;            // only where a sixteenth begins
+  const int q = 16 * done / total;
+  if (q == 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 8) __builtin_amdgcn_s_setprio(2);
+  else if (q == 12) __builtin_amdgcn_s_setprio(1);
+  else if (q == 15) __builtin_amdgcn_s_setprio(0);
 }
 
 // ------------------------------------------------------------------------------------------
