@@ -435,9 +435,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       const bool has_ovr = (m0 | m1) != 0ull;
       int kv0 = 0, kv1 = 0;
       float rv0 = 0.0f, rv1 = 0.0f;
+      unsigned tile_hit = 0u;                        // bit tau: some override falls in tile tau
       if (has_ovr) {
         pair_override(near0, p0, wp0, gsc, &kv0, &rv0);
         pair_override(near1, p1, wp1, gsc, &kv1, &rv1);
+        for (unsigned long long m = m0; m; m &= m - 1) {
+          const int k = __builtin_amdgcn_readlane(kv0, (int)__builtin_ctzll(m));
+          if (k != 0) tile_hit |= 1u << ((k - 1) >> 4);
+        }
+        for (unsigned long long m = m1; m; m &= m - 1) {
+          const int k = __builtin_amdgcn_readlane(kv1, (int)__builtin_ctzll(m));
+          if (k != 0) tile_hit |= 1u << ((k - 1) >> 4);
+        }
       }
       float rb[4];                                   // w / s for this lane's tile-1 code
 #pragma unroll
@@ -455,7 +464,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
           float r[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) r[t] = tau == 0 ? w[t] * is0 : rb[t];
-          if (OVR) {                                  // overrides are actual quotients w / s_k
+          if (OVR && ((tile_hit >> tau) & 1u)) {      // overrides are actual quotients w / s_k
             const float isc = 1.0f / sc;               // powers of two: exact
             float o[4] = {r[0] * isc, r[1] * isc, r[2] * isc, r[3] * isc};
             apply_overrides(m0, 0, kv0, rv0, tau, 0, i, gg, o);
