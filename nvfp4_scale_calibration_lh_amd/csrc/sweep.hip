@@ -134,14 +134,14 @@ __device__ inline float exact_side(float w, float m, float s) {
   return w < 0.0f ? -r : r;
 }
 
-// Per-lane description of this lane's flagged pair p (element p/7, midpoint p%7): the affected
-// candidate (0 if none) and the quotient to use for it.
-__device__ inline void pair_override(bool near, int p, float w_el, float gsc, int* kv, float* rv) {
+// Per-lane description of this lane's flagged (element, midpoint m) pair, inv_mg = fp32(1/(m g))
+// as near_midpoint used it: the affected candidate (0 if none) and the quotient to use for it.
+__device__ inline void pair_override(bool near, float m, float inv_mg, float w_el, float gsc, int* kv,
+                                     float* rv) {
   *kv = 0;
   *rv = 0.0f;
   if (!near) return;
-  const float m = kMid[p % 7];
-  const float z = fabsf(w_el) * (float)(1.0 / ((double)m * (double)gsc));
+  const float z = fabsf(w_el) * inv_mg;           // as near_midpoint formed it
   const int k = near_candidate(z);
   if (k == 0) return;
   *kv = k;
@@ -364,8 +364,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const float s1 = cand_scale(i + 17, gsc), is1 = inv_scale(s1);
   // midpoint proximity: this lane tests pairs p = lane and lane + 64 of (element, midpoint)
   const int p0 = lane, p1 = lane + 64;
-  const float img0 = fast ? (float)(1.0 / ((double)kMid[p0 % 7] * (double)gsc)) : 0.0f;
-  const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)kMid[p1 % 7] * (double)gsc)) : 0.0f;
+  const float mid0 = kMid[p0 % 7], mid1 = kMid[(p1 < 112 ? p1 : 0) % 7];
+  const float img0 = fast ? (float)(1.0 / ((double)mid0 * (double)gsc)) : 0.0f;
+  const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)mid1 * (double)gsc)) : 0.0f;
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
@@ -437,8 +438,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       float rv0 = 0.0f, rv1 = 0.0f;
       unsigned tile_hit = 0u;                        // bit tau: some override falls in tile tau
       if (has_ovr) {
-        pair_override(near0, p0, wp0, gsc, &kv0, &rv0);
-        pair_override(near1, p1, wp1, gsc, &kv1, &rv1);
+        pair_override(near0, mid0, img0, wp0, gsc, &kv0, &rv0);
+        pair_override(near1, mid1, img1, wp1, gsc, &kv1, &rv1);
         for (unsigned long long m = m0; m; m &= m - 1) {
           const int k = __builtin_amdgcn_readlane(kv0, (int)__builtin_ctzll(m));
           if (k != 0) tile_hit |= 1u << ((k - 1) >> 4);
