@@ -50,7 +50,8 @@ def code_digest(path):
 
 
 def measured_traffic(cfg, prefix):
-    """HBM bytes per call of the kernels whose names start with `prefix`, from the rocprofv3
+    """HBM bytes per call of the kernels whose names start with `prefix` (a string or a tuple of
+    them), from the rocprofv3
     FETCH_SIZE / WRITE_SIZE passes recorded in profiles/traffic.json, scaled by the copy-kernel
     calibration factors.  None when no record exists or a kernel's code changed since."""
     try:
@@ -302,7 +303,7 @@ def main():
         "roofline": roof,
         "accumulate": {"avg_launch_ms": ms_acc, "algorithmic_bytes": acc_bytes, "achieved_gbs": acc_gbs,
                        "peak_gbs": HBM_PEAK_GBS, "frac": acc_gbs / HBM_PEAK_GBS,
-                       "traffic": measured_traffic(rec, "k_acc"),
+                       "traffic": measured_traffic(rec, ("k_acc", "k_imp")),
                        "copy_gbs": copy_gbs, "frac_of_copy": acc_gbs / copy_gbs},
         "absmax": {"avg_launch_ms": ms_abs, "achieved_gbs": abs_gbs, "frac": abs_gbs / HBM_PEAK_GBS},
         "dequantize": {"avg_launch_ms": ms_dq, "algorithmic_bytes": dq_bytes,
