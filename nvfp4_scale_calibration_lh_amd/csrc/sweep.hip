@@ -60,9 +60,13 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;            // waves per workgroup; wave w takes block column 4*bx + w
 constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
 constexpr int kExactRows = 16;       // rows per wave of the float64 passes
-// Filter error bound factor.  Full form: the fp32 arithmetic and the two-piece bf16 split of H
-// together contribute at most about 2^-17.2 (S_e^2 + S_e S_w + 2|e|^T(|P||w|)) <= 2^-17.2 A
-// (A_k as in the header), so 2^-16 leaves a margin above 2x.
+// Filter error bound factor.  Full form: per element i the computed s y_i misses (H e + 2b)_i by
+// at most d_i (S_w + S_e) 2^-18 (two-piece split of H), gamma_32 d_i (2 S_w + S_e) (fp32
+// accumulation of 32 exact products onto the accumulator input, whose size is at most
+// d_i S_w + 2(|P||w|)_i), 2^-20 d_i S_w (H w on fp32 MFMA) and 2^-23 d_i S_w (the accumulator
+// input's two roundings); weighted by |e_i| and summed, with the dot product's own roundings,
+// that is at most about 2^-16.8 (S_e^2 + S_e S_w + 2|e|^T(|P||w|)) <= 2^-16.8 A (A_k as in the
+// header), so 2^-16 leaves a margin of about 1.75x.
 constexpr float kErrC = 0x1p-16f;
 constexpr int kNearUlps = 16;        // midpoint proximity test, in ulps of |w|/(m g)
 
@@ -291,6 +295,20 @@ __device__ inline float group_sum(float v) {
   auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
+// Maximum of a value >= 0 over the wave, wave-uniform (bit patterns of such floats order like
+// unsigned integers).
+__device__ inline float wave_max_nonneg(float x) {
+  unsigned v = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(b[0], b[1]);
+  v = max(v, (unsigned)dppi<0x128>((int)v));
+  v = max(v, (unsigned)dppi<0x124>((int)v));
+  v = max(v, (unsigned)dppi<0x122>((int)v));
+  v = max(v, (unsigned)dppi<0x121>((int)v));
+  return __uint_as_float((unsigned)__builtin_amdgcn_readfirstlane((int)v));
+}
 
 // 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
 // more and drop to 3 waves, which costs about 10%).  EQUALIZE: wave priority by progress (short
@@ -332,6 +350,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   //            (2 d_col in the coupled form)
   float a[4], dm[4], pa[4], pv[4];
   unsigned h1[4], h2[4];
+  float hpmax = 0.0f;                               // max |H_ij|, |P_ij| of the column
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int col = 4 * gg + t;
@@ -347,6 +366,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     dm[t] = sqrtf(mx) * (COUPLED ? 2.0000004f : 1.0000002f);   // (2x when coupled) with sqrt margin
     pv[t] = coupled ? L.P[i * 16 + col] : 0.0f;
     pa[t] = fabsf(pv[t]);
+    hpmax = fmaxf(hpmax, fmaxf(mx, pa[t]));
   }
   // one 16x16x32 bf16 MFMA per tile: K slots [H1 | H2] against [q | q]
   const v4u A1u = {h1[0] | (h1[1] << 16), h1[2] | (h1[3] << 16), h2[0] | (h2[1] << 16), h2[2] | (h2[3] << 16)};
@@ -358,8 +378,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // the lane forms w * is1 once per block and the FP4 converts apply the power of 4 through their
   // exponent-only scale operand (on the way in and out), which is exact.  Codes 127 and 128
   // (tile 7, i >= 14) do not exist and are masked.
+  // The filter's fp32 values stay finite and normal-range for every candidate when |H|, |P| <=
+  // 2^100 and g^2 max(|H|, |P|) <= 2^76 (quotients |w|/s <= 2^20.4, |e| <= 2^12.4 g, 16 terms);
+  // other columns go to the float64 pass whole.
   const float gsc = global_scale(amax[g]);
-  const bool fast = filter_ok(gsc);
+  const float hpm = wave_max_nonneg(hpmax);
+  const bool fast = filter_ok(gsc) && hpm <= 0x1p100f && (double)gsc * (double)gsc * (double)hpm <= 0x1p76;
   const float s0 = cand_scale(i + 1, gsc), is0 = inv_scale(s0);
   const float s1 = cand_scale(i + 17, gsc), is1 = inv_scale(s1);
   // midpoint proximity: this lane tests pairs p = lane and lane + 64 of (element, midpoint)
@@ -367,6 +391,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   const float mid0 = kMid[p0 % 7], mid1 = kMid[(p1 < 112 ? p1 : 0) % 7];
   const float img0 = fast ? (float)(1.0 / ((double)mid0 * (double)gsc)) : 0.0f;
   const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)mid1 * (double)gsc)) : 0.0f;
+  const float sl0 = gg == 0 ? s0 : s1;             // scale of tile gg (first half of the tiles)
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
@@ -452,11 +477,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       float rb[4];                                   // w / s for this lane's tile-1 code
 #pragma unroll
       for (int t = 0; t < 4; ++t) rb[t] = w[t] * is1;
+      // accumulator inputs -(H w - 2 P w)_i / s of tile 0 and of tiles 1..7 (which share s1)
+      v4f cacc0, cacc1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        cacc0[t] = -gq[t] * is0;
+        cacc1[t] = -gq[t] * is1;
+      }
 
       // Scoring of tile tau (16 codes): quotients (with exact overrides) -> FP4 round trip
-      // q' = q * 4^(tau-1) (exact in bf16), e = fma(q', s, -w), y = H q' on bf16 MFMA (H in
-      // two pieces, products exact, fp32 accumulation), (H e + 2b)_i = s y_i - (H w - 2b)_i,
-      // L = sum_i e_i (H e + 2b)_i.  Instantiated twice so the common case has no override code.
+      // q' = q * 4^(tau-1) (exact in bf16), e = fma(q', s, -w), y = H q' - (H w - 2b)/s on bf16
+      // MFMA (H in two pieces, products exact, fp32 accumulation onto the accumulator input), so
+      // (H e + 2b)_i = s y_i and L = s sum_i e_i y_i, with s applied once after the sum over the
+      // lane groups.  Instantiated twice so the common case has no override code.
       unsigned pkc = 0u;
       auto score = [&](auto ovr_tag, float Lq[2], float Aq[2]) {
         constexpr bool OVR = decltype(ovr_tag)::value;
@@ -500,9 +533,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
             const int tau = 4 * q + u;
             const v4u Bu = {p01, p23, p01, p23};
             const v8bf B = __builtin_bit_cast(v8bf, Bu);
-            const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, zero4, 0, 0, 0);
+            const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, tau == 0 ? cacc0 : cacc1, 0, 0, 0);
             if (tau < 7) tile_err(tau + 1, en, pn01, pn23);         // overlaps the MFMAs
-            const float sb = tau == 0 ? s0 : s1;
             // bound: uncoupled, this lane's part of S_e = sum_i d_i |e_i| (A follows after the
             // group sum); coupled, (2 S_e,g)^2 + sum_i |e_i| om_i over the lane's 4 elements,
             // whose sum over the 4 groups is >= S_e^2 + S_e S_w + 2|e|^T(|P||w|) (Cauchy-Schwarz)
@@ -518,10 +550,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
               tp = fmaf(fabsf(e[3]), om[3], tp);
               ap = fmaf(sp, sp, tp);
             }
-            float lp = e[0] * fmaf(sb, y[0], -gq[0]);
-            lp = fmaf(e[1], fmaf(sb, y[1], -gq[1]), lp);
-            lp = fmaf(e[2], fmaf(sb, y[2], -gq[2]), lp);
-            lp = fmaf(e[3], fmaf(sb, y[3], -gq[3]), lp);
+            float lp = e[0] * y[0];
+            lp = fmaf(e[1], y[1], lp);
+            lp = fmaf(e[2], y[2], lp);
+            lp = fmaf(e[3], y[3], lp);
             pl[u] = lp;
             pa4[u] = ap;
             if (tau < 7) {
@@ -531,7 +563,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
               p23 = pn23;
             }
           }
-          Lq[q] = quad_sum(pl);
+          Lq[q] = quad_sum(pl) * (q == 0 ? sl0 : s1);   // lane group gg holds tile 4q + gg
           Aq[q] = quad_sum(pa4);
           if (!COUPLED) Aq[q] *= fmaf(4.0f, Aq[q], S_w);   // A = S_e (4 S_e + S_w)
         }
@@ -549,7 +581,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       const float U = wave_min_ordered(u1 < u0 ? u1 : u0);
       const unsigned long long M0 = __ballot(fmaf(-kErrC, Aq[0], Lq[0]) <= U);
       const unsigned long long M1 = __ballot(fmaf(-kErrC, Aq[1], Lq[1]) <= U);
-      const int cnt = __popcll(M0) + __popcll(M1);
+      // |L_k| <= A_k, so |U| >= 2^-100 keeps every bound that matters far above the absolute
+      // rounding of the subnormal range; smaller (or NaN) U goes to the float64 pass.
+      const int cnt = fabsf(U) >= 0x1p-100f ? __popcll(M0) + __popcll(M1) : 0;
       if (cnt == 1) {
         // unique winner: emit its codes.  Its scale and reciprocal come from the lane that owns
         // it (tiles >= 1 apply their power of 4 exactly).

@@ -438,6 +438,39 @@ def test_sweep_diag_importance_and_weight_ranges():
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
 
+@pytest.mark.parametrize("coupled", [False, True])
+def test_sweep_full_hessian_and_weight_ranges(coupled):
+    """Hessians far from unit scale, where the fp32 filter's intermediate values would overflow or
+    sink to the subnormal range (H and P near 1e34 and 1e-34, g^2 |H| above 2^76, entries
+    spanning 1e-24..1e24 in one block, tiny weights): every block must still get the oracle's
+    argmin, through the filter where its range allows and the float64 pass elsewhere."""
+    r = np.random.default_rng(35)
+    G, cout, cin = 6, 40, 64
+    nb = cin // 16
+    W = r.normal(0, 0.02, (G, cout, cin)).astype(np.float32)
+    W[3] *= np.float32(1e-20)
+    W[4] *= np.float32(1e12)
+    A = r.standard_normal((G, nb, 16, 16))
+    H = np.einsum("gnij,gnkj->gnik", A, A) / 16 + 0.5 * np.eye(16)
+    H[0] *= 1e34
+    H[1] *= 1e-34
+    d = 10.0 ** r.uniform(-12, 12, (nb, 16))
+    H[2] *= d[:, :, None] * d[:, None, :]
+    H[5] *= 1e20
+    H = H.astype(np.float32)
+    P = None
+    if coupled:
+        B = r.standard_normal((G, nb, 16, 16)) * 0.05
+        P = (B * np.sqrt(np.abs(np.einsum("gnii->gni", H.astype(np.float64))))[:, :, :, None]).astype(np.float32)
+    a = oracle.absmax(W.astype(np.float64)).astype(np.float32)
+    note(f"full sweep Hessian and weight ranges coupled={coupled} G={G} cout={cout} cin={cin}")
+    code, fp4, loss = lh.lh_scale_sweep(torch.from_numpy(W).to(DEV), torch.from_numpy(a).to(DEV),
+                                        torch.from_numpy(H).to(DEV),
+                                        torch.from_numpy(P).to(DEV) if coupled else None)
+    res = oracle.sweep(W.astype(np.float64), a, H, P)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
 def test_sweep_deterministic():
     wl = synth.make("c2", cout=100, cin=64, rows=300)
     note("sweep determinism")
