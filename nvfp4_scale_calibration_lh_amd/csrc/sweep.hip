@@ -22,8 +22,9 @@
 //    (H1 + H2 equals H to 2^-18 relative, a residual the error bound below covers), so one
 //    v_mfma_f32_16x16x32_bf16 with K slots [H1 | H2] gives H q for 16 candidates with exact products and fp32
 //    accumulation.  H w (and P w, |P||w| in the coupled form) comes from v_mfma_f32_16x16x4_f32
-//    once per 16-row tile.  The loss L = e^T (H e + 2 P w) is a 4-term dot per lane reduced over
-//    the 4 lane groups with permlane swaps; the argmin over lanes uses DPP row rotations and
+//    once per 16-row tile; -(H w - 2 P w)/s is the accumulator input of the H q MFMA, so its
+//    result times s is H e + 2 P w.  The loss L = e^T (H e + 2 P w) is a 4-term dot per lane
+//    reduced over the 4 lane groups with permlane swaps and scaled by s once; the argmin over lanes uses DPP row rotations and
 //    permlane swaps.  Quantization of the next tile is issued before the current tile's MFMA
 //    result is consumed.
 //  * Diagonal form: VALU only (there is no contraction to map onto MFMA); a lane scores two
