@@ -155,7 +155,10 @@ lh_status check_shapes_x(int64_t rows, int64_t cin, const int64_t* offsets, int6
 // Accumulation scratch of one device, kept between calls: a work area and arrival counters
 // (zero between calls: set to zero when allocated, and every call leaves them zero).  The memory is
 // handed from call to call in stream order: `ready` is recorded on the stream of the last call
-// that used it and the next call's stream waits for it, so two calls never use it at once.
+// that used it and the next call's stream waits for it, so two calls never use it at once.  Only
+// streams of the same device wait for `ready`, so its release needs device scope: the event is
+// created without the system-scope fence (which writes back and invalidates the caches on every
+// record, about 1.8 us per call measured on MI355X).
 struct DeviceScratch {
   std::mutex mu;
   void* work = nullptr;
@@ -208,7 +211,7 @@ lh_status run_accumulate(const void* X, const void* Xq, const float* x_amax, lh_
   DeviceScratch& sc = device_scratch(dev);
   std::lock_guard<std::mutex> lk(sc.mu);
   if (!sc.ready) {
-    e = hipEventCreateWithFlags(&sc.ready, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&sc.ready, hipEventDisableTiming | hipEventDisableSystemFence);
     if (e != hipSuccess) { sc.ready = nullptr; return hip_fail(e, "hipEventCreateWithFlags"); }
   } else {
     e = hipStreamWaitEvent(s, sc.ready, 0);

@@ -119,6 +119,35 @@ def test_accumulate_empty_groups_and_beta():
     assert_imp_close(imp.cpu().numpy(), imp2_ref)
 
 
+def test_accumulate_two_streams_share_scratch():
+    # the library's accumulation scratch is handed from call to call in stream order; calls that
+    # alternate between two streams without any host synchronization must each give the result
+    # of the same call made alone (multi-tile dense and grouped layers both use the scratch)
+    r = np.random.default_rng(11)
+    rows, cin = 3000, 320
+    off = np.array([0, 40, 1500, 1510, 3000], dtype=np.int64)
+    note(f"accumulate on two streams: X[{rows},{cin}] dense and 4 groups, 6 calls each")
+    Xs = [torch.from_numpy(synth.bf16_bits_from_f32(r.normal(0, 1 + k, (rows, cin)).astype(np.float32)))
+          .view(torch.bfloat16).to(DEV) for k in range(4)]
+    offd = torch.from_numpy(off).to(DEV)
+    alone = []
+    for k, X in enumerate(Xs):
+        o = offd if k % 2 else None
+        H, imp = lh.lh_accumulate(X, offsets=o, want_imp=True)
+        torch.cuda.synchronize()
+        alone.append((H.clone(), imp.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]     # default priority
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        for k, X in enumerate(Xs):
+            with torch.cuda.stream(streams[(k + rep) % 2]):
+                outs.append((k, lh.lh_accumulate(X, offsets=offd if k % 2 else None, want_imp=True)))
+    torch.cuda.synchronize()
+    for k, (H, imp) in outs:
+        assert torch.equal(H, alone[k][0]) and torch.equal(imp, alone[k][1]), f"input {k} differs"
+
+
 def test_accumulate_zero_rows():
     note("accumulate rows=0")
     X = torch.empty((0, 32), dtype=torch.bfloat16, device=DEV)
