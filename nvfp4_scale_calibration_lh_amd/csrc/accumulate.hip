@@ -799,11 +799,12 @@ int64_t dense_tile_rows(int64_t rows, int64_t nb, bool bf16, bool imp_only, bool
   return R;
 }
 
-// Rows per piece of grouped rows: about 8192 pieces over all slices (32 waves per compute unit),
-// a multiple of the chunk, between 64 and 1024 rows.
+// Rows per piece of grouped rows: about 4096 pieces over all slices (16 waves per compute unit),
+// a multiple of the chunk, between 64 and 1024 rows.  Measured on MI355X at the 512-expert
+// gate_up shape: 1.4-1.8% faster than 8192 pieces, 2048 and 6144 slower.
 int64_t piece_rows(int64_t rows, int64_t nb) {
   const int64_t slices = (nb + 3) / 4;
-  int64_t R = rows * slices / 8192;
+  int64_t R = rows * slices / 4096;
   R = (R + kChunk - 1) / kChunk * kChunk;
   return R < 64 ? 64 : (R > 1024 ? 1024 : R);
 }
