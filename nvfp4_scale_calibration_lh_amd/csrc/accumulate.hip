@@ -21,9 +21,10 @@
 //  * Dense layer (one group): a workgroup of 16 waves owns a tile of R rows whose chunks the
 //    waves take in turn; the waves add their sums in LDS at the end.  With several tiles, each
 //    tile stores its sums and the last tile of a slice to finish adds them all in tile order.
-//  * Grouped rows (MoE experts): a small planning kernel cuts every group into pieces of at most
-//    R rows (a group without rows is one empty piece); each wave owns one piece, so a group of at
-//    most R rows is finished by one wave with no synchronization.  Pieces of larger groups leave
+//  * Grouped rows (MoE experts): every group is cut into pieces of at most R rows (a group
+//    without rows is one empty piece), each workgroup finding its own pieces from a scan of the
+//    group offsets; each wave owns one piece, so a group of at most R rows is finished by one wave
+//    with no synchronization.  Pieces of larger groups leave
 //    partial sums and the last of them to finish adds them in piece order.
 //  * Pieces' partial sums cross workgroups through agent-scope relaxed atomic stores and loads (coherent
 //    across the per-XCD L2 caches without whole-cache flushes), ordered by waiting for the stores
@@ -48,7 +49,6 @@ constexpr int kChunk = 32;          // rows per chunk (one 16x16x32 MFMA per blo
 constexpr int kCh = 64;             // channels per slice (four blocks)
 constexpr int kPitchH = kCh + 8;    // bf16 LDS row pitch (halves); 144 bytes keeps 16-byte alignment
 constexpr int kPitchF = kCh + 4;    // fp32 LDS row pitch (floats)
-constexpr int kEntry = 4;           // int64 words of one piece-table entry
 
 template <bool BF16>
 struct Geo {
@@ -656,39 +656,55 @@ __global__ __launch_bounds__(NW * 64) void k_imp_dense(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Grouped rows: planning.  One workgroup cuts every group into pieces of at most R rows and
-// writes the piece table: word 0 = number of pieces; entry p (at 4 + 4p) = {group, first row,
-// end row, piece index in group << 32 | pieces in group}, pieces of one group consecutive; then,
-// at 4 + 4 cap, the schedule: piece numbers with the R-row pieces first.
+// Grouped rows.  Every group is cut into pieces of at most R rows (a group without rows is one
+// empty piece).  Pieces are numbered in group order, the pieces of one group consecutive; the
+// schedule runs the R-row pieces first (longest work first), then the others, each part in piece
+// order.  A 1-D grid of ceil(capacity / 4) x slices workgroups, slice fastest (the slices of the
+// same rows run together); wave w of workgroup x owns the piece in schedule slot 4x + w.  Each
+// workgroup derives its pieces itself from a scan of the group offsets in LDS (no planning
+// kernel, no table in memory).  Partial layout: [piece][slice][m][block][kPart]; counters:
+// [group][slice].
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict__ off, int64_t G,
-                                                       int64_t rows, int64_t R, int64_t cap,
-                                                       int64_t* __restrict__ table) {
+template <bool BF16, bool ACT, bool DIAG, bool FQ>
+__global__ __launch_bounds__(kThreads) void k_acc_pieces(
+    const void* __restrict__ Xv, const void* __restrict__ Xqv, const float* __restrict__ x_amax,
+    int64_t cin, const int64_t* __restrict__ off, int64_t G, int64_t rows, int64_t R, int64_t cap,
+    float beta, float* __restrict__ H, float* __restrict__ P, float* __restrict__ imp,
+    float* __restrict__ ws, unsigned* __restrict__ counters, int64_t nb) {
+  using St = Streamer<BF16, ACT, FQ>;
+  constexpr int kM = St::kM;
+  constexpr int kPart = DIAG ? 16 : 256;
+  __shared__ __attribute__((aligned(16))) unsigned smem[4 * kM * Geo<BF16>::kWords];
   __shared__ int64_t scan[kThreads];
-  const int tid = threadIdx.x;
-  const int64_t per = (G + kThreads - 1) / kThreads;
-  const int64_t g0 = min(G, tid * per), g1 = min(G, g0 + per);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, gg = lane >> 4;
+  const int64_t slices = (nb + 3) / 4, slice = blockIdx.x % slices;
+
   // rows of group g, clamped to [0, rows] so that offsets outside the contract never address
-  // memory outside X
+  // memory outside X; its pieces: f of exactly R rows and n in all
   auto span = [&](int64_t g, int64_t& a, int64_t& e) {
     a = min(max(off[g], (int64_t)0), rows);
     e = min(max(off[g + 1], a), rows);
   };
-  auto npieces = [&](int64_t g) -> int64_t {
-    int64_t a, e;
-    span(g, a, e);
-    return e > a ? (e - a + R - 1) / R : 1;   // a group without rows is one empty piece
+  auto counts = [&](int64_t a, int64_t e, int64_t& f, int64_t& n) {
+    f = (e - a) / R;
+    n = e > a ? (e - a + R - 1) / R : 1;
   };
-  // pieces of exactly R rows are scheduled first (longest work first), the others after them
-  int64_t nfull = 0, nrest = 0;
-  for (int64_t g = g0; g < g1; ++g) {
-    int64_t a, e;
-    span(g, a, e);
-    const int64_t n = npieces(g), f = (e - a) / R;
-    nfull += f;
-    nrest += n - f;
+  // thread t counts the full and the other pieces of groups [t per, (t + 1) per); both counts are
+  // scanned at once (each < 2^31)
+  const int64_t per = (G + kThreads - 1) / kThreads;
+  {
+    const int64_t g0 = min(G, tid * per), g1 = min(G, g0 + per);
+    int64_t nfull = 0, nrest = 0;
+    for (int64_t g = g0; g < g1; ++g) {
+      int64_t a, e, f, n;
+      span(g, a, e);
+      counts(a, e, f, n);
+      nfull += f;
+      nrest += n - f;
+    }
+    scan[tid] = nfull | (nrest << 32);
   }
-  scan[tid] = nfull | (nrest << 32);          // both counts scanned at once (each < 2^31)
   __syncthreads();
   for (int d = 1; d < kThreads; d <<= 1) {    // inclusive scan
     const int64_t v = tid >= d ? scan[tid - d] : 0;
@@ -696,50 +712,54 @@ __global__ __launch_bounds__(kThreads) void k_acc_plan(const int64_t* __restrict
     scan[tid] += v;
     __syncthreads();
   }
-  const int64_t tot_full = scan[kThreads - 1] & 0xFFFFFFFF, total = tot_full + (scan[kThreads - 1] >> 32);
-  if (tid == 0) table[0] = total <= cap ? total : 0;      // more pieces only if offsets break the contract
-  if (total > cap) return;
-  int64_t* sched = table + kEntry + cap * kEntry;
-  int64_t sf = (scan[tid] & 0xFFFFFFFF) - nfull;          // next schedule slot of a full piece
-  int64_t sr = tot_full + (scan[tid] >> 32) - nrest;      // ... and of any other piece
-  int64_t p = sf + sr - tot_full;                         // pieces of earlier threads
-  for (int64_t g = g0; g < g1; ++g) {
-    int64_t a, e;
-    span(g, a, e);
-    const int64_t n = npieces(g);
-    for (int64_t k = 0; k < n; ++k, ++p) {
-      int64_t* t = table + kEntry + p * kEntry;
-      t[0] = g;
-      t[1] = min(e, a + k * R);
-      t[2] = min(e, a + (k + 1) * R);
-      t[3] = (k << 32) | n;
-      sched[t[2] - t[1] == R ? sf++ : sr++] = p;
-    }
-  }
-}
-
-// Grouped rows: a 1-D grid of ceil(capacity / 4) x slices workgroups, slice fastest (the slices of
-// the same rows run together); wave w of workgroup x owns the piece in schedule slot 4x + w.
-// Partial layout: [piece][slice][m][block][kPart]; counters: [group][slice].
-template <bool BF16, bool ACT, bool DIAG, bool FQ>
-__global__ __launch_bounds__(kThreads) void k_acc_pieces(
-    const void* __restrict__ Xv, const void* __restrict__ Xqv, const float* __restrict__ x_amax,
-    int64_t cin, const int64_t* __restrict__ table, int64_t cap, float beta, float* __restrict__ H,
-    float* __restrict__ P, float* __restrict__ imp, float* __restrict__ ws,
-    unsigned* __restrict__ counters, int64_t nb) {
-  using St = Streamer<BF16, ACT, FQ>;
-  constexpr int kM = St::kM;
-  constexpr int kPart = DIAG ? 16 : 256;
-  __shared__ __attribute__((aligned(16))) unsigned smem[4 * kM * Geo<BF16>::kWords];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, gg = lane >> 4;
-  const int64_t slices = (nb + 3) / 4, slice = blockIdx.x % slices;
+  // wave-uniform values (LDS reads of one address) are moved to scalar registers
+  auto uni = [](int64_t v) -> int64_t {
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  const int64_t last = uni(scan[kThreads - 1]);
+  const int64_t tot_full = last & 0xFFFFFFFF;
+  const int64_t total = tot_full + (last >> 32);
   const int64_t sidx = (int64_t)(blockIdx.x / slices) * 4 + wave;
-  if (sidx >= table[0]) return;               // whole wave leaves; no workgroup barriers here
-  const int64_t p = table[kEntry + cap * kEntry + sidx];
-  const int64_t* e = table + kEntry + p * kEntry;
-  const int64_t g = e[0], r0 = e[1], r1 = e[2];
-  const int64_t k = e[3] >> 32, npieces = e[3] & 0xFFFFFFFF;
+  // more pieces than the capacity only if the offsets break the contract: then nothing is done
+  if (total > cap || sidx >= total) return;   // whole wave leaves; no workgroup barriers below
+  // schedule slot -> piece: the thread whose groups hold it (first inclusive count above the
+  // rank), then a walk over that thread's groups (wave-uniform)
+  const bool full = sidx < tot_full;
+  const int sh = full ? 0 : 32;
+  const int64_t rank = full ? sidx : sidx - tot_full;
+  int lo = 0, hi = kThreads - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (((uni(scan[mid]) >> sh) & 0xFFFFFFFF) > rank) hi = mid; else lo = mid + 1;
+  }
+  const int t = lo;
+  const int64_t before = t > 0 ? uni(scan[t - 1]) : 0;
+  int64_t left = rank - ((before >> sh) & 0xFFFFFFFF);
+  int64_t p = (before & 0xFFFFFFFF) + (before >> 32);   // pieces of the groups of earlier threads
+  const int64_t gend_t = min(G, (t + 1) * per);
+  int64_t g = min(G, t * per), a = 0, e = 0, k = -1, npieces = 1;
+  for (; g < gend_t; ++g) {
+    int64_t f, n;
+    span(g, a, e);
+    counts(a, e, f, n);
+    const int64_t c = full ? f : n - f;
+    if (left < c) {
+      k = full ? left : f;
+      npieces = n;
+      break;
+    }
+    left -= c;
+    p += n;
+  }
+  if (k < 0) return;                          // not reached: the scan counted this slot here
+  // the piece's numbers are wave-uniform: keep them in scalar registers
+  g = uni(g);
+  k = uni(k);
+  p = uni(p + k);
+  npieces = uni(npieces);
+  const int64_t r0 = uni(a + k * R), r1 = uni(min(e, a + k * R + R)), T = uni(e - a);
   const int64_t n0 = slice * 4;
   const int nblk = (int)min((int64_t)4, nb - n0);
 
@@ -748,9 +768,6 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
   if (FQ) st.set_fake_quant(x_amax[g]);
   st.run(r0, r1, 0, 1);
 
-  const int64_t gbeg = table[kEntry + (p - k) * kEntry + 1];
-  const int64_t gend = table[kEntry + (p - k + npieces - 1) * kEntry + 2];
-  const int64_t T = gend - gbeg;
   float* imp_g = imp ? imp + g * nb * 16 : nullptr;
   // (block loops have a constant trip count so the accumulators stay in registers)
   if (npieces == 1) {
@@ -831,14 +848,10 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
     return hipGetLastError();
   }
   const int64_t R = piece_rows(rows, nb);
-  const int64_t cap = rows / R + 2 * G;       // >= the number of pieces
-  int64_t* table = (int64_t*)work;
-  float* ws = (float*)(table + kEntry + 2 * cap * kEntry);
-  hipLaunchKernelGGL(k_acc_plan, dim3(1), dim3(kThreads), 0, stream, off, G, rows, R, cap, table);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int64_t cap = rows / R + G;           // >= sum over groups of max(1, ceil(T_g / R))
+  float* ws = (float*)work;
   hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG, FQ>), dim3((unsigned)(((cap + 3) / 4) * slices)),
-                     dim3(kThreads), 0, stream, X, Xq, x_amax, cin, table, cap, beta, H, P, imp, ws,
+                     dim3(kThreads), 0, stream, X, Xq, x_amax, cin, off, G, rows, R, cap, beta, H, P, imp, ws,
                      counters, nb);
   return hipGetLastError();
 }
@@ -869,8 +882,8 @@ AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, 
     s.counters = (size_t)slices;
   } else {
     const int64_t R = piece_rows(rows, nb);
-    const int64_t cap = rows / R + 2 * n_groups;
-    s.work_bytes = (size_t)(kEntry + 2 * cap * kEntry) * sizeof(int64_t) + (size_t)cap * slices * part;
+    const int64_t cap = rows / R + n_groups;
+    s.work_bytes = (size_t)cap * slices * part;
     s.counters = (size_t)n_groups * slices;
   }
   return s;

@@ -8,8 +8,8 @@
 
 namespace lh {
 
-// Scratch of one launch_accumulate call: a work area (piece table of grouped rows and partial
-// sums of row ranges that are added across workgroups) and arrival counters.  The counters must be
+// Scratch of one launch_accumulate call: a work area (partial sums of row ranges that are added
+// across workgroups) and arrival counters.  The counters must be
 // zero when a call starts and are zero again when it ends.  launch_accumulate checks the sizes it
 // is given against this and launches nothing if they are short.
 struct AccScratch {
