@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LH_VERSION 3
+#define LH_VERSION 4
 
 typedef enum {
   LH_OK = 0,
@@ -85,8 +85,10 @@ lh_status lh_accumulate(const void* X, lh_dtype x_dtype, int64_t rows, int64_t c
  * Activation-aware Hessian and cross matrix (PR #1976, What does this PR do?):
  *   H[g][n] = beta*H[g][n] + X_q^T X_q / T_g,   P[g][n] = beta*P[g][n] + X_q^T (X_q - X) / T_g
  * per 16-channel block, over the rows of group g.  X and Xq are [rows, cin] of the same dtype.
- * P is formed from the difference D = X_q - X (exact in fp32 for bf16 inputs), never as the
- * difference of two products.  H and P are both required.  Errors as lh_accumulate.
+ * P is formed from the difference D = X_q - X rounded once to fp32 (exact when X_q and X are
+ * within a factor 2^15 of each other, as a fake-quant of X is; otherwise within 2^-24 of D) and
+ * split exactly into bf16 pieces, never as the difference of two products.  H and P are both
+ * required.  Errors as lh_accumulate.
  */
 lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype, int64_t rows,
                                   int64_t cin, const int64_t* group_offsets, int64_t n_groups,
@@ -112,6 +114,20 @@ lh_status lh_accumulate_act_aware_fq(const void* X, lh_dtype dtype, int64_t rows
                                      const int64_t* group_offsets, int64_t n_groups,
                                      const float* x_amax, float beta, float* H, float* P,
                                      void* stream);
+
+/*
+ * The activation fake-quant alone: writes X_q, the NVFP4 fake-quant of X that
+ * lh_accumulate_act_aware_fq applies inside its kernel (same definition, same bits), for callers
+ * that need the quantized activations themselves or feed lh_accumulate_act_aware (PR #1976, What
+ * does this PR do?: X_q is what the layer's input quantizer emits).
+ * X, Xq [rows, cin] of dtype (Xq is written, fully; it must not overlap X).  x_amax [n_groups]
+ * fp32 device as in lh_accumulate_act_aware_fq; groups as everywhere (row r uses the amax of the
+ * group that holds it).  Errors: INVALID_ARGUMENT for the shape checks of lh_accumulate, NULL
+ * x_amax, NULL X or Xq with rows > 0, Xq == X, misaligned, non-device or mixed-device pointers.
+ */
+lh_status lh_activation_fake_quant(const void* X, lh_dtype dtype, int64_t rows, int64_t cin,
+                                   const int64_t* group_offsets, int64_t n_groups, const float* x_amax,
+                                   void* Xq, void* stream);
 
 /*
  * Exhaustive FP8 block-scale sweep with the local-Hessian objective (PR #788, review: block loss

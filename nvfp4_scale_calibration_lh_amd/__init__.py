@@ -21,8 +21,9 @@ LIB_PATH = os.environ.get("LH_LIBRARY") or os.path.join(_PKG, "liblh.so")
 LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 
-EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_dequantize", "lh_scale_sweep", "lh_scale_sweep_diag",
-            "lh_scale_sweep_mse", "lh_absmax", "lh_last_error", "lh_version")
+EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_activation_fake_quant",
+            "lh_dequantize", "lh_scale_sweep", "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_absmax",
+            "lh_last_error", "lh_version")
 
 
 class LHError(RuntimeError):
@@ -47,12 +48,14 @@ def lib() -> ctypes.CDLL:
         h.lh_accumulate.argtypes = [vp, i32, i64, i64, vp, i64, f32, vp, vp, vp]
         h.lh_accumulate_act_aware.argtypes = [vp, vp, i32, i64, i64, vp, i64, f32, vp, vp, vp]
         h.lh_accumulate_act_aware_fq.argtypes = [vp, i32, i64, i64, vp, i64, vp, f32, vp, vp, vp]
+        h.lh_activation_fake_quant.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, vp]
         h.lh_scale_sweep.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_diag.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_mse.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
         h.lh_absmax.argtypes = [vp, i32, i64, i64, vp, vp]
         h.lh_dequantize.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
-        for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep",
+        for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
+                  "lh_activation_fake_quant", "lh_scale_sweep",
                   "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_absmax", "lh_dequantize"):
             getattr(h, f).restype = ctypes.c_int
         h.lh_last_error.argtypes = []
@@ -169,6 +172,22 @@ def lh_accumulate_act_aware_fq(X: torch.Tensor, x_amax: torch.Tensor, H: Optiona
     _check(lib().lh_accumulate_act_aware_fq(_ptr(X), _dtype_code(X), rows, cin, _ptr(offsets), G, _ptr(x_amax),
                                             float(beta), _ptr(H), _ptr(P), _stream(X.device)))
     return H, P
+
+
+def lh_activation_fake_quant(X: torch.Tensor, x_amax: torch.Tensor, Xq: Optional[torch.Tensor] = None,
+                             offsets: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """X_q [rows, cin]: the NVFP4 fake-quant of X with the input quantizer's amax per group
+    (x_amax [G] fp32), as lh_accumulate_act_aware_fq applies it inside its kernel."""
+    _need(X, "X")
+    rows, cin = X.shape
+    offsets, G = _offsets(offsets, X)
+    _need(x_amax, "x_amax", (G,), torch.float32)
+    if Xq is None:
+        Xq = torch.empty_like(X)
+    _need(Xq, "Xq", X.shape, X.dtype)
+    _check(lib().lh_activation_fake_quant(_ptr(X), _dtype_code(X), rows, cin, _ptr(offsets), G, _ptr(x_amax),
+                                          _ptr(Xq), _stream(X.device)))
+    return Xq
 
 
 def _sweep_outputs(W, code, fp4, loss, want_fp4, want_loss):

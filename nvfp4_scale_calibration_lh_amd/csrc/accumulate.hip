@@ -15,9 +15,10 @@
 //  * bf16 inputs use v_mfma_f32_16x16x32_bf16: 32 tokens per instruction, products exact, fp32
 //    accumulation.  The operand A[i][k] = x_{t_k}[i] is also B[k][i], so one register set feeds
 //    both.  fp32 inputs use v_mfma_f32_16x16x4_f32 with the same mapping.
-//  * The cross matrix uses D = X_q - X formed in fp32 (exact for bf16 data) and split into a bf16
-//    high part (truncation) and the exact bf16 remainder, so P = X_q^T D_hi + X_q^T D_lo needs two
-//    more MFMAs and no catastrophic cancellation.
+//  * The cross matrix uses D = X_q - X formed in fp32 (one rounding, none when X_q and X are
+//    within 2^15 of each other) and split exactly into bf16 pieces: P = X_q^T D_hi + X_q^T D_lo
+//    (+ X_q^T D_rest when D has more than 16 significant bits), never a difference of two
+//    products, so no catastrophic cancellation.
 //  * Dense layer (one group): a workgroup of 16 waves owns a tile of R rows whose chunks the
 //    waves take in turn; the waves add their sums in LDS at the end.  With several tiles, each
 //    tile stores its sums and the last tile of a slice to finish adds them all in tile order.
@@ -209,6 +210,47 @@ __device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool f
   return out;
 }
 
+// X_q written out: the same fake-quant act_fake_quant applies inside the accumulation, as its own
+// streaming pass (the layer's input quantizer alone).  Thread u of the grid-stride walk owns the
+// 16-byte unit u of the row-major array, so the two (bf16) or four (fp32) lanes holding one
+// 16-channel block are a lane pair or quad of one wave; each lane finds its row's group by a
+// binary search of the offsets.  Four units per thread are loaded before any is converted.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_act_fake_quant(const v4u* __restrict__ X, v4u* __restrict__ Xq,
+                                                            int64_t units, int64_t units_per_row,
+                                                            const int64_t* __restrict__ off, int64_t G,
+                                                            const float* __restrict__ x_amax) {
+  constexpr int kU = 4;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads + threadIdx.x; base < units; base += kU * stride) {
+    v4u x[kU];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {       // every lane loads (clamped), so the DPP partners exist
+      const int64_t u = min(base + k * stride, units - 1);
+      x[k] = __builtin_nontemporal_load(&X[u]);
+    }
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int64_t u = base + k * stride;
+      const int64_t row = min(u, units - 1) / units_per_row;
+      int64_t g = 0;
+      if (off) {                         // last group whose first row is <= row
+        int64_t lo = 0, hi = G - 1;
+        while (lo < hi) {
+          const int64_t mid = (lo + hi + 1) >> 1;
+          if (off[mid] <= row) lo = mid; else hi = mid - 1;
+        }
+        g = lo;
+      }
+      const float amax = x_amax[g];
+      const float gx = amax / 2688.0f;   // fp32(amax / (6*448)), correctly rounded
+      const double inv6g = 1.0 / (6.0 * (double)gx);
+      const v4u q = act_fake_quant<BF16>(x[k], gx, inv6g, gx >= 0x1p-100f && gx <= 0x1p100f);
+      if (u < units) __builtin_nontemporal_store(q, &Xq[u]);
+    }
+  }
+}
+
 // One wave's streaming contraction of rows [r0, r1) of a 64-channel slice into four blocks of
 // accumulators, using the wave's own LDS stage.  Chunks are taken with a stride of `step` chunks
 // starting at chunk `first` (counted from r0), so several waves can share a range.  With FQ the
@@ -319,23 +361,43 @@ struct Streamer {
         const v8bf A = __builtin_bit_cast(v8bf, aq);
         accH[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, accH[b], 0, 0, 0);
         if (ACT) {
+          // d = fp32(xq - x) (relative error <= 2^-24, exact whenever the two are within 2^15 of
+          // each other) is split exactly into bf16 pieces: hi = its top 8 significant bits, lo =
+          // the next 8 bits of the remainder, rest = the at most 8 bits left.  rest is zero when d
+          // has at most 16 significant bits (always for a fake-quant of x); its MFMA runs only on
+          // the chunks where some lane has one.
           const unsigned short* tx = (const unsigned short*)(stage + (kM - 1) * Gm::kWords);
           v4u dh, dl;
+          float rest[8];
+          unsigned any_rest = 0u;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const unsigned x0 = tx[(8 * gg + 2 * u) * kPitchH + 16 * b + i];
             const unsigned x1 = tx[(8 * gg + 2 * u + 1) * kPitchH + 16 * b + i];
-            const float d0 = bf16_lo(aq[u]) - bf16_lo(x0);     // exact: both are bf16
+            const float d0 = bf16_lo(aq[u]) - bf16_lo(x0);
             const float d1 = bf16_hi(aq[u]) - bf16_lo(x1);
             const unsigned h0 = __float_as_uint(d0) & 0xFFFF0000u;
             const unsigned h1 = __float_as_uint(d1) & 0xFFFF0000u;
-            const float l0 = d0 - __uint_as_float(h0);         // exact remainder
+            const float l0 = d0 - __uint_as_float(h0);         // exact remainders
             const float l1 = d1 - __uint_as_float(h1);
             dh[u] = (h0 >> 16) | h1;
             dl[u] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
+            rest[2 * u] = l0;
+            rest[2 * u + 1] = l1;
+            any_rest |= (__float_as_uint(l0) | __float_as_uint(l1)) & 0xFFFFu;
           }
           accP[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dh), accP[b], 0, 0, 0);
           accP[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dl), accP[b], 0, 0, 0);
+          if (__builtin_amdgcn_ballot_w64(any_rest != 0u)) {
+            v4u dr;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float r0 = rest[2 * u] - __uint_as_float(__float_as_uint(rest[2 * u]) & 0xFFFF0000u);
+              const float r1 = rest[2 * u + 1] - __uint_as_float(__float_as_uint(rest[2 * u + 1]) & 0xFFFF0000u);
+              dr[u] = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xFFFF0000u);   // exact bf16
+            }
+            accP[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dr), accP[b], 0, 0, 0);
+          }
         }
       }
     } else {
@@ -867,6 +929,23 @@ hipError_t launch_zero_fill(unsigned* p, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
                      p, (int64_t)n);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_fake_quant(const void* X, bool bf16, int64_t rows, int64_t cin, const int64_t* offsets,
+                                 int64_t n_groups, const float* x_amax, void* Xq, hipStream_t stream) {
+  const int64_t units = rows * cin * (bf16 ? 2 : 4) / 16;
+  if (units == 0) return hipSuccess;
+  const int64_t upr = cin * (bf16 ? 2 : 4) / 16;
+  const int64_t want = (units + kThreads * 4 - 1) / (kThreads * 4);
+  const unsigned grid = (unsigned)min(want, (int64_t)8192);
+  const int64_t* off = (offsets && n_groups > 1) ? offsets : nullptr;
+  if (bf16)
+    hipLaunchKernelGGL(k_act_fake_quant<true>, dim3(grid), dim3(kThreads), 0, stream, (const v4u*)X, (v4u*)Xq,
+                       units, upr, off, n_groups, x_amax);
+  else
+    hipLaunchKernelGGL(k_act_fake_quant<false>, dim3(grid), dim3(kThreads), 0, stream, (const v4u*)X, (v4u*)Xq,
+                       units, upr, off, n_groups, x_amax);
   return hipGetLastError();
 }
 

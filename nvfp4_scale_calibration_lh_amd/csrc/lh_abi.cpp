@@ -284,6 +284,29 @@ lh_status lh_accumulate_act_aware_fq(const void* X, lh_dtype dtype, int64_t rows
   return run_accumulate(X ? X : H, nullptr, x_amax, dtype, rows, cin, group_offsets, n_groups, beta, H, P, nullptr, stream);
 }
 
+lh_status lh_activation_fake_quant(const void* X, lh_dtype dtype, int64_t rows, int64_t cin,
+                                   const int64_t* group_offsets, int64_t n_groups, const float* x_amax,
+                                   void* Xq, void* stream) {
+  if (!dtype_ok(dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  lh_status st = check_shapes_x(rows, cin, group_offsets, n_groups);
+  if (st != LH_OK) return st;
+  if (!x_amax) return fail(LH_ERR_INVALID_ARGUMENT, "x_amax is required");
+  if ((!X || !Xq) && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X and Xq are required");
+  if (rows == 0) return ok();
+  if (X == Xq) return fail(LH_ERR_INVALID_ARGUMENT, "Xq must not alias X");
+  int dev = -1;
+  st = check_pointers({{X, "X"}, {Xq, "Xq"}, {x_amax, "x_amax"}, {group_offsets, "group_offsets"}}, &dev);
+  if (st != LH_OK) return st;
+  if ((st = check_aligned(X, "X")) != LH_OK) return st;
+  if ((st = check_aligned(Xq, "Xq")) != LH_OK) return st;
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipError_t e = lh::launch_act_fake_quant(X, dtype == LH_DTYPE_BF16, rows, cin, group_offsets, n_groups, x_amax, Xq,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "activation fake-quant launch");
+  return ok();
+}
+
 lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
                          int64_t cin, const float* global_amax, const float* H, const float* P,
                          uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {

@@ -33,6 +33,10 @@ hipError_t launch_accumulate(const void* X, const void* Xq, const float* x_amax,
                              size_t work_bytes, unsigned* counters, size_t n_counters,
                              hipStream_t stream);
 
+// X_q = the activations' NVFP4 fake-quant (the one the FQ accumulation applies), written to Xq.
+hipError_t launch_act_fake_quant(const void* X, bool bf16, int64_t rows, int64_t cin, const int64_t* offsets,
+                                 int64_t n_groups, const float* x_amax, void* Xq, hipStream_t stream);
+
 hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout, int64_t cin,
                         const float* amax, const float* H, const float* P, uint8_t* code,
                         uint8_t* fp4, float* loss, hipStream_t stream);

@@ -1,10 +1,10 @@
 """Seeded synthetic inputs shared by the tests, the benchmark and the oracle's timing leg.
 
 This package holds no arithmetic of the calibration method (no Hessians, no scale
-search, no weight quantization).  It only draws tensors with fixed seeds and the
-shapes/distributions of the workloads, converts them to the storage dtype, and (for
-the activation-aware workload) produces the quantized activation input ``X_q`` by the
-input recipe documented in ``synth.configs.activation_fake_quant``.
+search, no weight or activation quantization).  It only draws tensors with fixed seeds
+and the shapes/distributions of the workloads and converts them to the storage dtype.
+The activation-aware workload's X_q (the input quantizer's fake-quant of X) is made by
+the oracle in the tests and by the library in the benchmark, never here.
 """
 from .configs import (  # noqa: F401
     CONFIGS,

@@ -6,11 +6,14 @@ distributions below.  Five workloads are defined:
 
 ``c1``  tiny dense: W [64,128] fp32 ~N(0,0.02), X [256,128] fp32 ~N(0,1), full Hessian.
 ``c2``  dense 2048x2048: W bf16 ~N(0,0.02), X [8192,2048] bf16 ~N(0,1) whose 1% outlier
-        channels are multiplied by 20 before rounding to bf16; full Hessian.
+        channels (at least one) are multiplied by 20 before rounding to bf16; full Hessian.
 ``c3``  activation-aware up_proj: W [12288,4096] bf16 ~N(0,0.015), X [8192,4096] bf16
-        Student-t(4); X_q from ``activation_fake_quant``; H and P, sweep with cross term.
+        Student-t(4); H and P, sweep with cross term.  Its X_q is not drawn here: it is the
+        NVFP4 fake-quant of X by the layer's input quantizer (per-tensor amax max|X|), which the
+        tests take from the oracle and the benchmark from the library
+        (``lh_activation_fake_quant``); ``Workload.Xq`` stays None until a caller sets it.
 ``c4``  WMSE down_proj: W [4096,12288] bf16 ~N(0,0.01), X [8192,12288] bf16 ~N(0,1) with
-        0.5% outlier channels x30; importance vector only, diagonal sweep.
+        0.5% outlier channels (at least one) x30; importance vector only, diagonal sweep.
 ``c5``  fused-MoE gate_up: 512 experts, each W [1280,2560] bf16 ~N(0,0.02); 8192 tokens of
         hidden size 2560 bf16 ~N(0,1); each token routed to 10 distinct experts drawn by
         Gumbel-top-k on Zipf(1.1) logits; the per-expert token slices are concatenated in
@@ -88,61 +91,6 @@ def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
     return a
 
 
-# ---------------------------------------------------------------------------------------------
-# Input recipe for X_q (activation-aware workload).  This models the input quantizer that sits
-# in front of the linear layer; its output is an *input* of the calibration method (both the
-# GPU path and the oracle consume the same X_q bytes), so nothing downstream depends on how it
-# was produced.  Recipe: one per-tensor global scale gX = fp32(max|X| / (6*448)); per token and
-# per 16-channel block, the block scale v = E4M3(amax_blk / (6*gX)) rounded to nearest-even and
-# saturated at 448 (v == 0 zeroes the block); elements are x/(v*gX) rounded to the nearest value
-# of {0,0.5,1,1.5,2,3,4,6} (ties to the even grid index, saturating at 6), multiplied back by
-# fp32(v*gX), and finally rounded to bf16 as a bf16 model's quantizer would emit.
-# ---------------------------------------------------------------------------------------------
-_FP4_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
-
-
-def _round_e4m3_pos(y: np.ndarray) -> np.ndarray:
-    """Nearest-even E4M3 value of non-negative y, saturating at 448 (float64 in/out)."""
-    y = np.minimum(y, 448.0)
-    m, e = np.frexp(y)                 # y = m * 2**e, m in [0.5, 1)
-    e = e - 1                          # y = (2m) * 2**e with 2m in [1, 2)
-    e = np.maximum(e, -6)              # below 2**-6 the spacing is fixed at 2**-9
-    step = np.ldexp(1.0, e - 3)
-    q = np.rint(y / step) * step       # np.rint rounds half to even
-    return np.minimum(q, 448.0)
-
-
-def _round_e2m1_mag(r: np.ndarray) -> np.ndarray:
-    """Nearest grid magnitude of non-negative r with ties to the even grid index."""
-    idx = np.searchsorted(_FP4_MAG, r)              # first grid value >= r
-    idx = np.clip(idx, 1, 7)
-    lo, hi = _FP4_MAG[idx - 1], _FP4_MAG[idx]
-    dlo, dhi = r - lo, hi - r
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((idx % 2) == 0))
-    out = np.where(pick_hi, hi, lo)
-    return np.where(r >= 6.0, 6.0, out)
-
-
-def activation_fake_quant(x_bits: np.ndarray) -> np.ndarray:
-    """X_q for the activation-aware workload, from bf16 X bits [rows, cin]; returns bf16 bits."""
-    x = f32_from_bf16_bits(x_bits).astype(np.float64)
-    rows, cin = x.shape
-    gx = float(np.float32(np.max(np.abs(x)) / 2688.0))
-    out = np.empty_like(x_bits)
-    step = 1024
-    for r0 in range(0, rows, step):
-        xb = x[r0:r0 + step].reshape(-1, cin // 16, 16)
-        amax_b = np.max(np.abs(xb), axis=-1)
-        v = _round_e4m3_pos(amax_b / (6.0 * gx)) if gx > 0 else np.zeros_like(amax_b)
-        sb = (v * gx).astype(np.float32).astype(np.float64)
-        safe = np.where(sb > 0, sb, 1.0)
-        r = np.abs(xb) / safe[..., None]
-        q = np.sign(xb) * _round_e2m1_mag(r) * sb[..., None]
-        q = np.where(sb[..., None] > 0, q, 0.0)
-        out[r0:r0 + step] = bf16_bits_from_f32(q.reshape(-1, cin).astype(np.float32))
-    return out
-
-
 @dataclasses.dataclass
 class Workload:
     name: str
@@ -153,7 +101,7 @@ class Workload:
     cin: int
     W: np.ndarray           # [n_groups, cout, cin] (uint16 bf16 bits or float32)
     X: np.ndarray           # [rows, cin]
-    Xq: Optional[np.ndarray]
+    Xq: Optional[np.ndarray]  # activation-aware input X_q; never made by the generator (see c3)
     offsets: np.ndarray     # int64 [n_groups + 1]; rows of group g are [off[g], off[g+1])
     description: str = ""
 
@@ -240,10 +188,9 @@ def make(name: str, seed: int = 0, **over) -> Workload:
     else:
         x32 = _normal(rng_for(seed, cid, 1), (rows, cin), 1.0)
     if "outlier_frac" in cfg:
-        n_out = int(np.floor(cfg["outlier_frac"] * cin))
+        n_out = max(1, int(np.floor(cfg["outlier_frac"] * cin)))   # at least one, also when shrunk
         ch = rng_for(seed, cid, 2).choice(cin, size=n_out, replace=False)
         x32[:, ch] *= np.float32(cfg["outlier_mul"])
     X = _to_storage(x32, dtype)
-    Xq = activation_fake_quant(X) if mode == "act" else None
     offsets = np.array([0, rows], dtype=np.int64)
-    return Workload(name, dtype, mode, 1, cout, cin, W, X, Xq, offsets, DESCRIPTIONS[name])
+    return Workload(name, dtype, mode, 1, cout, cin, W, X, None, offsets, DESCRIPTIONS[name])

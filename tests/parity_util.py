@@ -66,3 +66,39 @@ def assert_sweep_match(code, fp4, loss, res, allow_exempt=True):
         lbad = same & (np.abs(np.asarray(loss, dtype=np.float64) - res["loss"]) > REL * scale + 1e-30)
         assert not lbad.any(), f"{lbad.sum()} losses outside tolerance"
     return int(exempt.sum())
+
+
+def oracle_xq(X64, offsets, bf16, x_amax=None):
+    """X_q of the activation-aware workloads: the oracle's NVFP4 fake-quant of X with the input
+    quantizer's amax (default: max |X| of each group), in storage form (bf16 bits or float32)."""
+    import synth
+    offsets = np.asarray(offsets)
+    if x_amax is None:
+        x_amax = np.array([np.abs(X64[offsets[g]:offsets[g + 1]]).max(initial=0.0)
+                           for g in range(len(offsets) - 1)])
+    Xq64 = oracle.activation_fake_quant(X64, np.asarray(x_amax, dtype=np.float64), offsets, bf16=bf16)
+    return synth.bf16_bits_from_f32(Xq64.astype(np.float32)) if bf16 else Xq64.astype(np.float32)
+
+
+def with_oracle_xq(wl):
+    """The workload with its X_q input filled in from the oracle (activation-aware mode only)."""
+    if wl.mode == "act" and wl.Xq is None:
+        wl.Xq = oracle_xq(wl.X_f64(), wl.offsets, wl.dtype == "bf16")
+    return wl
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def pool_map(fn, tasks):
+    """fn over tasks in a pool of forked processes (up to 16, the host's CPU share of one GPU), one
+    BLAS thread each; results in task order.  The workers run NumPy only."""
+    import multiprocessing as mp
+    import os
+    n = max(1, min(16, len(os.sched_getaffinity(0)), len(tasks)))
+    if n == 1:
+        return [fn(t) for t in tasks]
+    with mp.get_context("fork").Pool(n, initializer=_one_blas_thread) as pool:
+        return pool.map(fn, tasks, chunksize=1)

@@ -20,7 +20,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_scale_sweep",
+    for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
+              "lh_activation_fake_quant", "lh_scale_sweep",
               "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_dequantize", "lh_absmax", "lh_last_error",
               "lh_version"):
         assert n in names
@@ -31,7 +32,8 @@ def test_library_exports_every_declared_symbol():
     L = lh.lib()
     for n in declared_functions():
         assert hasattr(L, n), n
-    assert lh.lh_version() == 3
+    want = int(re.search(r"#define LH_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lh.lh_version() == want
 
 
 VP = ctypes.c_void_p
@@ -55,6 +57,13 @@ def test_validation_errors_without_device():
     assert L.lh_accumulate(FAKE, 1, 10, 32, None, 0, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     c, m = _err(L.lh_accumulate(FAKE, 1, 10, 32, None, 3, 0.0, FAKE, None, None))
     assert c == lh.LH_ERR_INVALID_ARGUMENT and "group_offsets" in m
+    # activation fake-quant: x_amax required, Xq required, no aliasing, host memory rejected
+    c, m = _err(L.lh_activation_fake_quant(FAKE, 1, 10, 32, None, 1, None, VP(0x2000), None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "x_amax" in m
+    assert L.lh_activation_fake_quant(FAKE, 1, 10, 32, None, 1, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT
+    c, m = _err(L.lh_activation_fake_quant(FAKE, 1, 10, 32, None, 1, VP(0x3000), FAKE, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "alias" in m
+    assert L.lh_activation_fake_quant(FAKE, 9, 10, 32, None, 1, FAKE, FAKE, None) == lh.LH_ERR_UNSUPPORTED
     # no outputs, NULL input
     assert L.lh_accumulate(FAKE, 1, 10, 32, None, 1, 0.0, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_accumulate(None, 1, 10, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT

@@ -2,15 +2,17 @@
 
 Each workload (dense 2048x2048, activation-aware up_proj 12288x4096, WMSE down_proj 4096x12288,
 512-expert MoE gate_up 1280x2560) runs absmax -> accumulation -> sweep once on the GPU through the
-C ABI, exactly as one benchmark step does.  The oracle then checks, one by one:
+C ABI, exactly as one benchmark step does.  The oracle then checks:
 
 * the per-group absmax of every group, bit for bit;
-* the Hessian / cross matrix / importance of sampled blocks (every group for the MoE layer);
-* the full 126-candidate float64 search of several thousand sampled weight blocks (seeded random
-  blocks plus the block holding each sampled group's absmax), against the GPU's own fp32 H / P /
-  importance: codes and FP4 nibbles identical outside near-ties, losses within 1e-5;
-* over all blocks (all experts' blocks in 8 sampled experts for the MoE layer): every code is a
-  valid candidate byte and the FP4 nibbles are the E2M1 encoding of the block at the chosen scale.
+* H / P / importance of every block column of every group, in float64;
+* the full 126-candidate float64 search of every weight block of the dense layers and of every
+  block of eight whole experts of the MoE layer (seeded, with the experts of the largest and the
+  smallest routed-token counts), against the GPU's own fp32 H / P / importance: codes and FP4
+  nibbles identical outside near-ties, losses within 1e-5.  The oracle runs in a pool of up to 16
+  processes (one BLAS thread each); the count of near-tie blocks is printed;
+* the activation-aware layer's X_q made by lh_activation_fake_quant is the oracle's bit for bit,
+  and H, P made with X_q formed inside the accumulation kernel equal the two-input kernel's.
 """
 import numpy as np
 import pytest
@@ -18,14 +20,15 @@ import torch
 
 import oracle
 import synth
-from parity_util import assert_h_close, assert_imp_close, assert_p_close, assert_sweep_match
+from parity_util import (assert_h_close, assert_imp_close, assert_p_close, cross_gram, oracle_xq,
+                         pool_map)
 
 pytestmark = pytest.mark.gpu
 
 lh = pytest.importorskip("nvfp4_scale_calibration_lh_amd")
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
 FULL = ["c2", "c3", "c4", "c5"]
-N_SAMPLE = 6144
+MOE_EXPERTS = 8
 
 
 def note(msg):
@@ -39,11 +42,28 @@ def to_dev(a, dtype):
     return t.to(DEV)
 
 
+def _xq_rows(task):
+    X64, amax, bf16 = task
+    return oracle_xq(X64, np.array([0, len(X64)]), bf16, x_amax=[amax])
+
+
+def full_xq(wl):
+    """The oracle's X_q of a single-group activation-aware layer (per-tensor amax max|X|), made in
+    row chunks over the process pool."""
+    X64 = wl.X_f64()
+    amax = float(np.abs(X64).max())
+    step = 512
+    parts = pool_map(_xq_rows, [(X64[a:a + step], amax, wl.dtype == "bf16") for a in range(0, len(X64), step)])
+    return np.concatenate(parts)
+
+
 @pytest.fixture(scope="module", params=FULL)
 def run(request):
     name = request.param
     note(f"full-size {name}: generating inputs")
     wl = synth.make(name)
+    if wl.mode == "act":
+        wl.Xq = full_xq(wl)
     G, cout, cin = wl.n_groups, wl.cout, wl.cin
     note(f"full-size {name}: W{wl.W.shape} X{wl.X.shape} mode={wl.mode} on the GPU")
     W = to_dev(wl.W, wl.dtype)
@@ -71,14 +91,19 @@ def run(request):
     return name, wl, out
 
 
-def _sample_groups(wl, k=16):
+def _sweep_groups(wl):
+    """Groups whose every block is checked: all of a dense layer; for the MoE layer a seeded set of
+    whole experts holding the largest and the smallest routed-token counts."""
     G = wl.n_groups
     if G == 1:
         return np.array([0])
     T = np.diff(wl.offsets)
+    pick = {int(np.argmax(T)), int(np.argmin(T))}
     rng = np.random.default_rng(7)
-    pick = set(rng.choice(G, size=min(k, G), replace=False).tolist())
-    pick |= {int(np.argmax(T)), int(np.argmin(T)), 0, G - 1}
+    for g in rng.permutation(G):
+        if len(pick) >= MOE_EXPERTS:
+            break
+        pick.add(int(g))
     return np.array(sorted(pick))
 
 
@@ -89,13 +114,14 @@ def test_fullsize_absmax(run):
     np.testing.assert_array_equal(out["amax"], ref)
 
 
-def test_fullsize_accumulation_sampled(run):
+def test_fullsize_accumulation_all_columns(run):
+    """Every block column of every group against the float64 accumulation (64 columns at a time)."""
     name, wl, out = run
     nb = wl.n_blocks
-    blocks = sorted({0, nb - 1, *np.random.default_rng(3).choice(nb, size=min(6, nb), replace=False).tolist()})
-    note(f"full-size {name}: accumulation of blocks {blocks}")
-    for n in blocks:
-        cols = slice(16 * n, 16 * n + 16)
+    note(f"full-size {name}: accumulation of all {nb} block columns of {wl.n_groups} group(s)")
+    for n0 in range(0, nb, 4):
+        cols = slice(16 * n0, 16 * min(nb, n0 + 4))
+        blk = slice(n0, min(nb, n0 + 4))
         Xn = wl._f64(wl.X[:, cols])
         if wl.mode == "diag":
             _, imp_ref = oracle.accumulate(Xn, wl.offsets, want_h=False, want_imp=True)
@@ -103,39 +129,68 @@ def test_fullsize_accumulation_sampled(run):
         elif wl.mode == "act":
             Xqn = wl._f64(wl.Xq[:, cols])
             H_ref, P_ref = oracle.accumulate_act_aware(Xn, Xqn, wl.offsets)
-            R_ref, _ = oracle.accumulate(Xqn - Xn, wl.offsets)
-            assert_h_close(out["H"][:, n], H_ref[:, 0])
-            assert_p_close(out["P"][:, n], P_ref[:, 0], H_ref[:, 0], R_ref[:, 0])
+            R_ref = cross_gram(Xn, Xqn, wl.offsets)
+            assert_h_close(out["H"][:, blk], H_ref)
+            assert_p_close(out["P"][:, blk], P_ref, H_ref, R_ref)
         else:
             H_ref, _ = oracle.accumulate(Xn, wl.offsets)
-            assert_h_close(out["H"][:, n], H_ref[:, 0])
+            assert_h_close(out["H"][:, blk], H_ref)
 
 
-def test_fullsize_sweep_sampled(run):
+def _oracle_rows(task):
+    """Pool worker: the oracle's search of every block of rows [r0, r1) of one group; returns the
+    codes, packed nibbles, losses, the loss scale Q + |C| and the near-tie flags."""
+    mode, r0, w, g, H, P, imp = task
+    rows, cin = w.shape
+    nb = cin // 16
+    wb = w.reshape(-1, 16)
+    n = np.tile(np.arange(nb), rows)
+    gs = np.full(len(wb), g)
+    if mode == "diag":
+        res = oracle.sweep_blocks_diag(wb, gs, imp.reshape(nb, 16)[n])
+    else:
+        res = oracle.sweep_blocks(wb, gs, H, P, hidx=n)
+    fp4 = oracle.pack_nibbles(res["nib"]).reshape(rows, nb, 8)
+    return (r0, res["code"].reshape(rows, nb), fp4, res["loss"].reshape(rows, nb),
+            (res["Q1"] + np.abs(res["C1"])).reshape(rows, nb), oracle.exempt_mask(res).reshape(rows, nb))
+
+
+def test_fullsize_sweep_every_block(run):
+    """The whole layer (the dense workloads) or eight whole experts (MoE) against the oracle's
+    search on the GPU's own fp32 H / P / importance."""
     name, wl, out = run
-    G, cout, nb = wl.n_groups, wl.cout, wl.n_blocks
-    rng = np.random.default_rng(11)
-    groups = _sample_groups(wl)
-    per = max(1, N_SAMPLE // len(groups))
-    total_exempt = 0
-    note(f"full-size {name}: oracle search of {per * len(groups)}+ sampled blocks in {len(groups)} groups")
+    cout, nb = wl.cout, wl.n_blocks
+    groups = _sweep_groups(wl)
+    step = max(1, 16384 // nb)
+    total = exempt_total = 0
+    note(f"full-size {name}: oracle search of every block of group(s) {groups.tolist()} "
+         f"({len(groups) * cout * nb} blocks)")
     for g in groups:
-        Wg = wl.W_f64(int(g)).reshape(cout, nb, 16)
-        flat = rng.choice(cout * nb, size=min(per, cout * nb), replace=False)
-        am = int(np.argmax(np.abs(Wg).reshape(-1)))          # block holding the group's absmax
-        flat = np.unique(np.concatenate([flat, [am // 16, 0, cout * nb - 1]]))
-        c, n = flat // nb, flat % nb
-        w = Wg[c, n]
-        gs = np.repeat(oracle.global_scale(out["amax"][g:g + 1].astype(np.float64))[0], len(flat))
-        if wl.mode == "diag":
-            res = oracle.sweep_blocks_diag(w, gs, out["imp"][g].reshape(nb, 16)[n].astype(np.float64))
-        else:
-            P = None if out["P"] is None else out["P"][g].astype(np.float64)
-            res = oracle.sweep_blocks(w, gs, out["H"][g].astype(np.float64), P, hidx=n)
-        res["fp4"] = oracle.pack_nibbles(res["nib"])
-        total_exempt += assert_sweep_match(out["code"][g][c, n], out["fp4"][g].reshape(cout, nb, 8)[c, n],
-                                           out["loss"][g][c, n], res)
-    note(f"full-size {name}: {total_exempt} near-tie blocks exempt")
+        g = int(g)
+        Wg = wl.W_f64(g)
+        gsc = float(oracle.global_scale(out["amax"][g:g + 1].astype(np.float64))[0])
+        H = None if out["H"] is None else out["H"][g].astype(np.float64)
+        P = None if out["P"] is None else out["P"][g].astype(np.float64)
+        imp = None if out["imp"] is None else out["imp"][g].astype(np.float64)
+        mode = "diag" if wl.mode == "diag" else "full"
+        tasks = [(mode, r0, Wg[r0:r0 + step], gsc, H, P, imp) for r0 in range(0, cout, step)]
+        code = out["code"][g]
+        fp4 = out["fp4"][g].reshape(cout, nb, 8)
+        loss = out["loss"][g].astype(np.float64)
+        for r0, rc, rf, rl, rs, rx in pool_map(_oracle_rows, tasks):
+            sl = slice(r0, r0 + len(rc))
+            bad = (code[sl] != rc) & ~rx
+            assert not bad.any(), (f"group {g}: {bad.sum()} scale codes differ outside near-ties, first at "
+                                   f"rows/blocks {(np.argwhere(bad)[:3] + [r0, 0]).tolist()}")
+            fbad = (fp4[sl] != rf).any(-1) & ~rx
+            assert not fbad.any(), f"group {g}: {fbad.sum()} blocks with FP4 codes differing outside near-ties"
+            same = code[sl] == rc
+            lbad = same & (np.abs(loss[sl] - rl) > 1e-5 * rs + 1e-30)
+            assert not lbad.any(), f"group {g}: {lbad.sum()} losses outside 1e-5"
+            total += rc.size
+            exempt_total += int(rx.sum())
+    note(f"full-size {name}: {total} blocks checked, {exempt_total} near-tie blocks exempt")
+    assert total == len(groups) * cout * nb
 
 
 def test_fullsize_codes_and_nibbles_consistent(run):
@@ -158,7 +213,6 @@ def test_fullsize_codes_and_nibbles_consistent(run):
             ref = oracle.pack_nibbles(nib)
             bad = (fp4[r0:r1] != ref).any(-1)
             assert not bad.any(), f"group {g}: {bad.sum()} blocks whose FP4 bytes are not the encoding at their scale"
-
 
 
 def test_fullsize_dequantize(run):
@@ -186,16 +240,30 @@ def test_fullsize_dequantize(run):
             np.testing.assert_array_equal(got_w[k, r0:r1], ref_bits[0])
             np.testing.assert_array_equal(got_a[k, r0:r1].astype(np.float64), ref_a[0])
 
-def test_fullsize_fused_fake_quant_matches_two_input_path():
-    """Activation-aware up_proj 12288x4096 (X [8192,4096] bf16): H and P with X_q made in the
-    kernel equal, value for value, those of the two-input kernel fed the generator's X_q (the
-    same quantizer recipe, pinned against the oracle's), so every X_q element is bit-exact."""
+
+def test_fullsize_activation_fake_quant_and_fused_accumulation():
+    """Activation-aware up_proj 12288x4096 (X [8192,4096] bf16 Student-t(4)): the library's X_q
+    (lh_activation_fake_quant) is the oracle's bit for bit; H and P made with X_q formed inside the
+    accumulation kernel are within tolerance of the oracle's on every block column and equal,
+    value for value, those of the two-input kernel fed the oracle's X_q."""
     wl = synth.make("c3")
-    note("full-size c3: fused fake-quant accumulation against the two-input path")
+    note("full-size c3: oracle X_q")
+    Xq_ref = full_xq(wl)
+    note("full-size c3: X_q and fused fake-quant accumulation on the GPU")
     X = to_dev(wl.X, "bf16")
-    Xq = to_dev(wl.Xq, "bf16")
     amax = torch.tensor([float(np.abs(wl.X_f64()).max())], dtype=torch.float32, device=DEV)
-    H1, P1 = lh.lh_accumulate_act_aware(X, Xq)
+    Xq_gpu = lh.lh_activation_fake_quant(X, amax)
+    H1, P1 = lh.lh_accumulate_act_aware(X, to_dev(Xq_ref, "bf16"))
     H2, P2 = lh.lh_accumulate_act_aware_fq(X, amax)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(Xq_gpu.view(torch.int16).cpu().numpy(), Xq_ref.view(np.int16))
     assert torch.equal(H1, H2) and torch.equal(P1, P2)
+    H2, P2 = H2.cpu().numpy(), P2.cpu().numpy()
+    note("full-size c3: fused H and P against the oracle on every block column")
+    for n0 in range(0, wl.n_blocks, 4):
+        cols = slice(16 * n0, 16 * (n0 + 4))
+        Xn = wl._f64(wl.X[:, cols])
+        Xqn = wl._f64(Xq_ref[:, cols])
+        H_ref, P_ref = oracle.accumulate_act_aware(Xn, Xqn, wl.offsets)
+        assert_h_close(H2[:, n0:n0 + 4], H_ref)
+        assert_p_close(P2[:, n0:n0 + 4], P_ref, H_ref, cross_gram(Xn, Xqn, wl.offsets))

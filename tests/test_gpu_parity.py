@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 from parity_util import (assert_h_close, assert_imp_close, assert_p_close, assert_sweep_match,
-                         cross_gram)
+                         cross_gram, with_oracle_xq)
 
 pytestmark = pytest.mark.gpu
 
@@ -163,7 +163,7 @@ def test_accumulate_act_aware(name):
         Xq = (wl.X + 0.05 * r.standard_normal(wl.X.shape)).astype(np.float32)
         wl.Xq = Xq
     else:
-        wl = synth.make(name, **SMALL[name])
+        wl = with_oracle_xq(synth.make(name, **SMALL[name]))
     note(f"act-aware accumulate {name} X{wl.X.shape}")
     _, X, Xq, off = upload(wl)
     H, P = lh.lh_accumulate_act_aware(X, Xq, offsets=off)
@@ -213,6 +213,69 @@ def test_accumulate_fused_fake_quant_beta_and_zero_rows():
     lh.lh_accumulate_act_aware_fq(X[:0], amax, H=H, P=P, beta=0.5)
     torch.testing.assert_close(H, H0, rtol=1e-6, atol=0)
 
+@pytest.mark.parametrize("name", ["c3", "c1", "c5"])
+def test_activation_fake_quant_entry_point(name):
+    """lh_activation_fake_quant writes, bit for bit, the oracle's X_q (per-group amax, one group
+    saturating at 448 and one at amax 0), and the two-input accumulation fed that X_q equals the
+    fused one value for value."""
+    wl = synth.make(name, **SMALL[name])
+    G, bf16 = wl.n_groups, wl.dtype == "bf16"
+    X64 = wl.X_f64()
+    amax = np.array([np.abs(X64[wl.offsets[g]:wl.offsets[g + 1]]).max(initial=0.0) for g in range(G)])
+    if G > 2:
+        amax[1] *= 0.25
+        amax[2] = 0.0
+    amax = amax.astype(np.float32)
+    note(f"activation fake-quant {name} X{wl.X.shape} G={G} dtype={wl.dtype}")
+    _, X, _, off = upload(wl)
+    am = torch.from_numpy(amax).to(DEV)
+    Xq = lh.lh_activation_fake_quant(X, am, offsets=off)
+    ref = oracle.activation_fake_quant(X64, amax.astype(np.float64), wl.offsets, bf16=bf16)
+    got = Xq.float().cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(got, ref)
+    # signs of zero follow x (a negative x that quantizes to 0 gives -0, as the fp32 product does)
+    np.testing.assert_array_equal(np.signbit(got[got == 0]), np.signbit(ref[ref == 0]))
+    H1, P1 = lh.lh_accumulate_act_aware(X, Xq, offsets=off)
+    H2, P2 = lh.lh_accumulate_act_aware_fq(X, am, offsets=off)
+    assert torch.equal(H1, H2) and torch.equal(P1, P2)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_accumulate_act_aware_unrelated_xq(bf16):
+    """X_q far from X: a 9-12 binade gap (D with more than 16 significant bits), blocks where
+    X_q or X is zero, and X_q larger than X.  H and P within the 1e-5 Cauchy-Schwarz tolerance."""
+    r = np.random.default_rng(17)
+    rows, cin = 700, 96
+    X = r.normal(0, 1, (rows, cin)).astype(np.float32)
+    Xq = X * np.float32(2.0 ** -12) * (1 + r.integers(0, 7, (rows, cin))).astype(np.float32)
+    X[:, 1] = 1.0078125                          # the case 1 + 2^-7 against X * 2^-12
+    Xq[:, 1] = np.float32(1.0078125 * 2 ** -12)
+    Xq[:, 16:32] = 0.0                           # X_q zero block
+    X[:, 32:48] = 0.0                            # X zero block (D = X_q)
+    Xq[:, 48:64] = X[:, 48:64] * np.float32(512.0)   # X_q 9 binades above X
+    Xq[100:200, 64:80] = X[100:200, 64:80]       # rows where D = 0
+    if bf16:
+        Xs, Xqs = synth.bf16_bits_from_f32(X), synth.bf16_bits_from_f32(Xq)
+        X64, Xq64 = synth.f32_from_bf16_bits(Xs).astype(np.float64), synth.f32_from_bf16_bits(Xqs).astype(np.float64)
+        dt = "bf16"
+    else:
+        Xs, Xqs, X64, Xq64, dt = X, Xq, X.astype(np.float64), Xq.astype(np.float64), "f32"
+    off = np.array([0, rows])
+    note(f"act-aware accumulate, X_q unrelated to X, bf16={bf16}")
+    H, P = lh.lh_accumulate_act_aware(to_dev(Xs, dt), to_dev(Xqs, dt))
+    H_ref, P_ref = oracle.accumulate_act_aware(X64, Xq64, off)
+    R_ref = cross_gram(X64, Xq64, off)
+    assert_h_close(H.cpu().numpy(), H_ref)
+    assert_p_close(P.cpu().numpy(), P_ref, H_ref, R_ref)
+    # the same through the grouped kernel (rows split into three experts)
+    offg = np.array([0, 250, 250, rows])
+    Hg, Pg = lh.lh_accumulate_act_aware(to_dev(Xs, dt), to_dev(Xqs, dt), offsets=torch.from_numpy(offg).to(DEV))
+    H_ref, P_ref = oracle.accumulate_act_aware(X64, Xq64, offg)
+    R_ref = cross_gram(X64, Xq64, offg)
+    assert_h_close(Hg.cpu().numpy(), H_ref)
+    assert_p_close(Pg.cpu().numpy(), P_ref, H_ref, R_ref)
+
+
 # ------------------------------------------------------------------------------------ sweep
 def _oracle_h32(wl):
     """fp32 Hessians computed by the oracle: the identical input both sweeps receive."""
@@ -225,7 +288,7 @@ def _oracle_h32(wl):
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
 def test_sweep_full_parity(name):
-    wl = synth.make(name, **SMALL[name])
+    wl = with_oracle_xq(synth.make(name, **SMALL[name]))
     note(f"sweep {name} W{wl.W.shape} mode={wl.mode}")
     W, _, _, _ = upload(wl)
     H32, P32 = _oracle_h32(wl)
@@ -517,7 +580,7 @@ def test_sweep_deterministic():
 @pytest.mark.parametrize("name", list(SMALL))
 def test_end_to_end(name):
     """absmax -> accumulate -> sweep entirely on the GPU, against the oracle's own float64 path."""
-    wl = synth.make(name, **SMALL[name])
+    wl = with_oracle_xq(synth.make(name, **SMALL[name]))
     note(f"end-to-end {name}")
     W, X, Xq, off = upload(wl)
     amax = lh.lh_absmax(W)

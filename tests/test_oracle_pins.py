@@ -48,6 +48,104 @@ def test_global_and_candidate_scales_are_fp32_roundings():
     assert abs(6 * s[-1] - float(amax)) <= 2 * 6 * np.spacing(np.float32(s[-1]))
 
 
+# ------------------------------------------------------------------ max calibration (absmax)
+def _pin_absmax(absmax_fn):
+    """max |W_g| per group, checked against an element-by-element walk over exact values that
+    never calls abs(): each element's magnitude is decided by a comparison with zero."""
+    r = rng(21)
+    W = r.normal(0, 0.02, (5, 7, 32)).astype(np.float32).astype(np.float64)
+    W[0, 3, 5] = -0.5                       # group 0: its largest magnitude is negative
+    W[1] = np.abs(W[1])                     # group 1: all positive
+    W[2] = -np.abs(W[2])                    # group 2: all negative
+    W[3] = 0.0
+    W[3, 0, 0] = -0.0                       # group 3: zeros, one of them -0
+    W[4, 6, 31] = 0.25                      # group 4: the max is the last element
+    got = absmax_fn(W)
+    assert got.shape == (5,)
+    for g in range(5):
+        best = 0.0
+        for x in W[g].reshape(-1).tolist():
+            mag = -x if x < 0 else x
+            if mag > best:
+                best = mag
+        assert got[g] == best, (g, got[g], best)
+    assert got[0] == 0.5 and got[3] == 0.0 and not np.signbit(got[3]) and got[4] == 0.25
+    # groups are independent: changing one group changes only its own amax
+    W2 = W.copy()
+    W2[1, 0, 0] = 7.0
+    got2 = absmax_fn(W2)
+    assert got2[1] == 7.0 and np.array_equal(np.delete(got2, 1), np.delete(got, 1))
+    # an empty group (no elements) gives 0
+    assert np.array_equal(absmax_fn(np.zeros((3, 0))), np.zeros(3))
+
+
+def test_absmax_against_elementwise_walk():
+    _pin_absmax(oracle.absmax)
+
+
+def _pin_accumulate_beta(accumulate_fn):
+    """Streaming form H = beta H_prev + (1/T) sum_t x_t x_t^T and imp = beta imp_prev + sum_t x_t^2,
+    each entry checked against a correctly rounded scalar sum (math.fsum) of the definition, with
+    H_prev and imp_prev unrelated to the new batch; an empty group keeps only the beta term."""
+    import math
+    r = rng(22)
+    cin = 32
+    X = r.normal(0, 1, (11, cin))
+    off = np.array([0, 7, 7, 11])            # groups of 7, 0 and 4 rows
+    G = 3
+    H_prev = r.normal(0, 1, (G, cin // 16, 16, 16))
+    imp_prev = r.uniform(0, 5, (G, cin))
+    for beta in (0.5, -1.25, 1.0):
+        H, imp = accumulate_fn(X, off, beta=beta, H_prev=H_prev, imp_prev=imp_prev, want_h=True, want_imp=True)
+        for g in range(G):
+            rows = X[off[g]:off[g + 1]]
+            T = len(rows)
+            for n in range(cin // 16):
+                for i in range(16):
+                    for j in range(16):
+                        s = math.fsum(rows[t, 16 * n + i] * rows[t, 16 * n + j] for t in range(T))
+                        want = beta * H_prev[g, n, i, j] + (s / T if T else 0.0)
+                        assert abs(H[g, n, i, j] - want) <= 1e-13 * (abs(want) + 1.0), (beta, g, n, i, j)
+            for i in range(cin):
+                want = beta * imp_prev[g, i] + math.fsum(rows[t, i] ** 2 for t in range(T))
+                assert abs(imp[g, i] - want) <= 1e-13 * (abs(want) + 1.0), (beta, g, i)
+
+
+def test_accumulate_beta_against_closed_form():
+    _pin_accumulate_beta(oracle.accumulate)
+
+
+def test_pins_catch_planted_mistakes():
+    """Each pin above fails on a plausible slip planted in a copy of the oracle function."""
+    def no_abs(W):                                   # max instead of max |.|
+        W = np.asarray(W, dtype=np.float64)
+        return W.reshape(W.shape[0], -1).max(axis=1) if W.size else np.zeros(W.shape[0])
+
+    def first_group_only(W):                         # one amax for every group
+        a = oracle.absmax(W)
+        return np.full_like(a, a[0]) if a.size else a
+
+    for planted in (no_abs, first_group_only):
+        with pytest.raises(AssertionError):
+            _pin_absmax(planted)
+
+    def beta_ignored(X, off, beta=0.0, H_prev=None, imp_prev=None, **kw):
+        return oracle.accumulate(X, off, beta=1.0 if beta != 0 else 0.0, H_prev=H_prev, imp_prev=imp_prev, **kw)
+
+    def beta_on_new_term(X, off, beta=0.0, H_prev=None, imp_prev=None, **kw):
+        H, imp = oracle.accumulate(X, off, **kw)
+        return H_prev + beta * H, imp_prev + beta * imp
+
+    def imp_divided_by_t(X, off, beta=0.0, H_prev=None, imp_prev=None, **kw):
+        H, imp = oracle.accumulate(X, off, beta=beta, H_prev=H_prev, imp_prev=imp_prev, **kw)
+        T = np.maximum(np.diff(off), 1)[:, None]
+        return H, beta * imp_prev + (imp - beta * imp_prev) / T
+
+    for planted in (beta_ignored, beta_on_new_term, imp_divided_by_t):
+        with pytest.raises(AssertionError):
+            _pin_accumulate_beta(planted)
+
+
 # ------------------------------------------------------------------ P2: E2M1 rounding
 def _exact_index(w: float, s: float) -> int:
     if s == 0:
@@ -460,15 +558,6 @@ def test_activation_fake_quant_matches_exact_rationals(bf16):
         for row in range(6):
             np.testing.assert_array_equal(got[row], _exact_act_fq(x[row], a, bf16))
     assert np.all(oracle.activation_fake_quant(x.astype(np.float64), [0.0], np.array([0, 6]), bf16) == 0.0)
-
-
-def test_activation_fake_quant_agrees_with_generator_recipe():
-    """The generator's own quantizer (which makes the activation-aware workload's X_q input) and
-    the oracle's, written independently, give the same X_q."""
-    wl = synth.make("c3", cout=8, cin=96, rows=530)
-    X = wl.X_f64()
-    got = oracle.activation_fake_quant(X, [np.abs(X).max()], np.array([0, X.shape[0]]), bf16=True)
-    np.testing.assert_array_equal(got, wl.Xq_f64())
 
 
 def test_activation_fake_quant_is_on_the_grid_and_per_group():
