@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LH_VERSION 4
+#define LH_VERSION 5
 
 typedef enum {
   LH_OK = 0,
@@ -130,6 +130,29 @@ lh_status lh_activation_fake_quant(const void* X, lh_dtype dtype, int64_t rows, 
                                    void* Xq, void* stream);
 
 /*
+ * Options of the weight-scale search, taken by the *_ex entry points (the others use the
+ * defaults: 448-normalized scaling and all 126 candidates).
+ *   scale_norm     the E4M3 value the global amax maps to: g = fp32(global_amax / (6 * scale_norm)).
+ *                  448 is NVFP4's scaling, 256 that of its "4/6" variant ("Add composable scale
+ *                  calibration to GPTQ", What does this PR do?: 448-normalized scaling, 4/6 uses
+ *                  256).  It must be one of the 126 positive finite E4M3 values.
+ *   n_multipliers  0: the FP8 scale sweep over all 126 candidates.  1..128: the amax-multiplier
+ *                  search ("add local hessian calibration", Changes: configurable step size and
+ *                  multipliers for the amax search): a block of amax a = max_i |w_i| takes only the
+ *                  candidates whose code is the positive finite E4M3 value nearest to the exact
+ *                  a * m / (6 g) for one of the multipliers m (ties to the even code, saturating
+ *                  at 448 and at 2^-9), and keeps the lowest-loss one of those (lowest code on
+ *                  ties, which is the first in an ascending grid).
+ *   multipliers    HOST array of n_multipliers positive finite values, any order (a grid
+ *                  start + j * step is the usual choice), read during the call.
+ */
+typedef struct {
+  float scale_norm;
+  int32_t n_multipliers;
+  const float* multipliers;
+} lh_sweep_options;
+
+/*
  * Exhaustive FP8 block-scale sweep with the local-Hessian objective (PR #788, review: block loss
  * cnb,nbd,cnd->cn; PR #1976, review: dw = quant(w) - w, coupling term 2 dw^T (P W0) with
  * P.W0 = nbd,cnd->cnb, best_loss = inf so negative losses are handled; PR #2283, How: the 126
@@ -159,6 +182,17 @@ lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int6
                          uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream);
 
 /*
+ * lh_scale_sweep with options (see lh_sweep_options; NULL = the defaults, identical to
+ * lh_scale_sweep).  Errors as lh_scale_sweep, plus INVALID_ARGUMENT for a scale_norm that is not
+ * a positive finite E4M3 value, n_multipliers outside [0, 128], a NULL multipliers array with
+ * n_multipliers > 0, or a multiplier that is not positive and finite.
+ */
+lh_status lh_scale_sweep_ex(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                            int64_t cin, const float* global_amax, const float* H, const float* P,
+                            const lh_sweep_options* options, uint8_t* scale_code, uint8_t* fp4,
+                            float* best_loss, void* stream);
+
+/*
  * Same sweep scored by the importance-weighted error L_k = sum_i imp[g][16n+i] * e_{k,i}^2
  * (PR #2283, What / How: H replaced by diag(Imp), einsum cnb,nb->cn, no diag_embed and no
  * matmul on the hot path).  A block whose importance sums to zero uses Imp = 1.
@@ -180,6 +214,15 @@ lh_status lh_scale_sweep_mse(const void* W, lh_dtype w_dtype, int64_t n_groups, 
                              float* best_loss, void* stream);
 
 /*
+ * lh_scale_sweep_diag with options (see lh_sweep_options); imp may be NULL for the plain-MSE
+ * objective of lh_scale_sweep_mse.  Errors as lh_scale_sweep_ex.
+ */
+lh_status lh_scale_sweep_diag_ex(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                                 int64_t cin, const float* global_amax, const float* imp,
+                                 const lh_sweep_options* options, uint8_t* scale_code, uint8_t* fp4,
+                                 float* best_loss, void* stream);
+
+/*
  * Fake-quantized weights and per-block amax from a sweep's result: the calibrated quantizer state
  * ("Add WMSE weight scale search calibration": the shared-path check fingerprints the quantizers'
  * amax and scales and the final fake-quantized weights):
@@ -197,6 +240,15 @@ lh_status lh_scale_sweep_mse(const void* W, lh_dtype w_dtype, int64_t n_groups, 
 lh_status lh_dequantize(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
                         int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
                         void* Wq, float* block_amax, void* stream);
+
+/*
+ * lh_dequantize for codes a sweep chose under scale_norm (see lh_sweep_options):
+ * s_k = fp32(v_k * fp32(global_amax[g] / (6 * scale_norm))).  Errors as lh_dequantize, plus
+ * INVALID_ARGUMENT for a scale_norm that is not a positive finite E4M3 value.
+ */
+lh_status lh_dequantize_ex(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
+                           int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
+                           float scale_norm, void* Wq, float* block_amax, void* stream);
 
 /*
  * Per-group absolute maximum amax_out[g] = max |W_g| over elems_per_group elements: the max

@@ -22,8 +22,15 @@ LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_activation_fake_quant",
-            "lh_dequantize", "lh_scale_sweep", "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_absmax",
-            "lh_last_error", "lh_version")
+            "lh_dequantize", "lh_dequantize_ex", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag",
+            "lh_scale_sweep_diag_ex", "lh_scale_sweep_mse", "lh_absmax", "lh_last_error", "lh_version")
+MAX_MULTIPLIERS = 128
+
+
+class SweepOptions(ctypes.Structure):
+    """lh_sweep_options: scale_norm (448 or 256 for "4/6"), the amax multipliers (host array)."""
+    _fields_ = [("scale_norm", ctypes.c_float), ("n_multipliers", ctypes.c_int32),
+                ("multipliers", ctypes.POINTER(ctypes.c_float))]
 
 
 class LHError(RuntimeError):
@@ -51,11 +58,15 @@ def lib() -> ctypes.CDLL:
         h.lh_activation_fake_quant.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, vp]
         h.lh_scale_sweep.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_diag.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        h.lh_scale_sweep_ex.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+        h.lh_scale_sweep_diag_ex.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        h.lh_dequantize_ex.argtypes = [vp, vp, i32, i64, i64, i64, vp, f32, vp, vp, vp]
         h.lh_scale_sweep_mse.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
         h.lh_absmax.argtypes = [vp, i32, i64, i64, vp, vp]
         h.lh_dequantize.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
-                  "lh_activation_fake_quant", "lh_scale_sweep",
+                  "lh_activation_fake_quant", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag_ex",
+                  "lh_dequantize_ex",
                   "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_absmax", "lh_dequantize"):
             getattr(h, f).restype = ctypes.c_int
         h.lh_last_error.argtypes = []
@@ -257,11 +268,61 @@ def lh_scale_sweep_mse(W: torch.Tensor, amax: torch.Tensor, code: Optional[torch
     return code, fp4, loss
 
 
+def _options(norm: float, multipliers):
+    """(ctypes options, keep-alive array) for the *_ex entry points."""
+    import array
+    m = array.array("f", [] if multipliers is None else [float(x) for x in multipliers])
+    buf = (ctypes.c_float * max(1, len(m)))(*m) if len(m) else None
+    opt = SweepOptions(float(norm), len(m), ctypes.cast(buf, ctypes.POINTER(ctypes.c_float)) if buf else None)
+    return opt, buf
+
+
+def lh_scale_sweep_ex(W: torch.Tensor, amax: torch.Tensor, H: torch.Tensor, P: Optional[torch.Tensor] = None,
+                      code: Optional[torch.Tensor] = None, fp4: Optional[torch.Tensor] = None,
+                      loss: Optional[torch.Tensor] = None, *, norm: float = 448.0, multipliers=None,
+                      want_fp4: bool = True, want_loss: bool = True):
+    """lh_scale_sweep with the global scale normalized to `norm` (448, or 256 for "4/6") and, when
+    `multipliers` is given (at most 128 positive values), the amax-multiplier search."""
+    W = _as3d(W)
+    _need(W, "W")
+    G, cout, cin = W.shape
+    _need(amax, "amax", (G,), torch.float32)
+    _need(H, "H", (G, cin // 16, 16, 16), torch.float32)
+    if P is not None:
+        _need(P, "P", (G, cin // 16, 16, 16), torch.float32)
+    code, fp4, loss = _sweep_outputs(W, code, fp4, loss, want_fp4, want_loss)
+    opt, keep = _options(norm, multipliers)
+    _check(lib().lh_scale_sweep_ex(_ptr(W), _dtype_code(W), G, cout, cin, _ptr(amax), _ptr(H), _ptr(P),
+                                   ctypes.byref(opt), _ptr(code), _ptr(fp4), _ptr(loss), _stream(W.device)))
+    del keep
+    return code, fp4, loss
+
+
+def lh_scale_sweep_diag_ex(W: torch.Tensor, amax: torch.Tensor, imp: Optional[torch.Tensor],
+                           code: Optional[torch.Tensor] = None, fp4: Optional[torch.Tensor] = None,
+                           loss: Optional[torch.Tensor] = None, *, norm: float = 448.0, multipliers=None,
+                           want_fp4: bool = True, want_loss: bool = True):
+    """lh_scale_sweep_diag (imp None: plain MSE) with the options of lh_scale_sweep_ex."""
+    W = _as3d(W)
+    _need(W, "W")
+    G, cout, cin = W.shape
+    _need(amax, "amax", (G,), torch.float32)
+    if imp is not None:
+        _need(imp, "imp", (G, cin), torch.float32)
+    code, fp4, loss = _sweep_outputs(W, code, fp4, loss, want_fp4, want_loss)
+    opt, keep = _options(norm, multipliers)
+    _check(lib().lh_scale_sweep_diag_ex(_ptr(W), _dtype_code(W), G, cout, cin, _ptr(amax), _ptr(imp),
+                                        ctypes.byref(opt), _ptr(code), _ptr(fp4), _ptr(loss), _stream(W.device)))
+    del keep
+    return code, fp4, loss
+
+
 def lh_dequantize(code: torch.Tensor, fp4: torch.Tensor, amax: torch.Tensor, dtype: torch.dtype = torch.bfloat16,
                   Wq: Optional[torch.Tensor] = None, block_amax: Optional[torch.Tensor] = None,
-                  want_wq: bool = True, want_block_amax: bool = True):
+                  want_wq: bool = True, want_block_amax: bool = True, norm: float = 448.0):
     """Fake-quantized weights Wq [G, cout, cin] (bf16 or fp32) and per-block amax [G, cout, cin/16]
-    from the sweep's scale codes and FP4 nibbles."""
+    from the sweep's scale codes and FP4 nibbles (norm: the sweep's scale normalization, through
+    lh_dequantize_ex when it is not 448)."""
     if code.dim() != 3:
         raise ValueError("code must be [G, cout, cin/16]")
     G, cout, nb = code.shape
@@ -279,8 +340,12 @@ def lh_dequantize(code: torch.Tensor, fp4: torch.Tensor, amax: torch.Tensor, dty
         _need(Wq, "Wq", (G, cout, cin), dtype)
     if block_amax is not None:
         _need(block_amax, "block_amax", (G, cout, nb), torch.float32)
-    _check(lib().lh_dequantize(_ptr(code), _ptr(fp4), 1 if dtype == torch.bfloat16 else 0, G, cout, cin,
-                               _ptr(amax), _ptr(Wq), _ptr(block_amax), _stream(code.device)))
+    if norm == 448.0:
+        _check(lib().lh_dequantize(_ptr(code), _ptr(fp4), 1 if dtype == torch.bfloat16 else 0, G, cout, cin,
+                                   _ptr(amax), _ptr(Wq), _ptr(block_amax), _stream(code.device)))
+    else:
+        _check(lib().lh_dequantize_ex(_ptr(code), _ptr(fp4), 1 if dtype == torch.bfloat16 else 0, G, cout, cin,
+                                      _ptr(amax), float(norm), _ptr(Wq), _ptr(block_amax), _stream(code.device)))
     return Wq, block_amax
 
 

@@ -2,7 +2,8 @@
 // calibration leaves behind ("Add WMSE weight scale search calibration": the refactor check
 // compares the quantizers' amax and scales and the final fake-quantized weights bit for bit).
 //
-//   g   = fp32(global_amax[g] / (6*448)),  s = fp32(v_code * g)  (the sweep's own scale)
+//   g   = fp32(global_amax[g] / (6*norm)),  s = fp32(v_code * g)  (the sweep's own scale; norm
+//         448, or 256 for the "4/6" variant of "Add composable scale calibration to GPTQ")
 //   Wq  = sign * E2M1 value of the nibble * s, rounded to fp32, then to nearest-even bf16 for a
 //         bf16 output
 //   block_amax = fp32(6 s)
@@ -31,11 +32,11 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
                                                          const float* __restrict__ amax,
                                                          int64_t per_group, int64_t n_blocks,
                                                          void* __restrict__ Wq,
-                                                         float* __restrict__ block_amax) {
+                                                         float* __restrict__ block_amax, float gdiv) {
   const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (b >= n_blocks) return;
   const int64_t g = b / per_group;
-  const float gs = (float)((double)amax[g] / 2688.0);
+  const float gs = (float)((double)amax[g] / (double)gdiv);
   const float s = (float)(e4m3_byte_value(code[b]) * (double)gs);
   if (block_amax) block_amax[b] = 6.0f * s;
   if (!Wq) return;
@@ -77,15 +78,15 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* __restri
 }  // namespace
 
 hipError_t launch_dequantize(const uint8_t* code, const uint8_t* fp4, const float* amax, int64_t n_groups,
-                             int64_t cout, int64_t cin, bool bf16, void* Wq, float* block_amax,
+                             int64_t cout, int64_t cin, bool bf16, void* Wq, float* block_amax, float gdiv,
                              hipStream_t stream) {
   const int64_t per_group = cout * (cin / 16), n = n_groups * per_group;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
   if (bf16)
-    hipLaunchKernelGGL(k_dequantize<true>, grid, dim3(kThreads), 0, stream, code, fp4, amax, per_group, n, Wq, block_amax);
+    hipLaunchKernelGGL(k_dequantize<true>, grid, dim3(kThreads), 0, stream, code, fp4, amax, per_group, n, Wq, block_amax, gdiv);
   else
-    hipLaunchKernelGGL(k_dequantize<false>, grid, dim3(kThreads), 0, stream, code, fp4, amax, per_group, n, Wq, block_amax);
+    hipLaunchKernelGGL(k_dequantize<false>, grid, dim3(kThreads), 0, stream, code, fp4, amax, per_group, n, Wq, block_amax, gdiv);
   return hipGetLastError();
 }
 

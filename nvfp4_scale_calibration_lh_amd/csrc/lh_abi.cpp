@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -240,6 +241,33 @@ lh_status check_sweep_shapes(int64_t n_groups, int64_t cout, int64_t cin) {
   return LH_OK;
 }
 
+// The launch options of a sweep from the caller's: the divisor 6 * norm (norm must be one of the
+// 126 positive finite E4M3 values, so 6 * norm is exact in fp32) and the multipliers, copied.
+lh_status sweep_opts(const lh_sweep_options* in, lh::SweepOpts* out) {
+  std::memset(out, 0, sizeof(*out));
+  out->gdiv = 6.0f * 448.0f;
+  if (!in) return LH_OK;
+  const float norm = in->scale_norm;
+  bool e4m3 = false;
+  for (int k = 1; k <= 126 && !e4m3; ++k) {
+    const int e = k >> 3, m = k & 7;
+    const float v = e == 0 ? std::ldexp((float)m, -9) : std::ldexp(1.0f + (float)m / 8.0f, e - 7);
+    e4m3 = (v == norm);
+  }
+  if (!e4m3) return fail(LH_ERR_INVALID_ARGUMENT, "scale_norm must be a positive finite E4M3 value such as 448 or 256 (got %g)", (double)norm);
+  out->gdiv = 6.0f * norm;
+  if (in->n_multipliers < 0 || in->n_multipliers > lh::kMaxMultipliers)
+    return fail(LH_ERR_INVALID_ARGUMENT, "n_multipliers must be in [0, %d] (got %d)", lh::kMaxMultipliers, (int)in->n_multipliers);
+  if (in->n_multipliers > 0 && !in->multipliers) return fail(LH_ERR_INVALID_ARGUMENT, "multipliers is NULL");
+  for (int j = 0; j < in->n_multipliers; ++j) {
+    const float m = in->multipliers[j];
+    if (!(m > 0.0f) || !std::isfinite(m)) return fail(LH_ERR_INVALID_ARGUMENT, "multiplier %d is not a positive finite number", j);
+    out->mult[j] = m;
+  }
+  out->nm = in->n_multipliers;
+  return LH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -307,14 +335,17 @@ lh_status lh_activation_fake_quant(const void* X, lh_dtype dtype, int64_t rows, 
   return ok();
 }
 
-lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
-                         int64_t cin, const float* global_amax, const float* H, const float* P,
-                         uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {
+lh_status lh_scale_sweep_ex(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                            int64_t cin, const float* global_amax, const float* H, const float* P,
+                            const lh_sweep_options* options, uint8_t* scale_code, uint8_t* fp4,
+                            float* best_loss, void* stream) {
   if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);
   lh_status st = check_sweep_shapes(n_groups, cout, cin);
   if (st != LH_OK) return st;
   if (!global_amax || !H || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax, H and scale_code are required");
   if (!W && cout > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
+  lh::SweepOpts opts;
+  if ((st = sweep_opts(options, &opts)) != LH_OK) return st;
   int dev = -1;
   st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {H, "H"}, {P, "P"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
   if (st != LH_OK) return st;
@@ -323,19 +354,29 @@ lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int6
   DeviceGuard guard;
   if ((st = guard.enter(dev)) != LH_OK) return st;
   hipError_t e = lh::launch_sweep(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, H, P,
-                                  scale_code, fp4, best_loss, reinterpret_cast<hipStream_t>(stream));
+                                  scale_code, fp4, best_loss, opts, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "sweep launch");
   return ok();
 }
 
-lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
-                              int64_t cin, const float* global_amax, const float* imp,
-                              uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {
+lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                         int64_t cin, const float* global_amax, const float* H, const float* P,
+                         uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {
+  return lh_scale_sweep_ex(W, w_dtype, n_groups, cout, cin, global_amax, H, P, nullptr, scale_code, fp4,
+                           best_loss, stream);
+}
+
+lh_status lh_scale_sweep_diag_ex(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                                 int64_t cin, const float* global_amax, const float* imp,
+                                 const lh_sweep_options* options, uint8_t* scale_code, uint8_t* fp4,
+                                 float* best_loss, void* stream) {
   if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);
   lh_status st = check_sweep_shapes(n_groups, cout, cin);
   if (st != LH_OK) return st;
-  if (!global_amax || !imp || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax, imp and scale_code are required");
+  if (!global_amax || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax and scale_code are required");
   if (!W && cout > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
+  lh::SweepOpts opts;
+  if ((st = sweep_opts(options, &opts)) != LH_OK) return st;
   int dev = -1;
   st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {imp, "imp"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
   if (st != LH_OK) return st;
@@ -343,40 +384,38 @@ lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups,
   DeviceGuard guard;
   if ((st = guard.enter(dev)) != LH_OK) return st;
   hipError_t e = lh::launch_sweep_diag(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, imp,
-                                       scale_code, fp4, best_loss, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "diagonal sweep launch");
+                                       scale_code, fp4, best_loss, opts, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, imp ? "diagonal sweep launch" : "plain-MSE sweep launch");
   return ok();
+}
+
+lh_status lh_scale_sweep_diag(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
+                              int64_t cin, const float* global_amax, const float* imp,
+                              uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {
+  if (!imp) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax, imp and scale_code are required");
+  return lh_scale_sweep_diag_ex(W, w_dtype, n_groups, cout, cin, global_amax, imp, nullptr, scale_code, fp4,
+                                best_loss, stream);
 }
 
 lh_status lh_scale_sweep_mse(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
                              int64_t cin, const float* global_amax, uint8_t* scale_code, uint8_t* fp4,
                              float* best_loss, void* stream) {
-  if (!dtype_ok(w_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)w_dtype);
-  lh_status st = check_sweep_shapes(n_groups, cout, cin);
-  if (st != LH_OK) return st;
-  if (!global_amax || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax and scale_code are required");
-  if (!W && cout > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
-  int dev = -1;
-  st = check_pointers({{W, "W"}, {global_amax, "global_amax"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
-  if (st != LH_OK) return st;
-  if ((st = check_aligned(W, "W")) != LH_OK) return st;
-  DeviceGuard guard;
-  if ((st = guard.enter(dev)) != LH_OK) return st;
-  hipError_t e = lh::launch_sweep_diag(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, nullptr,
-                                       scale_code, fp4, best_loss, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "plain-MSE sweep launch");
-  return ok();
+  return lh_scale_sweep_diag_ex(W, w_dtype, n_groups, cout, cin, global_amax, nullptr, nullptr, scale_code, fp4,
+                                best_loss, stream);
 }
 
-lh_status lh_dequantize(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
-                        int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
-                        void* Wq, float* block_amax, void* stream) {
+lh_status lh_dequantize_ex(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
+                           int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
+                           float scale_norm, void* Wq, float* block_amax, void* stream) {
   if (!dtype_ok(out_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)out_dtype);
   lh_status st = check_sweep_shapes(n_groups, cout, cin);
   if (st != LH_OK) return st;
   if (!scale_code || !global_amax) return fail(LH_ERR_INVALID_ARGUMENT, "scale_code and global_amax are required");
   if (!Wq && !block_amax) return fail(LH_ERR_INVALID_ARGUMENT, "at least one of Wq, block_amax must be given");
   if (Wq && !fp4) return fail(LH_ERR_INVALID_ARGUMENT, "fp4 is required for Wq");
+  lh_sweep_options o{scale_norm, 0, nullptr};
+  lh::SweepOpts opts;
+  if ((st = sweep_opts(&o, &opts)) != LH_OK) return st;
   int dev = -1;
   st = check_pointers({{scale_code, "scale_code"}, {fp4, "fp4"}, {global_amax, "global_amax"}, {Wq, "Wq"}, {block_amax, "block_amax"}}, &dev);
   if (st != LH_OK) return st;
@@ -385,9 +424,16 @@ lh_status lh_dequantize(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype 
   DeviceGuard guard;
   if ((st = guard.enter(dev)) != LH_OK) return st;
   hipError_t e = lh::launch_dequantize(scale_code, fp4, global_amax, n_groups, cout, cin, out_dtype == LH_DTYPE_BF16,
-                                       Wq, block_amax, reinterpret_cast<hipStream_t>(stream));
+                                       Wq, block_amax, opts.gdiv, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "dequantize launch");
   return ok();
+}
+
+lh_status lh_dequantize(const uint8_t* scale_code, const uint8_t* fp4, lh_dtype out_dtype,
+                        int64_t n_groups, int64_t cout, int64_t cin, const float* global_amax,
+                        void* Wq, float* block_amax, void* stream) {
+  return lh_dequantize_ex(scale_code, fp4, out_dtype, n_groups, cout, cin, global_amax, 448.0f, Wq, block_amax,
+                          stream);
 }
 
 lh_status lh_absmax(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t elems_per_group,

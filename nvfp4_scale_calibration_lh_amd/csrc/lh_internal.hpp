@@ -37,17 +37,29 @@ hipError_t launch_accumulate(const void* X, const void* Xq, const float* x_amax,
 hipError_t launch_act_fake_quant(const void* X, bool bf16, int64_t rows, int64_t cin, const int64_t* offsets,
                                  int64_t n_groups, const float* x_amax, void* Xq, hipStream_t stream);
 
+// Options of one sweep launch, passed to the kernels by value: the divisor of the global scale,
+// g = fp32(amax / gdiv) with gdiv = 6 * norm (norm an E4M3 value, so gdiv is exact in fp32), and
+// the amax-multiplier grid (nm = 0: every one of the 126 candidates; otherwise a block takes only
+// the codes its nm multipliers propose).
+constexpr int kMaxMultipliers = 128;
+struct SweepOpts {
+  float gdiv;
+  int nm;
+  float mult[kMaxMultipliers];
+};
+
 hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout, int64_t cin,
                         const float* amax, const float* H, const float* P, uint8_t* code,
-                        uint8_t* fp4, float* loss, hipStream_t stream);
+                        uint8_t* fp4, float* loss, const SweepOpts& opts, hipStream_t stream);
 
 hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t cout,
                              int64_t cin, const float* amax, const float* imp, uint8_t* code,
-                             uint8_t* fp4, float* loss, hipStream_t stream);
+                             uint8_t* fp4, float* loss, const SweepOpts& opts, hipStream_t stream);
 
-// Wq (bf16 or fp32, may be NULL) and block_amax (may be NULL) from scale codes and FP4 nibbles.
+// Wq (bf16 or fp32, may be NULL) and block_amax (may be NULL) from scale codes and FP4 nibbles;
+// g = fp32(amax / gdiv) as in the sweep.
 hipError_t launch_dequantize(const uint8_t* code, const uint8_t* fp4, const float* amax, int64_t n_groups,
-                             int64_t cout, int64_t cin, bool bf16, void* Wq, float* block_amax,
+                             int64_t cout, int64_t cin, bool bf16, void* Wq, float* block_amax, float gdiv,
                              hipStream_t stream);
 
 }  // namespace lh

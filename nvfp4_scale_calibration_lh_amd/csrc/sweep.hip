@@ -48,6 +48,13 @@
 //    diagonal form needs no such override (see k_sweep_diag).  A winner's nibbles are always
 //    exact rounding decisions and its reported loss is evaluated again from them.  The result
 //    is the argmin of the float64 objective.
+//  * Options (SweepOpts): the global scale's normalization, g = fp32(amax / (6 norm)) with norm
+//    448 or 256 (the "4/6" variant, "Add composable scale calibration to GPTQ"), and the
+//    amax-multiplier search ("add local hessian calibration", Changes: configurable step size and
+//    multipliers): a block of amax a then takes only the candidates whose code is the E4M3 value
+//    nearest to a m / (6 g) for one of its multipliers m; the others score +inf before the
+//    filter and the float64 passes.  Each row marks the proposed codes in a per-wave LDS table
+//    tagged with the row, so a lane reads its own codes' flags.
 #include "lh_internal.hpp"
 
 #include <type_traits>
@@ -80,7 +87,9 @@ __device__ inline double e4m3_value(int k) {
   return (double)(8 + m) * __longlong_as_double((long long)(e - 10 + 1023) << 52);
 }
 
-__device__ inline float global_scale(float amax) { return (float)((double)amax / 2688.0); }
+// g = fp32(amax / gdiv), gdiv = 6 * norm exact in fp32: one float64 divide rounded to fp32 is the
+// correctly rounded quotient.
+__device__ inline float global_scale(float amax, float gdiv) { return (float)((double)amax / (double)gdiv); }
 __device__ inline float cand_scale(int k, float g) { return (float)(e4m3_value(k) * (double)g); }
 __device__ inline float inv_scale(float s) { return s > 0.0f ? (float)(1.0 / (double)s) : 0.0f; }
 // The float32 filter is used only where scales and quotients stay normal and finite.
@@ -105,6 +114,45 @@ __device__ inline double exact_err(float wf, float s, int* nib) {
   const double mag = e2m1_value(c) * (double)s;
   *nib = c | (wf < 0.0f ? 8 : 0);
   return (wf < 0.0f ? -mag : mag) - w;
+}
+
+// Code (1..126) of the positive E4M3 value nearest to am / g6, ties to the even code, saturating
+// at 448 and at 2^-9: the candidate a multiplier m proposes for a block of amax a (am = a m, exact
+// in float64, at most 48 bits; g6 = 6 g exact, ig6 ~ 1/g6).  The float64 quotient only places y
+// in its binade and between two neighbouring values j, j + 1 (it is within 2^-51 of the exact
+// one, so an estimate off by one is off next to a value, far from their midpoint); the choice
+// between j and j + 1 is the sign of am - (2j + 1) 2^(e-4) g6, both terms exact in float64
+// (the midpoint has at most 6 significant bits, g6 at most 26).
+__device__ inline int mult_code(double am, double g6, double ig6) {
+  if (!(am > 0.0)) return 1;                 // zero block: every candidate is 0; lowest code
+  const double y = am * ig6;
+  if (!(y < 448.0)) return 126;              // saturation (also g6 == 0)
+  const int e = max(ilogb(y), -6);           // value spacing 2^(e-3); subnormal below 2^-6
+  const double t = ldexp(y, 3 - e);          // in [0, 16]
+  int j = (int)floor(t);
+  const double mid = ldexp((double)(2 * j + 1), e - 4) * g6;
+  if (am > mid || (am == mid && (j & 1))) ++j;
+  return min(max(((e + 7) << 3) + j - 8, 1), 126);   // code of j 2^(e-3), valid for j in [0, 16]
+}
+
+// Multiplier search: marks in mk (this wave's 128-entry table) the codes the lane's multipliers
+// m0, m1 (0: none) propose for a block of amax ab, tagged with `tag` (unique per block), and
+// returns whether codes k0 and k1 (0: none) are proposed.  Wave-wide: every lane must call it.
+__device__ inline void mark_allowed(float ab, double g6, double ig6, float m0, float m1, int tag, int* mk,
+                                   int k0, int k1, bool& a0, bool& a1) {
+  if (m0 != 0.0f) mk[mult_code((double)ab * (double)m0, g6, ig6)] = tag;
+  if (m1 != 0.0f) mk[mult_code((double)ab * (double)m1, g6, ig6)] = tag;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  a0 = k0 > 0 && mk[k0] == tag;
+  a1 = k1 > 0 && mk[k1] == tag;
+}
+
+// The lane's two multipliers (lane and lane + 64 of the grid; 0 where the grid has none).
+__device__ inline void lane_multipliers(const SweepOpts& o, int lane, float& m0, float& m1) {
+  m0 = lane < o.nm ? o.mult[lane] : 0.0f;
+  m1 = lane + 64 < o.nm ? o.mult[lane + 64] : 0.0f;
 }
 
 // True when |w|/s_k may lie within a few ulps of an E2M1 midpoint m for some candidate k:
@@ -277,6 +325,8 @@ struct FullLds {
   int kw[16];          // winner's code per row       }
   unsigned short wn[16][4];   // winner's signed nibbles per row and lane group (override rows)
   double ex[4][16];    // float64 refinement: e of up to 4 contenders
+  float ab[16];        // block amax per row of the tile (multiplier search)
+  int mk[128];         // codes proposed by the multipliers, tagged with the row
 };
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -318,7 +368,7 @@ template <bool BF16, bool COUPLED, bool EQUALIZE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
-    uint8_t* __restrict__ fp4, float* __restrict__ loss, int rows_per_wave) {
+    uint8_t* __restrict__ fp4, float* __restrict__ loss, int rows_per_wave, const SweepOpts opt) {
   __shared__ FullLds lds_all[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   FullLds& L = lds_all[wave];
@@ -382,8 +432,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // The filter's fp32 values stay finite and normal-range for every candidate when |H|, |P| <=
   // 2^100 and g^2 max(|H|, |P|) <= 2^76 (quotients |w|/s <= 2^20.4, |e| <= 2^12.4 g, 16 terms);
   // other columns go to the float64 pass whole.
-  const float gsc = global_scale(amax[g]);
+  const float gsc = global_scale(amax[g], opt.gdiv);
   const float hpm = wave_max_nonneg(hpmax);
+  // multiplier search: the lane's multipliers and the float64 6g, 1/(6g)
+  const bool msearch = opt.nm > 0;
+  float mu0 = 0.0f, mu1 = 0.0f;
+  if (msearch) {
+    lane_multipliers(opt, lane, mu0, mu1);
+    L.mk[lane] = -1;
+    L.mk[lane + 64] = -1;
+  }
+  const double g6 = 6.0 * (double)gsc, ig6 = 1.0 / g6;
   const bool fast = filter_ok(gsc) && hpm <= 0x1p100f && (double)gsc * (double)gsc * (double)hpm <= 0x1p76;
   const float s0 = cand_scale(i + 1, gsc), is0 = inv_scale(s0);
   const float s1 = cand_scale(i + 17, gsc), is1 = inv_scale(s1);
@@ -431,6 +490,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       }
     }
     if (gg == 0) L.sw[i] = swr;
+    if (msearch) {
+      // block amax of row i: the lane's 4 elements, then the 4 lane groups
+      unsigned am = max(max(__float_as_uint(fabsf(wt[0])), __float_as_uint(fabsf(wt[1]))),
+                        max(__float_as_uint(fabsf(wt[2])), __float_as_uint(fabsf(wt[3]))));
+      auto x = __builtin_amdgcn_permlane32_swap(am, am, false, false);
+      am = max(x[0], x[1]);
+      auto y = __builtin_amdgcn_permlane16_swap(am, am, false, false);
+      am = max(y[0], y[1]);
+      if (gg == 0) L.ab[i] = __uint_as_float(am);
+    }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -575,6 +644,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
 
       // lane l now holds codes l + 1 (tiles 0..3) and l + 65 (tiles 4..7); 127 and 128 do not exist
       if (lane >= 62) Lq[1] = __builtin_inff();
+      if (msearch) {                                 // candidates no multiplier proposes drop out
+        bool al0, al1;
+        mark_allowed(L.ab[rr], g6, ig6, mu0, mu1, (int)(c - c_begin), L.mk, lane + 1, lane + 65, al0, al1);
+        if (!al0) Lq[0] = __builtin_inff();
+        if (!al1) Lq[1] = __builtin_inff();
+      }
       // Each candidate's exact loss lies in [L_k - cA_k, L_k + cA_k].  U, the lowest upper end,
       // is >= the exact minimum, so the exact argmin is one of the candidates whose lower end is
       // <= U; when there is only one, it is the argmin.
@@ -731,6 +806,7 @@ struct ExactLds {
   float P[256];
   float w[16];
   double b[16];
+  int mk[128];         // codes proposed by the multipliers, tagged with the block
 };
 
 // Bit r: block (row c0 + r, column myn) was left undecided (code 0) by the filter.  The rows are
@@ -752,7 +828,7 @@ template <bool BF16, bool COUPLED>
 __global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
-    uint8_t* __restrict__ fp4, float* __restrict__ loss) {
+    uint8_t* __restrict__ fp4, float* __restrict__ loss, const SweepOpts opt) {
   __shared__ ExactLds lds_all[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ExactLds& L = lds_all[wave];
@@ -762,7 +838,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
   const int64_t c0 = ((int64_t)blockIdx.x * kWaves + wave) * kExactRows;
   const int64_t n0 = (int64_t)blockIdx.y * 64;
   const int64_t g = blockIdx.z;
-  const float gsc = global_scale(amax[g]);
+  const float gsc = global_scale(amax[g], opt.gdiv);
+  const bool msearch = opt.nm > 0;
+  float mu0 = 0.0f, mu1 = 0.0f;
+  if (msearch) lane_multipliers(opt, lane, mu0, mu1);
+  L.mk[lane] = -1;
+  L.mk[lane + 64] = -1;
+  const double g6 = 6.0 * (double)gsc, ig6 = 1.0 / g6;
+  int tag = 0;
   const int64_t myn = n0 + lane;
   const unsigned undecided = undecided_rows(code, g, cout, nb, c0, myn);
   for (int r = 0; r < kExactRows; ++r) {
@@ -796,11 +879,18 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      bool al[2] = {true, true};
+      if (msearch) {
+        float ab = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ab = fmaxf(ab, fabsf(L.w[j]));
+        mark_allowed(ab, g6, ig6, mu0, mu1, tag++, L.mk, lane + 1, lane + 65, al[0], al[1]);
+      }
       double best = __builtin_inf();
       int bestK = 1 << 20;
       for (int h = 0; h < 2; ++h) {
         const int k = lane + 1 + 64 * h;
-        if (k > 126) continue;
+        if (k > 126 || !al[h]) continue;
         const float sk = cand_scale(k, gsc);
         double e[16];
         int nib;
@@ -936,8 +1026,10 @@ template <bool BF16>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_sweep_diag(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ imp, uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
-    float* __restrict__ loss) {
+    float* __restrict__ loss, const SweepOpts opt) {
   __shared__ __attribute__((aligned(16))) float wt_all[kWaves][kRowsPerWave][16];   // w (+0 for -0)
+  __shared__ float ab_all[kWaves][kRowsPerWave];      // block amax of the row (multiplier search)
+  __shared__ int mk_all[kWaves][128];                 // codes proposed by the multipliers
   __shared__ __attribute__((aligned(16))) float ut_all[kWaves][kRowsPerWave][16];   // w a
   __shared__ __attribute__((aligned(16))) float sa_all[kWaves][16];                 // a = sqrt(Imp)
   __shared__ float im_all[kWaves][16];
@@ -970,7 +1062,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  const float gsc = uniform(global_scale(amax[g]));
+  const float gsc = uniform(global_scale(amax[g], opt.gdiv));
+  const bool msearch = opt.nm > 0;
+  float mu0 = 0.0f, mu1 = 0.0f;
+  if (msearch) {
+    lane_multipliers(opt, lane, mu0, mu1);
+    mk_all[wave][lane] = -1;
+    mk_all[wave][lane + 64] = -1;
+  }
+  const double g6 = 6.0 * (double)gsc, ig6 = 1.0 / g6;
   float a[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1046,9 +1146,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
       }
       const float wrow = wp + __shfl_xor(wp, 1, 64);
       lp += __shfl_xor(lp, 1, 64);
+      float am = 0.0f;
+      if (msearch) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(v[q]));
+        am = fmaxf(am, __shfl_xor(am, 1, 64));
+      }
       if (h == 0) {
         wr_all[wave][rr] = (wrow >= 0x1p-100f && wrow <= 0x1p+100f) ? wrow : -1.0f;
         lone_all[wave][rr] = lp;
+        ab_all[wave][rr] = am;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1105,6 +1212,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
       }
       const float lone_L = lone_all[wave][rr];
       L1 = single ? __builtin_inff() : (lone ? lone_L : L1);
+      if (msearch) {                                 // candidates no multiplier proposes drop out
+        bool al0, al1;
+        mark_allowed(ab_all[wave][rr], g6, ig6, mu0, mu1, rr, mk_all[wave], pr.k0,
+                     single ? 0 : (lone ? kDiagLoneCode : pr.k1), al0, al1);
+        if (!al0) L0 = __builtin_inff();
+        if (!al1) L1 = __builtin_inff();
+      }
       // losses are >= 0 or +inf, ordered like their bit patterns
       const float m = wave_min_nonneg(__uint_as_float(min(__float_as_uint(L0), __float_as_uint(L1))));
       if (!have_line) {
@@ -1212,14 +1326,22 @@ template <bool BF16>
 __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ imp, uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
-    float* __restrict__ loss) {
+    float* __restrict__ loss, const SweepOpts opt) {
+  __shared__ int mk_all[kWaves][128];                 // codes proposed by the multipliers
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nb = cin / 16;
   // wave: rows c0 .. c0+kExactRows-1, block columns n0 .. n0+63 (see k_sweep_full_exact)
   const int64_t c0 = ((int64_t)blockIdx.x * kWaves + wave) * kExactRows;
   const int64_t n0 = (int64_t)blockIdx.y * 64;
   const int64_t g = blockIdx.z;
-  const float gsc = global_scale(amax[g]);
+  const float gsc = global_scale(amax[g], opt.gdiv);
+  const bool msearch = opt.nm > 0;
+  float mu0 = 0.0f, mu1 = 0.0f;
+  if (msearch) lane_multipliers(opt, lane, mu0, mu1);
+  mk_all[wave][lane] = -1;
+  mk_all[wave][lane + 64] = -1;
+  const double g6 = 6.0 * (double)gsc, ig6 = 1.0 / g6;
+  int tag = 0;
   const int64_t myn = n0 + lane;
   const unsigned undecided = undecided_rows(code, g, cout, nb, c0, myn);
   for (int r = 0; r < kExactRows; ++r) {
@@ -1243,11 +1365,18 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
       const int64_t base = (g * cout + c) * cin + n * 16;
       float w[16];
       load_w16<BF16>(W, base, w);
+      bool al[2] = {true, true};
+      if (msearch) {
+        float ab = 0.0f;
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) ab = fmaxf(ab, fabsf(w[j]));
+        mark_allowed(ab, g6, ig6, mu0, mu1, tag++, mk_all[wave], lane + 1, lane + 65, al[0], al[1]);
+      }
       double best = __builtin_inf();
       int bestK = 1 << 20;
       for (int h = 0; h < 2; ++h) {
         const int k = lane + 1 + 64 * h;
-        if (k > 126) continue;
+        if (k > 126 || !al[h]) continue;
         const float sk = cand_scale(k, gsc);
         double Ls = 0.0;
         int nib;
@@ -1278,7 +1407,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
 
 hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout, int64_t cin,
                         const float* amax, const float* H, const float* P, uint8_t* code,
-                        uint8_t* fp4, float* loss, hipStream_t stream) {
+                        uint8_t* fp4, float* loss, const SweepOpts& opt, hipStream_t stream) {
   const int64_t nb = cin / 16;
   if (cout == 0) return hipSuccess;
   // a launch of at most four rounds of resident waves (4096 at a time) ends in a tail that the
@@ -1295,12 +1424,12 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
 #define LH_SWEEP_PAIR(B, C)                                                                        \
   if (equalize)                                                                                   \
     hipLaunchKernelGGL((k_sweep_full<B, C, true>), grid, block, 0, stream, W, cout, cin, amax, H, P, \
-                       code, fp4, loss, rpw);                                                      \
+                       code, fp4, loss, rpw, opt);                                                   \
   else                                                                                             \
     hipLaunchKernelGGL((k_sweep_full<B, C, false>), grid, block, 0, stream, W, cout, cin, amax, H,  \
-                       P, code, fp4, loss, rpw);                                                   \
+                       P, code, fp4, loss, rpw, opt);                                                \
   hipLaunchKernelGGL((k_sweep_full_exact<B, C>), xgrid, block, 0, stream, W, cout, cin, amax, H, P, \
-                     code, fp4, loss)
+                     code, fp4, loss, opt)
   if (bf16 && P) {
     LH_SWEEP_PAIR(true, true);
   } else if (bf16) {
@@ -1316,7 +1445,7 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
 
 hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t cout,
                              int64_t cin, const float* amax, const float* imp, uint8_t* code,
-                             uint8_t* fp4, float* loss, hipStream_t stream) {
+                             uint8_t* fp4, float* loss, const SweepOpts& opt, hipStream_t stream) {
   const int64_t nb = cin / 16;
   if (cout == 0) return hipSuccess;
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + kRowsPerWave - 1) / kRowsPerWave),
@@ -1325,11 +1454,11 @@ hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t
   const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
                    (unsigned)((nb + 63) / 64), (unsigned)n_groups);
   if (bf16) {
-    hipLaunchKernelGGL((k_sweep_diag<true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
-    hipLaunchKernelGGL((k_sweep_diag_exact<true>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
+    hipLaunchKernelGGL((k_sweep_diag<true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
+    hipLaunchKernelGGL((k_sweep_diag_exact<true>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
   } else {
-    hipLaunchKernelGGL((k_sweep_diag<false>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
-    hipLaunchKernelGGL((k_sweep_diag_exact<false>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss);
+    hipLaunchKernelGGL((k_sweep_diag<false>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
+    hipLaunchKernelGGL((k_sweep_diag_exact<false>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
   }
   return hipGetLastError();
 }

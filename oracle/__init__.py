@@ -23,6 +23,8 @@ from .lh_oracle import (  # noqa: F401
     exempt_mask,
     fake_quant,
     global_scale,
+    multiplier_allowed,
+    multiplier_codes,
     pack_nibbles,
     sweep,
     sweep_blocks,

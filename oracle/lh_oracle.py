@@ -75,10 +75,13 @@ def e4m3_ladder() -> np.ndarray:
     return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
 
 
-def global_scale(amax) -> np.ndarray:
-    """fp32(amax / (6 * 448)): one float64 divide rounded once to fp32 is the correctly rounded
+def global_scale(amax, norm: float = E4M3_MAX) -> np.ndarray:
+    """fp32(amax / (6 * norm)): the per-matrix scale that maps the global amax to the E4M3 value
+    norm -- 448 for NVFP4 ("Add composable scale calibration to GPTQ", What does this PR do?:
+    448-normalized scaling), 256 for its "4/6" variant (same passage).  norm is an E4M3 value, so
+    6 * norm is an fp32 number and one float64 divide rounded once to fp32 is the correctly rounded
     fp32 quotient (double rounding is harmless for a single binary32 division)."""
-    return np.asarray(np.asarray(amax, dtype=np.float64) / (FP4_MAX * E4M3_MAX), dtype=np.float32).astype(np.float64)
+    return np.asarray(np.asarray(amax, dtype=np.float64) / (FP4_MAX * float(norm)), dtype=np.float32).astype(np.float64)
 
 
 def candidate_scales(g) -> np.ndarray:
@@ -92,6 +95,38 @@ def absmax(W) -> np.ndarray:
     """Per-group max |W_g| (max calibration of the weight, the step that runs first)."""
     W = np.asarray(W, dtype=np.float64)
     return np.abs(W.reshape(W.shape[0], -1)).max(axis=1) if W.size else np.zeros(W.shape[0])
+
+
+def multiplier_codes(block_amax, g, multipliers) -> np.ndarray:
+    """Candidate codes of the amax-multiplier search ("add local hessian calibration", Changes: the
+    local-Hessian calibration config has a configurable step size and multipliers for its amax
+    search, next to the FP8 scale sweep).  A block with amax a and multiplier m proposes the block
+    amax a*m, i.e. the block scale (a*m)/6 under the global scale g: its code is the positive
+    finite E4M3 value (bytes 1..126) nearest to the exact real y = a*m / (6 g), ties to the even
+    code, saturating at 448 above and at 2^-9 below.
+
+    block_amax [B], g [B], multipliers [M] -> codes [B, M] (int).  a*m is exact in float64 (at most
+    48 significant bits) and so is v*6g for every ladder value v (at most 30 bits); two ladder values
+    nearest to y lie within a factor 2 of a*m, where the float64 difference |a*m - v*6g| is exact
+    (Sterbenz), so the nearest value and every tie are decided exactly."""
+    a = np.asarray(block_amax, dtype=np.float64)[:, None, None]
+    gg = np.asarray(g, dtype=np.float64)[:, None, None]
+    m = np.asarray(multipliers, dtype=np.float64)[None, :, None]
+    ladder = e4m3_ladder()[None, None, :]
+    d = np.abs(a * m - ladder * (6.0 * gg))                    # [B, M, 126], exact where it matters
+    is_min = d == d.min(axis=-1, keepdims=True)
+    codes = np.arange(1, 127)
+    even_min = is_min & (codes % 2 == 0)
+    idx = np.where(even_min.any(axis=-1), np.argmax(even_min, axis=-1), np.argmax(is_min, axis=-1))
+    return idx + 1
+
+
+def multiplier_allowed(block_amax, g, multipliers) -> np.ndarray:
+    """[B, 126] mask of the codes the multiplier grid proposes for each block."""
+    codes = multiplier_codes(block_amax, g, multipliers)
+    allowed = np.zeros((codes.shape[0], N_CANDIDATES), dtype=bool)
+    np.put_along_axis(allowed, codes - 1, True, axis=1)
+    return allowed
 
 
 # ----------------------------------------------------------------------------- fake quant
@@ -225,7 +260,8 @@ def activation_fake_quant(X, x_amax, offsets, bf16: bool, rows_per_chunk: int = 
     the block scale v = the E4M3 value nearest to max|x| / (6 gX) (ties to the even code, so 448 at
     most and 0 for a block whose max rounds to 0), s = fp32(v gX); each element becomes
     sign(x) * E2M1(|x|/s) * s, the product rounded to fp32 and then, for bf16 activations, to bf16.
-    x_amax = 0 gives X_q = 0."""
+    sign(x) is the sign bit of x, as in an IEEE product: an element that quantizes to 0 keeps it
+    (-0 for a negative or -0 input).  x_amax = 0 gives X_q = sign(x) * 0."""
     X = np.asarray(X, dtype=np.float64)
     x_amax = np.asarray(x_amax, dtype=np.float64)
     offsets = np.asarray(offsets, dtype=np.int64)
@@ -236,19 +272,20 @@ def activation_fake_quant(X, x_amax, offsets, bf16: bool, rows_per_chunk: int = 
         gx = float(global_scale(x_amax[g]))
         r0, r1 = _group_rows(offsets, g)
         if gx == 0.0:
+            out[r0:r1] = np.copysign(0.0, X[r0:r1])
             continue
         for a in range(r0, r1, rows_per_chunk):
             b = min(r1, a + rows_per_chunk)
             xb = X[a:b].reshape(b - a, nb, BLOCK)
             v = e4m3_nearest(np.abs(xb).max(axis=-1) / (6.0 * gx))
             s = (v * gx).astype(np.float32).astype(np.float64)       # v gX is exact in float64
-            _, wq, _ = fake_quant(xb, s[..., None])                  # sign(x) E2M1(|x|/s) s, exact
-            q32 = wq.astype(np.float32)                              # the product in fp32
+            _, wq, _ = fake_quant(xb, s[..., None])                  # E2M1(|x|/s) s, exact
+            q32 = np.copysign(np.abs(wq), xb).astype(np.float32)     # sign bit of x; the product in fp32
             out[a:b] = (_bf16_round(q32) if bf16 else q32.astype(np.float64)).reshape(b - a, cin)
     return out
 
 
-def dequantize(code, fp4, amax, bf16: bool):
+def dequantize(code, fp4, amax, bf16: bool, norm: float = E4M3_MAX):
     """Fake-quantized weights and per-block amax from scale codes [G, cout, nb] (bytes 1..126)
     and packed nibbles [G, cout, cin/2] -- the calibrated quantizer state whose amax, scales and
     final fake-quantized weights "Add WMSE weight scale search calibration" fingerprints.
@@ -259,7 +296,7 @@ def dequantize(code, fp4, amax, bf16: bool):
     code = np.asarray(code, dtype=np.int64)
     fp4 = np.asarray(fp4, dtype=np.uint8)
     G, cout, nb = code.shape
-    g = global_scale(np.asarray(amax, dtype=np.float64))
+    g = global_scale(np.asarray(amax, dtype=np.float64), norm)
     v = e4m3_ladder()[code - 1]
     s = (v * g[:, None, None]).astype(np.float32).astype(np.float64)
     nib = np.empty((G, cout, nb * BLOCK), dtype=np.uint8)
@@ -308,12 +345,14 @@ def candidate_losses(w, g, H, P=None):
     return _candidate_losses(w, candidate_scales(np.asarray(g, dtype=np.float64)), H, P)
 
 
-def sweep_blocks(w, g, H, P=None, hidx=None, chunk: int = 2048):
+def sweep_blocks(w, g, H, P=None, hidx=None, chunk: int = 2048, allowed=None):
     """Core search on a list of blocks.
 
     w: [B,16] weights, g: [B] global scale of each block's matrix, H: [M,16,16] Hessians and
-    P: [M,16,16] or None, with block b using H[hidx[b]] (hidx defaults to 0..B-1).  Returns a dict
-    with code (uint8 E4M3 byte), nib [B,16], loss, and the runner-up data."""
+    P: [M,16,16] or None, with block b using H[hidx[b]] (hidx defaults to 0..B-1).  allowed: None
+    (all 126 candidates) or a [B,126] mask of the candidates block b may take (the multiplier
+    search); the others score +inf.  Returns a dict with code (uint8 E4M3 byte), nib [B,16], loss,
+    and the runner-up data."""
     w = np.asarray(w, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     H = np.asarray(H, dtype=np.float64)
@@ -335,6 +374,8 @@ def sweep_blocks(w, g, H, P=None, hidx=None, chunk: int = 2048):
             Pb[dead] = 0.0
         s = candidate_scales(g[sl])                              # [b, 126]
         L, Q, C = _candidate_losses(wb, s, Hb, Pb)
+        if allowed is not None:
+            L = np.where(allowed[sl], L, np.inf)
         k1, info = _select(L, Q, C)
         nib, _, _ = fake_quant(wb, s[np.arange(len(k1)), k1][:, None])
         out["code"][sl] = (k1 + 1).astype(np.uint8)
@@ -345,8 +386,9 @@ def sweep_blocks(w, g, H, P=None, hidx=None, chunk: int = 2048):
     return out
 
 
-def sweep_blocks_diag(w, g, imp, chunk: int = 4096):
-    """Diagonal search on a list of blocks: imp [B,16] importance of the block's channels."""
+def sweep_blocks_diag(w, g, imp, chunk: int = 4096, allowed=None):
+    """Diagonal search on a list of blocks: imp [B,16] importance of the block's channels;
+    allowed as in sweep_blocks."""
     w = np.asarray(w, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     imp = np.asarray(imp, dtype=np.float64)
@@ -362,7 +404,9 @@ def sweep_blocks_diag(w, g, imp, chunk: int = 4096):
         s = candidate_scales(g[sl])
         _, _, E = fake_quant(wb[:, None, :], s[:, :, None])
         L = np.einsum("bki,bi->bk", E * E, ib)
-        k1, info = _select(L, L, np.zeros_like(L))
+        if allowed is not None:
+            L = np.where(allowed[sl], L, np.inf)
+        k1, info = _select(L, np.where(np.isfinite(L), L, 0.0), np.zeros_like(L))
         nib, _, _ = fake_quant(wb, s[np.arange(len(k1)), k1][:, None])
         out["code"][sl] = (k1 + 1).astype(np.uint8)
         out["nib"][sl] = nib
@@ -390,12 +434,21 @@ def _reshape_out(res, G, cout, nb):
     return out
 
 
-def sweep(W, amax, H, P=None):
-    """Full-matrix sweep.  W [G,cout,cin], amax [G], H [G,nb,16,16], P same or None.
+def _allowed(wl, gl, multipliers):
+    """Candidate mask of the multiplier search for blocks wl [B,16] (None: all 126)."""
+    if multipliers is None:
+        return None
+    return multiplier_allowed(np.abs(wl).max(axis=1), gl, multipliers)
+
+
+def sweep(W, amax, H, P=None, norm: float = E4M3_MAX, multipliers=None):
+    """Full-matrix sweep.  W [G,cout,cin], amax [G], H [G,nb,16,16], P same or None; norm the
+    E4M3 value the global amax maps to (448, or 256 for "4/6"); multipliers None (the 126-candidate
+    FP8 sweep) or the amax multipliers of the multiplier search.
 
     Returns code [G,cout,nb] (E4M3 byte), fp4 [G,cout,cin/2], loss, L1/L2/Q/C diagnostics."""
     Wb, G, cout, nb = _flatten_blocks(W)
-    g = global_scale(amax)
+    g = global_scale(amax, norm)
     H = np.asarray(H, dtype=np.float64)
     wl = Wb.reshape(-1, BLOCK)
     gl = np.repeat(g, cout * nb)
@@ -404,18 +457,18 @@ def sweep(W, amax, H, P=None):
             + np.zeros((1, cout, 1), dtype=np.int64)).reshape(-1)
     Ht = H.reshape(G * nb, BLOCK, BLOCK)
     Pt = None if P is None else np.asarray(P, dtype=np.float64).reshape(G * nb, BLOCK, BLOCK)
-    return _reshape_out(sweep_blocks(wl, gl, Ht, Pt, hidx), G, cout, nb)
+    return _reshape_out(sweep_blocks(wl, gl, Ht, Pt, hidx, allowed=_allowed(wl, gl, multipliers)), G, cout, nb)
 
 
-def sweep_diag(W, amax, imp):
-    """Full-matrix diagonal sweep.  imp [G, cin]."""
+def sweep_diag(W, amax, imp, norm: float = E4M3_MAX, multipliers=None):
+    """Full-matrix diagonal sweep.  imp [G, cin]; norm and multipliers as in sweep."""
     Wb, G, cout, nb = _flatten_blocks(W)
-    g = global_scale(amax)
+    g = global_scale(amax, norm)
     imp = np.asarray(imp, dtype=np.float64).reshape(G, 1, nb, BLOCK)
     wl = Wb.reshape(-1, BLOCK)
     gl = np.repeat(g, cout * nb)
     il = np.broadcast_to(imp, (G, cout, nb, BLOCK)).reshape(-1, BLOCK)
-    return _reshape_out(sweep_blocks_diag(wl, gl, il), G, cout, nb)
+    return _reshape_out(sweep_blocks_diag(wl, gl, il, allowed=_allowed(wl, gl, multipliers)), G, cout, nb)
 
 
 def exempt_mask(res, rel: float = 1e-6) -> np.ndarray:

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
-              "lh_activation_fake_quant", "lh_scale_sweep",
+              "lh_activation_fake_quant", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag_ex",
+              "lh_dequantize_ex",
               "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_dequantize", "lh_absmax", "lh_last_error",
               "lh_version"):
         assert n in names
@@ -64,6 +65,21 @@ def test_validation_errors_without_device():
     c, m = _err(L.lh_activation_fake_quant(FAKE, 1, 10, 32, None, 1, VP(0x3000), FAKE, None))
     assert c == lh.LH_ERR_INVALID_ARGUMENT and "alias" in m
     assert L.lh_activation_fake_quant(FAKE, 9, 10, 32, None, 1, FAKE, FAKE, None) == lh.LH_ERR_UNSUPPORTED
+    # sweep options: scale_norm must be an E4M3 value, at most 128 positive finite multipliers
+    def opt(norm, mults):
+        arr = (ctypes.c_float * max(1, len(mults)))(*mults)
+        return lh.SweepOptions(norm, len(mults), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))), arr
+    for o_, msg in ((opt(300.0, []), "scale_norm"), (opt(0.0, []), "scale_norm"), (opt(448.0, [1.0, -2.0]), "multiplier"),
+                    (opt(256.0, [float("nan")]), "multiplier"), (opt(448.0, [1.0] * 129), "n_multipliers")):
+        c, m = _err(L.lh_scale_sweep_ex(FAKE, 1, 1, 16, 32, FAKE, FAKE, None, ctypes.byref(o_[0]), FAKE, None, None, None))
+        assert c == lh.LH_ERR_INVALID_ARGUMENT and msg in m, (c, m)
+        c, m = _err(L.lh_scale_sweep_diag_ex(FAKE, 1, 1, 16, 32, FAKE, None, ctypes.byref(o_[0]), FAKE, None, None, None))
+        assert c == lh.LH_ERR_INVALID_ARGUMENT and msg in m, (c, m)
+    c, m = _err(L.lh_dequantize_ex(FAKE, FAKE, 1, 1, 16, 32, FAKE, 100.0, FAKE, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "scale_norm" in m
+    nul = lh.SweepOptions(448.0, 3, None)
+    c, m = _err(L.lh_scale_sweep_ex(FAKE, 1, 1, 16, 32, FAKE, FAKE, None, ctypes.byref(nul), FAKE, None, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "multipliers" in m
     # no outputs, NULL input
     assert L.lh_accumulate(FAKE, 1, 10, 32, None, 1, 0.0, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_accumulate(None, 1, 10, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT

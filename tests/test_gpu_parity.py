@@ -220,6 +220,10 @@ def test_activation_fake_quant_entry_point(name):
     fused one value for value."""
     wl = synth.make(name, **SMALL[name])
     G, bf16 = wl.n_groups, wl.dtype == "bf16"
+    plant = np.float32([-0.0, -1e-9, 1e-9, 0.0])          # signed zeros and values that quantize to 0
+    xs = synth.f32_from_bf16_bits(wl.X) if bf16 else wl.X.copy()
+    xs[::7, 5] = plant[np.arange(xs[::7].shape[0]) % 4]
+    wl.X = synth.bf16_bits_from_f32(xs) if bf16 else xs
     X64 = wl.X_f64()
     amax = np.array([np.abs(X64[wl.offsets[g]:wl.offsets[g + 1]]).max(initial=0.0) for g in range(G)])
     if G > 2:
@@ -233,8 +237,8 @@ def test_activation_fake_quant_entry_point(name):
     ref = oracle.activation_fake_quant(X64, amax.astype(np.float64), wl.offsets, bf16=bf16)
     got = Xq.float().cpu().numpy().astype(np.float64)
     np.testing.assert_array_equal(got, ref)
-    # signs of zero follow x (a negative x that quantizes to 0 gives -0, as the fp32 product does)
-    np.testing.assert_array_equal(np.signbit(got[got == 0]), np.signbit(ref[ref == 0]))
+    # zeros carry the sign bit of x (-0 for -0 and for a negative x that quantizes to 0)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))
     H1, P1 = lh.lh_accumulate_act_aware(X, Xq, offsets=off)
     H2, P2 = lh.lh_accumulate_act_aware_fq(X, am, offsets=off)
     assert torch.equal(H1, H2) and torch.equal(P1, P2)

@@ -512,6 +512,7 @@ def test_e4m3_nearest_matches_library_encoder_and_saturates():
 
 def _exact_act_fq(x, amax, bf16):
     """One row's X_q by exact rational arithmetic (brute force over every E4M3 and E2M1 value)."""
+    import math
     import torch
     gx = Fraction(float(np.float32(Fraction(amax) / 2688)))
     vals = [Fraction(0)] + [Fraction(v) for v in oracle.e4m3_ladder()]
@@ -527,7 +528,7 @@ def _exact_act_fq(x, amax, bf16):
         s = Fraction(float(np.float32(vals[code[0]] * gx)))
         for t in blk:
             if s == 0:
-                out.append(0.0)
+                out.append(math.copysign(0.0, float(t)))
                 continue
             rr = abs(Fraction(float(t))) / s
             dg = [abs(rr - gv) for gv in grid]
@@ -535,7 +536,7 @@ def _exact_act_fq(x, amax, bf16):
             c = [k for k in range(8) if dg[k] == m]
             c = [k for k in c if k % 2 == 0] or c
             q = float(np.float32(float(grid[c[0]] * s)))
-            out.append(-q if t < 0 else q)
+            out.append(math.copysign(q, float(t)))           # the sign bit of x, -0 included
     out = np.array(out, dtype=np.float32)
     if bf16:
         out = torch.from_numpy(out).to(torch.bfloat16).to(torch.float32).numpy()
@@ -550,14 +551,19 @@ def test_activation_fake_quant_matches_exact_rationals(bf16):
     x[2, 16:32] *= 1e-4                              # block far below the global scale
     x[3, 32:48] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5] * 2, dtype=np.float32)
     x[4] = -x[4]
+    x[5, 48:52] = -0.0                               # negative zeros keep their sign
+    x[5, 52:56] = -1e-9                              # tiny negatives quantize to -0
     if bf16:
         x = synth.f32_from_bf16_bits(synth.bf16_bits_from_f32(x))
     amax = float(np.abs(x).max())
-    for a in (amax, amax / 3.0):                      # the second saturates some blocks at 448
+    for a in (amax, amax / 3.0, 0.0):                 # the second saturates some blocks at 448
         got = oracle.activation_fake_quant(x.astype(np.float64), [a], np.array([0, 6]), bf16=bf16)
         for row in range(6):
-            np.testing.assert_array_equal(got[row], _exact_act_fq(x[row], a, bf16))
-    assert np.all(oracle.activation_fake_quant(x.astype(np.float64), [0.0], np.array([0, 6]), bf16) == 0.0)
+            want = _exact_act_fq(x[row], a, bf16)
+            np.testing.assert_array_equal(got[row], want)
+            np.testing.assert_array_equal(np.signbit(got[row]), np.signbit(want))
+    zero = oracle.activation_fake_quant(x.astype(np.float64), [0.0], np.array([0, 6]), bf16)
+    assert np.all(zero == 0.0) and np.array_equal(np.signbit(zero), np.signbit(x))
 
 
 def test_activation_fake_quant_is_on_the_grid_and_per_group():
@@ -598,3 +604,137 @@ def test_dequantize_reproduces_fake_quant_of_the_chosen_scale(bf16):
     assert np.signbit(Wq[1, 2, 3]) and Wq[1, 2, 3] == 0.0
     np.testing.assert_array_equal(bam, (6.0 * sb).astype(np.float32).astype(np.float64))
     assert np.all(np.abs(Wq).reshape(G, cout, -1, 16).max(axis=-1) <= bam * (1 + 2 ** -7))
+
+
+# ------------------------------------------------------------------ 256-normalized ("4/6") scaling
+def test_global_scale_256_normalized_is_fp32_rounding():
+    """norm 256: g = fp32(amax / (6 * 256)) correctly rounded, for many amax."""
+    r = rng(31)
+    for amax in np.float32(r.uniform(1e-3, 10.0, 200)):
+        want = np.float32(Fraction(float(amax)) / 1536)
+        assert oracle.global_scale(amax, 256.0) == np.float64(want)
+    assert oracle.global_scale(np.float32(3.0), 256.0) == 3.0 / 1536
+
+
+def test_256_normalization_equals_448_with_scaled_amax():
+    """The global scale is all the normalization changes: amax / (6*256) = (7/4 amax) / (6*448), so
+    with 7/4 amax exact in fp32 the 256-normalized search equals the 448 one on 7/4 amax (codes,
+    nibbles, losses), for the full and the diagonal form; and it differs from the 448 search on
+    the same amax for some blocks."""
+    wl = synth.make("c2", cout=24, cin=64, rows=200)
+    W, X = wl.W_f64(), wl.X_f64()
+    H, imp = oracle.accumulate(X, wl.offsets, want_imp=True)
+    amax = oracle.absmax(W).astype(np.float32)                # bf16 values: 7/4 amax is exact
+    amax7 = (amax * np.float32(1.75)).astype(np.float64)
+    assert Fraction(float(amax7[0])) == Fraction(7, 4) * Fraction(float(amax[0]))
+    a = oracle.sweep(W, amax, H, norm=256.0)
+    b = oracle.sweep(W, amax7, H, norm=448.0)
+    for k in ("code", "fp4", "loss"):
+        np.testing.assert_array_equal(a[k], b[k])
+    c = oracle.sweep(W, amax, H)
+    assert np.any(a["code"] != c["code"])
+    ad = oracle.sweep_diag(W, amax, imp, norm=256.0)
+    bd = oracle.sweep_diag(W, amax7, imp, norm=448.0)
+    np.testing.assert_array_equal(ad["code"], bd["code"])
+    np.testing.assert_array_equal(ad["fp4"], bd["fp4"])
+    # dequantize follows the same scale
+    Wq, bam = oracle.dequantize(a["code"], a["fp4"], amax, bf16=True, norm=256.0)
+    Wq7, bam7 = oracle.dequantize(b["code"], b["fp4"], amax7, bf16=True)
+    np.testing.assert_array_equal(Wq, Wq7)
+    np.testing.assert_array_equal(bam, bam7)
+
+
+# ------------------------------------------------------------------ amax-multiplier search
+def _exact_code(a, m, g):
+    """Nearest of the 126 positive E4M3 values to a*m/(6g), ties to the even code, by rationals."""
+    y = Fraction(float(a)) * Fraction(float(m)) / (6 * Fraction(float(g)))
+    vals = [Fraction(float(v)) for v in oracle.e4m3_ladder()]
+    d = [abs(y - v) for v in vals]
+    best = min(d)
+    ks = [k + 1 for k in range(126) if d[k] == best]
+    even = [k for k in ks if k % 2 == 0]
+    return even[0] if even else ks[0]
+
+
+def test_multiplier_codes_match_exact_rationals():
+    """Random blocks and multipliers, exact midpoints (ties go to the even code) and their float
+    neighbours, saturation at 448 and at 2^-9, and an all-zero block."""
+    r = rng(32)
+    a = np.float32(r.uniform(1e-3, 0.2, 60)).astype(np.float64)
+    g = np.float32(r.uniform(1e-5, 1e-4, 60)).astype(np.float64)
+    m = np.float32(r.uniform(0.2, 3.0, 12)).astype(np.float64)
+    got = oracle.multiplier_codes(a, g, m)
+    for b in range(0, 60, 3):
+        for j in range(12):
+            assert got[b, j] == _exact_code(a[b], m[j], g[b])
+    # exact midpoints y = (v_k + v_k+1)/2 with a = 6 g y exactly, m = 1, and their neighbours
+    lad = oracle.e4m3_ladder()
+    gg = 2.0 ** -10
+    ys = (lad[:-1] + lad[1:]) / 2
+    aa = []
+    for y in ys:
+        t = np.float32(6 * gg * y)
+        aa += [float(t), float(np.nextafter(t, np.float32(1))), float(np.nextafter(t, np.float32(0)))]
+    aa += [0.0, 1e-30, 1e6]                                  # zero block, underflow, saturation
+    aa = np.array(aa)
+    got = oracle.multiplier_codes(aa, np.full(len(aa), gg), np.array([1.0]))[:, 0]
+    want = [_exact_code(x, 1.0, gg) for x in aa]
+    np.testing.assert_array_equal(got, want)
+    assert got[-3] == 1 and got[-2] == 1 and got[-1] == 126
+    ties = got[0:3 * len(ys):3]
+    assert np.all(ties % 2 == 0)                             # every exact midpoint went to the even code
+
+
+def _dense_grid(lo=1e-7, hi=1e3, ratio=1.01):
+    return np.float32(lo * ratio ** np.arange(int(np.log(hi / lo) / np.log(ratio)) + 1)).astype(np.float64)
+
+
+def test_multiplier_search_with_a_covering_grid_is_the_full_sweep():
+    """A grid dense enough to propose every code for every block turns the multiplier search into
+    the 126-candidate sweep (full, coupled and diagonal forms)."""
+    wl = synth.make("c2", cout=16, cin=48, rows=120)
+    W, X = wl.W_f64(), wl.X_f64()
+    W[0, 0, :16] = 0.0                                       # all-zero block: every code proposes 1
+    Xq = X + 0.1 * rng(33).standard_normal(X.shape)
+    H, P = oracle.accumulate_act_aware(X, Xq, wl.offsets)
+    _, imp = oracle.accumulate(X, wl.offsets, want_h=False, want_imp=True)
+    amax = oracle.absmax(W)
+    grid = _dense_grid()
+    g = oracle.global_scale(amax)
+    blk_amax = np.abs(W.reshape(-1, 16)).max(axis=1)
+    allowed = oracle.multiplier_allowed(blk_amax, np.repeat(g, len(blk_amax)), grid)
+    assert allowed[blk_amax > 0].all()
+    for a, b in ((oracle.sweep(W, amax, H, P, multipliers=grid), oracle.sweep(W, amax, H, P)),
+                 (oracle.sweep_diag(W, amax, imp, multipliers=grid), oracle.sweep_diag(W, amax, imp))):
+        np.testing.assert_array_equal(a["code"], b["code"])
+        np.testing.assert_array_equal(a["fp4"], b["fp4"])
+        np.testing.assert_array_equal(a["loss"], b["loss"])
+
+
+def test_multiplier_search_against_scalar_reevaluation():
+    """Each block's winner is the lowest-loss candidate over its multipliers' codes, re-evaluated
+    by an independent scalar loop (quantizer and objective written out per element)."""
+    r = rng(34)
+    B = 30
+    w = r.normal(0, 0.02, (B, 16))
+    w[3] = 0.0
+    g = oracle.global_scale(np.full(B, 0.1))
+    A = r.standard_normal((B, 16, 16))
+    H = np.einsum("bij,bkj->bik", A, A) / 16
+    P = 0.1 * r.standard_normal((B, 16, 16))
+    mult = np.float32(np.arange(0.5, 1.6, 0.1)).astype(np.float64)
+    allowed = oracle.multiplier_allowed(np.abs(w).max(axis=1), g, mult)
+    res = oracle.sweep_blocks(w, g, H, P, allowed=allowed)
+    for b in range(B):
+        s = oracle.candidate_scales(g[b])
+        bias = P[b] @ w[b]
+        best, kbest = np.inf, None
+        for m in mult:
+            k = _exact_code(np.abs(w[b]).max(), m, g[b])
+            e = np.array([_scalar_quant(x, s[k - 1]) for x in w[b]]) - w[b]
+            L = float(e @ H[b] @ e + 2 * e @ bias)
+            if L < best or (L == best and k < kbest):
+                best, kbest = L, k
+        assert res["code"][b] == kbest, (b, res["code"][b], kbest)
+        assert np.isclose(res["loss"][b], best, rtol=1e-10, atol=1e-18)
+    assert res["code"][3] == 1
