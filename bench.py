@@ -348,6 +348,11 @@ def main():
     ms_dq = t_dq["avg_launch_ms"]
     del wq_buf, bam_buf
     dq_bytes = blocks * (1 + 8 + 32 + 4) + G * 4
+    # grouped full-Hessian layers: the same accumulation and sweep in one launch with H kept on chip
+    # (lh_accumulate_sweep), bit-identical results; timed as a phase of its own
+    t_fused = None
+    if G > 1 and wl.mode == "full" and cout <= 8192:
+        t_fused = phase(lambda j: lh.lh_accumulate_sweep(Xs[j], Ws[j], amax, off, code, fp4, loss))
     # reference: a device-to-device copy of X (the same rotating sources), bytes read + written
     xdst = torch.empty_like(Xs[0])
     ms_copy = phase(lambda j: xdst.copy_(Xs[j]))["avg_launch_ms"]
@@ -394,6 +399,10 @@ def main():
                        "frac": dq_bytes / (ms_dq * 1e-3) / 1e9 / HBM_PEAK_GBS, "outside_step": True},
         "sweep": {**t_sw, "blocks_per_s": blocks / (ms_sw * 1e-3), "tflops": sweep_tflops},
     }
+    if t_fused is not None:
+        out["fused_accumulate_sweep"] = {**t_fused, "blocks_per_s": blocks / (t_fused["avg_launch_ms"] * 1e-3),
+                                         "vs_two_calls": (ms_acc + ms_sw) / t_fused["avg_launch_ms"],
+                                         "outside_step": True}
     if not args.no_cpu_baseline:
         del Ws, Xs, W0, X0
         if act:

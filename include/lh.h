@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define LH_VERSION 5
+#define LH_VERSION 6
 
 typedef enum {
   LH_OK = 0,
@@ -191,6 +191,27 @@ lh_status lh_scale_sweep_ex(const void* W, lh_dtype w_dtype, int64_t n_groups, i
                             int64_t cin, const float* global_amax, const float* H, const float* P,
                             const lh_sweep_options* options, uint8_t* scale_code, uint8_t* fp4,
                             float* best_loss, void* stream);
+
+/*
+ * Accumulation and sweep of grouped rows (MoE experts) in one launch, the Hessians kept on chip:
+ * per expert, the per-block Hessian of its routed rows and the weight-scale search of its weight
+ * matrix against it, without writing H to memory ("[2/3] Speed up layerwise GPTQ on MoE models",
+ * embedded #2840 text: one Hessian per expert and projection, over exactly the tokens routed to
+ * it; its size per MoE layer is what makes such calibration memory-bound).
+ *   H[g][n] = (1/T_g) sum_{t in g} x_t[n] x_t[n]^T   (as lh_accumulate, beta = 0)
+ *   then the search of lh_scale_sweep_ex on W[g] with H[g], P = NULL and `options`.
+ * For n_groups >= 2 each H is summed in the order lh_accumulate's grouped path uses, so codes,
+ * nibbles and losses are bit-identical to lh_accumulate followed by lh_scale_sweep_ex; with one
+ * group lh_accumulate takes its dense path, whose order differs (results agree within its
+ * rounding).  A group without rows gets H = 0, i.e. the plain weight-MSE search.
+ * X [rows, cin] and W [n_groups, cout, cin] of dtype; group_offsets as everywhere (NULL with one
+ * group); global_amax [n_groups]; outputs as lh_scale_sweep.
+ * Errors: those of lh_accumulate and lh_scale_sweep_ex, plus INVALID_ARGUMENT for cout > 8192.
+ */
+lh_status lh_accumulate_sweep(const void* X, const void* W, lh_dtype dtype, int64_t rows, int64_t cin,
+                              const int64_t* group_offsets, int64_t n_groups, int64_t cout,
+                              const float* global_amax, const lh_sweep_options* options,
+                              uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream);
 
 /*
  * Same sweep scored by the importance-weighted error L_k = sum_i imp[g][16n+i] * e_{k,i}^2

@@ -22,7 +22,7 @@ LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_activation_fake_quant",
-            "lh_dequantize", "lh_dequantize_ex", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag",
+            "lh_accumulate_sweep", "lh_dequantize", "lh_dequantize_ex", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag",
             "lh_scale_sweep_diag_ex", "lh_scale_sweep_mse", "lh_absmax", "lh_last_error", "lh_version")
 MAX_MULTIPLIERS = 128
 
@@ -61,12 +61,13 @@ def lib() -> ctypes.CDLL:
         h.lh_scale_sweep_ex.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_diag_ex.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         h.lh_dequantize_ex.argtypes = [vp, vp, i32, i64, i64, i64, vp, f32, vp, vp, vp]
+        h.lh_accumulate_sweep.argtypes = [vp, vp, i32, i64, i64, vp, i64, i64, vp, vp, vp, vp, vp, vp]
         h.lh_scale_sweep_mse.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
         h.lh_absmax.argtypes = [vp, i32, i64, i64, vp, vp]
         h.lh_dequantize.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
         for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
                   "lh_activation_fake_quant", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag_ex",
-                  "lh_dequantize_ex",
+                  "lh_dequantize_ex", "lh_accumulate_sweep",
                   "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_absmax", "lh_dequantize"):
             getattr(h, f).restype = ctypes.c_int
         h.lh_last_error.argtypes = []
@@ -294,6 +295,29 @@ def lh_scale_sweep_ex(W: torch.Tensor, amax: torch.Tensor, H: torch.Tensor, P: O
     opt, keep = _options(norm, multipliers)
     _check(lib().lh_scale_sweep_ex(_ptr(W), _dtype_code(W), G, cout, cin, _ptr(amax), _ptr(H), _ptr(P),
                                    ctypes.byref(opt), _ptr(code), _ptr(fp4), _ptr(loss), _stream(W.device)))
+    del keep
+    return code, fp4, loss
+
+
+def lh_accumulate_sweep(X: torch.Tensor, W: torch.Tensor, amax: torch.Tensor, offsets: Optional[torch.Tensor] = None,
+                        code: Optional[torch.Tensor] = None, fp4: Optional[torch.Tensor] = None,
+                        loss: Optional[torch.Tensor] = None, *, norm: float = 448.0, multipliers=None,
+                        want_fp4: bool = True, want_loss: bool = True):
+    """Per-expert Hessians of X's grouped rows and the scale search of W [G, cout, cin] against
+    them in one launch, H never written to memory: (code, fp4, loss) as lh_scale_sweep_ex."""
+    _need(X, "X")
+    W = _as3d(W)
+    _need(W, "W")
+    rows, cin = X.shape
+    offsets, G = _offsets(offsets, X)
+    if W.shape[0] != G or W.shape[2] != cin or W.dtype != X.dtype:
+        raise ValueError(f"W must be [{G}, cout, {cin}] of X's dtype")
+    _need(amax, "amax", (G,), torch.float32)
+    code, fp4, loss = _sweep_outputs(W, code, fp4, loss, want_fp4, want_loss)
+    opt, keep = _options(norm, multipliers)
+    _check(lib().lh_accumulate_sweep(_ptr(X), _ptr(W), _dtype_code(X), rows, cin, _ptr(offsets), G, W.shape[1],
+                                     _ptr(amax), ctypes.byref(opt), _ptr(code), _ptr(fp4), _ptr(loss),
+                                     _stream(X.device)))
     del keep
     return code, fp4, loss
 

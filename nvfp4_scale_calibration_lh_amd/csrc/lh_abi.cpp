@@ -366,6 +366,35 @@ lh_status lh_scale_sweep(const void* W, lh_dtype w_dtype, int64_t n_groups, int6
                            best_loss, stream);
 }
 
+lh_status lh_accumulate_sweep(const void* X, const void* W, lh_dtype dtype, int64_t rows, int64_t cin,
+                              const int64_t* group_offsets, int64_t n_groups, int64_t cout,
+                              const float* global_amax, const lh_sweep_options* options,
+                              uint8_t* scale_code, uint8_t* fp4, float* best_loss, void* stream) {
+  if (!dtype_ok(dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  lh_status st = check_shapes_x(rows, cin, group_offsets, n_groups);
+  if (st != LH_OK) return st;
+  if ((st = check_sweep_shapes(n_groups, cout, cin)) != LH_OK) return st;
+  if (cout > lh::kFusedMaxCout) return fail(LH_ERR_INVALID_ARGUMENT, "cout must be at most %d for the fused path (got %lld)", lh::kFusedMaxCout, (long long)cout);
+  if (!global_amax || !scale_code) return fail(LH_ERR_INVALID_ARGUMENT, "global_amax and scale_code are required");
+  if (!X && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X is NULL");
+  if (!W && cout > 0) return fail(LH_ERR_INVALID_ARGUMENT, "W is NULL");
+  lh::SweepOpts opts;
+  if ((st = sweep_opts(options, &opts)) != LH_OK) return st;
+  int dev = -1;
+  st = check_pointers({{X, "X"}, {W, "W"}, {group_offsets, "group_offsets"}, {global_amax, "global_amax"}, {scale_code, "scale_code"}, {fp4, "fp4"}, {best_loss, "best_loss"}}, &dev);
+  if (st != LH_OK) return st;
+  if ((st = check_aligned(X, "X")) != LH_OK) return st;
+  if ((st = check_aligned(W, "W")) != LH_OK) return st;
+  if (fp4 && (reinterpret_cast<uintptr_t>(fp4) % 2) != 0) return fail(LH_ERR_INVALID_ARGUMENT, "fp4 must be 2-byte aligned");
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  hipError_t e = lh::launch_accumulate_sweep(X, W, dtype == LH_DTYPE_BF16, rows, cin, n_groups > 1 ? group_offsets : nullptr,
+                                             n_groups, cout, global_amax, scale_code, fp4, best_loss, opts,
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fused accumulate-and-sweep launch");
+  return ok();
+}
+
 lh_status lh_scale_sweep_diag_ex(const void* W, lh_dtype w_dtype, int64_t n_groups, int64_t cout,
                                  int64_t cin, const float* global_amax, const float* imp,
                                  const lh_sweep_options* options, uint8_t* scale_code, uint8_t* fp4,

@@ -56,6 +56,14 @@ hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t
                              int64_t cin, const float* amax, const float* imp, uint8_t* code,
                              uint8_t* fp4, float* loss, const SweepOpts& opts, hipStream_t stream);
 
+// Hessians of grouped rows (n_groups >= 1, offsets device int64[n_groups+1] or NULL for one
+// group) made in LDS and swept at once; outputs as launch_sweep with P = NULL.  cout <= kFusedMaxCout.
+constexpr int kFusedMaxCout = 8192;
+hipError_t launch_accumulate_sweep(const void* X, const void* W, bool bf16, int64_t rows, int64_t cin,
+                                   const int64_t* offsets, int64_t n_groups, int64_t cout, const float* amax,
+                                   uint8_t* code, uint8_t* fp4, float* loss, const SweepOpts& opts,
+                                   hipStream_t stream);
+
 // Wq (bf16 or fp32, may be NULL) and block_amax (may be NULL) from scale codes and FP4 nibbles;
 // g = fp32(amax / gdiv) as in the sweep.
 hipError_t launch_dequantize(const uint8_t* code, const uint8_t* fp4, const float* amax, int64_t n_groups,

@@ -56,6 +56,7 @@
 //    filter and the float64 passes.  Each row marks the proposed codes in a per-wave LDS table
 //    tagged with the row, so a lane reads its own codes' flags.
 #include "lh_internal.hpp"
+#include "acc_stream.hpp"
 
 #include <type_traits>
 
@@ -361,32 +362,84 @@ __device__ inline float wave_max_nonneg(float x) {
   return __uint_as_float((unsigned)__builtin_amdgcn_readfirstlane((int)v));
 }
 
-// 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
-// more and drop to 3 waves, which costs about 10%).  EQUALIZE: wave priority by progress (short
-// launches, see wave_priority_by_progress); rows_per_wave: 32, or 64 when one round holds them all.
-template <bool BF16, bool COUPLED, bool EQUALIZE>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
-    const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
-    const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
-    uint8_t* __restrict__ fp4, float* __restrict__ loss, int rows_per_wave, const SweepOpts opt) {
-  __shared__ FullLds lds_all[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  FullLds& L = lds_all[wave];
+// Float64 re-scoring of one block by a whole wave: lane l scores codes l + 1 and l + 65 (those
+// with al0 / al1 set) with exact quantization, and the winner's code, nibbles and loss are written
+// to code_p, fp4_p (the block's 8 bytes, or NULL) and loss_p (or NULL).  Hs, Ps (16x16 row-major)
+// and ws (16 weights) are in LDS; bs is 16 doubles of LDS scratch for P w.  dead: the block's H
+// has zero trace and is scored as H = I without the cross term.
+template <bool COUPLED>
+__device__ inline void exact_block(const float* Hs, const float* Ps,
+                                   const float* ws, double* bs, bool dead,
+                                   float gsc, bool al0, bool al1, int lane, uint8_t* code_p, uint8_t* fp4_p,
+                                   float* loss_p) {
+  const bool coupled = COUPLED && !dead;
+  if (lane < 16) {
+    double acc = 0.0;
+    if (coupled)
+      for (int j = 0; j < 16; ++j) acc += (double)Ps[lane * 16 + j] * (double)ws[j];
+    bs[lane] = acc;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  double best = __builtin_inf();
+  int bestK = 1 << 20;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    const int k = lane + 1 + 64 * h;
+    if (k > 126 || !(h == 0 ? al0 : al1)) continue;
+    const float sk = cand_scale(k, gsc);
+    double e[16], er[16];
+    int nib;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) er[j] = e[j] = exact_err(ws[j], sk, &nib);
+    // L = sum_r e_r ((H e)_r + 2 b_r), one row of H per step; er turns so that er[0] = e_r
+    // (a rolled loop keeps the register count low: this path is rare)
+    double Ls = 0.0;
+#pragma unroll 1
+    for (int r2 = 0; r2 < 16; ++r2) {
+      double y = 0.0;
+      if (dead) {
+        y = er[0];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y += (double)Hs[r2 * 16 + j] * e[j];
+      }
+      Ls += er[0] * (y + 2.0 * bs[r2]);
+#pragma unroll
+      for (int j = 0; j < 15; ++j) er[j] = er[j + 1];
+    }
+    if (Ls < best) { best = Ls; bestK = k; }
+  }
+  wave_argmin_d(best, bestK);
+  const float sw = cand_scale(bestK, gsc);
+  if (lane < 8 && fp4_p) {
+    int lo, hi;
+    exact_err(ws[2 * lane], sw, &lo);
+    exact_err(ws[2 * lane + 1], sw, &hi);
+    fp4_p[lane] = (uint8_t)(lo | (hi << 4));
+  }
+  if (lane == 0) {
+    *code_p = (uint8_t)bestK;
+    if (loss_p) *loss_p = (float)best;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The full-Hessian float32 filter over rows [c_begin, c_end) of block column n of group g by one
+// wave, with H_n (and P_n) already in L.H (and L.P).  Blocks the filter cannot decide get code 0
+// and are left to k_sweep_full_exact, or with RECORD are marked in the wave's LDS bit array `undec_bits`
+// (bit c - c_begin) for the caller to re-score in float64 (the fused accumulate-and-sweep kernel,
+// which keeps H in LDS only).  EQUALIZE: wave priority by progress (short launches, see
+// wave_priority_by_progress).
+template <bool BF16, bool COUPLED, bool EQUALIZE, bool RECORD, bool MSEARCH>
+__device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W, int64_t cout, int64_t cin,
+                                         int64_t g, int64_t n, int64_t c_begin, int64_t c_end, float gsc,
+                                         uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
+                                         float* __restrict__ loss, int rows_per_wave, const SweepOpts& opt,
+                                         unsigned* undec_bits = nullptr) {
+  const int lane = threadIdx.x & 63;
   const int i = lane & 15, gg = lane >> 4;
   const int64_t nb = cin / 16;
-  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
-  const int64_t g = blockIdx.z;
-  const int64_t c_begin = (int64_t)blockIdx.y * rows_per_wave;
-  if (n >= nb || c_begin >= cout) return;          // whole wave leaves; no workgroup barriers below
-  const int64_t c_end = min(cout, c_begin + rows_per_wave);
-
-  // ---- column set-up: H_n (and P_n) through LDS into registers
-  const float* Hn = Hg + (g * nb + n) * 256;
-  for (int q = 0; q < 4; ++q) L.H[lane * 4 + q] = Hn[lane * 4 + q];
-  if (COUPLED) {
-    const float* Pn = Pg + (g * nb + n) * 256;
-    for (int q = 0; q < 4; ++q) L.P[lane * 4 + q] = Pn[lane * 4 + q];
-  }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   double tr = 0.0;
@@ -432,17 +485,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // The filter's fp32 values stay finite and normal-range for every candidate when |H|, |P| <=
   // 2^100 and g^2 max(|H|, |P|) <= 2^76 (quotients |w|/s <= 2^20.4, |e| <= 2^12.4 g, 16 terms);
   // other columns go to the float64 pass whole.
-  const float gsc = global_scale(amax[g], opt.gdiv);
   const float hpm = wave_max_nonneg(hpmax);
-  // multiplier search: the lane's multipliers and the float64 6g, 1/(6g)
-  const bool msearch = opt.nm > 0;
+  // multiplier search (its own instantiation, so the plain sweep keeps its registers): the lane's
+  // multipliers and the float64 6g, 1/(6g)
+  constexpr bool msearch = MSEARCH;
   float mu0 = 0.0f, mu1 = 0.0f;
+  double g6 = 0.0, ig6 = 0.0;
   if (msearch) {
     lane_multipliers(opt, lane, mu0, mu1);
     L.mk[lane] = -1;
     L.mk[lane + 64] = -1;
+    g6 = 6.0 * (double)gsc;
+    ig6 = 1.0 / g6;
   }
-  const double g6 = 6.0 * (double)gsc, ig6 = 1.0 / g6;
   const bool fast = filter_ok(gsc) && hpm <= 0x1p100f && (double)gsc * (double)gsc * (double)hpm <= 0x1p76;
   const float s0 = cand_scale(i + 1, gsc), is0 = inv_scale(s0);
   const float s1 = cand_scale(i + 17, gsc), is1 = inv_scale(s1);
@@ -506,6 +561,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
     const int rows_here = (int)min((int64_t)16, c_end - c0);
     unsigned batched = 0u;   // rows whose unique winner is emitted by the per-tile pass below
     unsigned emitted = 0u;   // rows with midpoint overrides, emitted at once (loss per tile)
+    unsigned undec = 0u;     // rows the filter leaves undecided (RECORD)
     for (int rr = 0; rr < rows_here; ++rr) {
       const int64_t c = c0 + rr;
       const int64_t oblk = (g * cout + c) * nb + n;
@@ -525,7 +581,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
       const bool near1 = p1 < 112 && near_midpoint(fabsf(wp1), img1);
       const unsigned long long m0 = __ballot(near0), m1 = __ballot(near1);
       if (!fast) {
-        if (lane == 0) code[oblk] = 0;              // resolved by the float64 pass
+        if (RECORD) undec |= 1u << rr;
+        else if (lane == 0) code[oblk] = 0;         // resolved by the float64 pass
         continue;
       }
       const bool has_ovr = (m0 | m1) != 0ull;
@@ -751,7 +808,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
         }
         __builtin_amdgcn_wave_barrier();
       } else {
-        if (lane == 0) code[oblk] = 0;              // many contenders: float64 pass
+        if (RECORD) undec |= 1u << rr;
+        else if (lane == 0) code[oblk] = 0;         // many contenders: float64 pass
       }
     }
     if (batched | emitted) {
@@ -794,7 +852,152 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
         if (gg == 0 && on) loss[((g * cout + c0 + i) * nb) + n] = Lrow;
       }
     }
+    if (RECORD && lane == 0 && undec) {             // the tile's 16 rows share one word
+      const int64_t rel = c0 - c_begin;
+      undec_bits[rel >> 5] |= undec << (rel & 31);
+    }
     __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
+// more and drop to 3 waves, which costs about 10%).  rows_per_wave: 32, or 64 when one round holds
+// them all.
+template <bool BF16, bool COUPLED, bool EQUALIZE, bool MSEARCH>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
+    const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
+    const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
+    uint8_t* __restrict__ fp4, float* __restrict__ loss, int rows_per_wave, const SweepOpts opt) {
+  __shared__ FullLds lds_all[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  FullLds& L = lds_all[wave];
+  const int64_t nb = cin / 16;
+  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t g = blockIdx.z;
+  const int64_t c_begin = (int64_t)blockIdx.y * rows_per_wave;
+  if (n >= nb || c_begin >= cout) return;          // whole wave leaves; no workgroup barriers below
+  const int64_t c_end = min(cout, c_begin + rows_per_wave);
+  // column set-up: H_n (and P_n) through LDS into registers
+  const float* Hn = Hg + (g * nb + n) * 256;
+  for (int q = 0; q < 4; ++q) L.H[lane * 4 + q] = Hn[lane * 4 + q];
+  if (COUPLED) {
+    const float* Pn = Pg + (g * nb + n) * 256;
+    for (int q = 0; q < 4; ++q) L.P[lane * 4 + q] = Pn[lane * 4 + q];
+  }
+  sweep_full_column<BF16, COUPLED, EQUALIZE, false, MSEARCH>(L, W, cout, cin, g, n, c_begin, c_end,
+                                                    global_scale(amax[g], opt.gdiv), code, fp4, loss,
+                                                    rows_per_wave, opt);
+}
+
+// ------------------------------------------------------------------------------------------
+// Fused accumulate-and-sweep for grouped rows (MoE experts): one workgroup per (group, 64-channel
+// slice) builds that expert's four block Hessians in LDS and sweeps the four block columns over
+// all cout rows, one wave per column; blocks the filter leaves undecided are re-scored in float64
+// by the same wave.  H never goes to memory.  The Hessian is summed exactly as k_acc_pieces sums
+// it: the same pieces of at most R rows, each contracted by one wave over its 32-row chunks in
+// order, the pieces added in piece order and divided by T; so H, and with it every code, nibble
+// and loss, is bit-identical to lh_accumulate followed by lh_scale_sweep.
+// ------------------------------------------------------------------------------------------
+
+template <bool BF16>
+union FusedLds {
+  struct {
+    unsigned stage[kWaves * stream::Geo<BF16>::kWords];   // each wave's chunk stage
+    v4f part[kWaves][4][64];                              // one round of pieces: [piece][block][lane]
+  } acc;
+  struct {
+    FullLds L[kWaves];                                    // the sweep, after the Hessian is made
+    unsigned undec[kWaves][kFusedMaxCout / 32];           // rows the filter leaves undecided
+  } sw;
+};
+
+template <bool BF16, bool MSEARCH>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_moe_fused(
+    const void* __restrict__ X, const void* __restrict__ W, int64_t rows, int64_t cin, int64_t cout,
+    const int64_t* __restrict__ off, int64_t R, const float* __restrict__ amax, uint8_t* __restrict__ code,
+    uint8_t* __restrict__ fp4, float* __restrict__ loss, const SweepOpts opt) {
+  __shared__ FusedLds<BF16> sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, gg = lane >> 4;
+  const int64_t nb = cin / 16;
+  const int64_t slice = blockIdx.x, g = blockIdx.y;
+  const int64_t n0 = slice * 4;
+  const int nblk = (int)min((int64_t)4, nb - n0);
+  // rows of group g, clamped to [0, rows] as k_acc_pieces clamps them; pieces of at most R rows
+  int64_t a = 0, e = rows;
+  if (off) {
+    a = min(max(off[g], (int64_t)0), rows);
+    e = min(max(off[g + 1], a), rows);
+  }
+  const int64_t T = e - a;
+  const int64_t npieces = T > 0 ? (T + R - 1) / R : 1;
+
+  stream::Streamer<BF16, false, false> st{(const char*)X, nullptr, cin, slice * stream::kCh, nblk, lane, i, gg,
+                                          sm.acc.stage + wave * stream::Geo<BF16>::kWords, {}, {}};
+  v4f tot = {0.f, 0.f, 0.f, 0.f};                 // wave b: the running sum of block b
+  for (int64_t k0 = 0; k0 < npieces; k0 += kWaves) {
+    const int64_t k = k0 + wave;
+    if (k < npieces) {
+      st.run(a + k * R, min(e, a + k * R + R), 0, 1);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) sm.acc.part[wave][b][lane] = st.accH[b];
+    }
+    __syncthreads();
+    const int nk = (int)min((int64_t)kWaves, npieces - k0);
+    if (wave < nblk) {
+      if (npieces == 1) {
+        tot = sm.acc.part[0][wave][lane];         // one piece: its sums as they are
+      } else {
+        for (int w = 0; w < nk; ++w) tot += sm.acc.part[w][wave][lane];   // piece order
+      }
+    }
+    __syncthreads();                              // the round's stages and partials are free again
+  }
+  if (wave >= nblk) return;                       // whole wave leaves; no workgroup barriers below
+  FullLds& L = sm.sw.L[wave];
+  unsigned* ub = sm.sw.undec[wave];
+  const int64_t n = n0 + wave;
+  // H[4gg + r][i] = sum / T (zero for a group without rows)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) L.H[(4 * gg + r) * 16 + i] = T > 0 ? tot[r] / (float)T : 0.0f;
+  const float gsc = global_scale(amax[g], opt.gdiv);
+  // the float32 filter over all rows records the undecided ones; the wave then re-scores those in
+  // float64 (so the filter's registers are not live during the float64 pass, nor the reverse)
+  for (int q = lane; q < kFusedMaxCout / 32; q += 64) ub[q] = 0u;
+  sweep_full_column<BF16, false, false, true, MSEARCH>(L, W, cout, cin, g, n, 0, cout, gsc, code, fp4, loss,
+                                                       (int)cout, opt, ub);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double tr = 0.0;
+  for (int j = 0; j < 16; ++j) tr += (double)L.H[j * 17];
+  const bool dead = (tr == 0.0);
+  float mu0 = 0.0f, mu1 = 0.0f;
+  double g6 = 0.0, ig6 = 0.0;
+  if (MSEARCH) {
+    lane_multipliers(opt, lane, mu0, mu1);
+    g6 = 6.0 * (double)gsc;
+    ig6 = 1.0 / g6;
+  }
+  int tag = -2;                                   // below the filter's row tags and the initial -1
+  for (int wi = 0; wi < (int)((cout + 31) / 32); ++wi) {
+    for (unsigned u = ub[wi]; u; u &= u - 1) {
+      const int64_t c = 32 * wi + __builtin_ctz(u);
+      const int64_t oblk = (g * cout + c) * nb + n;
+      if (lane < 16) L.w[0][lane] = load_w(W, BF16, (g * cout + c) * cin + n * 16 + lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      bool al0 = true, al1 = true;
+      if (MSEARCH) {
+        float ab = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ab = fmaxf(ab, fabsf(L.w[0][j]));
+        mark_allowed(ab, g6, ig6, mu0, mu1, tag--, L.mk, lane + 1, lane + 65, al0, al1);
+      }
+      exact_block<false>(L.H, L.P, L.w[0], &L.ex[0][0], dead, gsc, al0, al1, lane, code + oblk,
+                         fp4 ? fp4 + (g * cout + c) * (cin / 2) + n * 8 : nullptr, loss ? loss + oblk : nullptr);
+    }
   }
 }
 
@@ -866,63 +1069,20 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_full_exact(
       double tr = 0.0;
       for (int j = 0; j < 16; ++j) tr += (double)L.H[j * 17];
       const bool dead = (tr == 0.0);
-      const bool coupled = COUPLED && !dead;
       const int64_t base = (g * cout + c) * cin + n * 16;
       if (lane < 16) L.w[lane] = load_w(W, BF16, base + lane);
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      if (lane < 16) {
-        double acc = 0.0;
-        if (coupled)
-          for (int j = 0; j < 16; ++j) acc += (double)L.P[lane * 16 + j] * (double)L.w[j];
-        L.b[lane] = acc;
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      bool al[2] = {true, true};
+      bool al0 = true, al1 = true;
       if (msearch) {
         float ab = 0.0f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) ab = fmaxf(ab, fabsf(L.w[j]));
-        mark_allowed(ab, g6, ig6, mu0, mu1, tag++, L.mk, lane + 1, lane + 65, al[0], al[1]);
+        mark_allowed(ab, g6, ig6, mu0, mu1, tag++, L.mk, lane + 1, lane + 65, al0, al1);
       }
-      double best = __builtin_inf();
-      int bestK = 1 << 20;
-      for (int h = 0; h < 2; ++h) {
-        const int k = lane + 1 + 64 * h;
-        if (k > 126 || !al[h]) continue;
-        const float sk = cand_scale(k, gsc);
-        double e[16];
-        int nib;
-  #pragma unroll
-        for (int j = 0; j < 16; ++j) e[j] = exact_err(L.w[j], sk, &nib);
-        double Ls = 0.0;
-  #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) {
-          double y = 0.0;
-          if (dead) {
-            y = e[r2];
-          } else {
-  #pragma unroll
-            for (int j = 0; j < 16; ++j) y += (double)L.H[r2 * 16 + j] * e[j];
-          }
-          Ls += e[r2] * (y + 2.0 * L.b[r2]);
-        }
-        if (Ls < best) { best = Ls; bestK = k; }
-      }
-      wave_argmin_d(best, bestK);
-      const float sw = cand_scale(bestK, gsc);
-      if (lane < 8 && fp4) {
-        int lo, hi;
-        exact_err(L.w[2 * lane], sw, &lo);
-        exact_err(L.w[2 * lane + 1], sw, &hi);
-        fp4[(g * cout + c) * (cin / 2) + n * 8 + lane] = (uint8_t)(lo | (hi << 4));
-      }
-      if (lane == 0) {
-        code[(g * cout + c) * nb + n] = (uint8_t)bestK;
-        if (loss) loss[(g * cout + c) * nb + n] = (float)best;
-      }
-      __builtin_amdgcn_wave_barrier();
+      const int64_t oblk = (g * cout + c) * nb + n;
+      exact_block<COUPLED>(L.H, L.P, L.w, L.b, dead, gsc, al0, al1, lane, code + oblk,
+                           fp4 ? fp4 + (g * cout + c) * (cin / 2) + n * 8 : nullptr, loss ? loss + oblk : nullptr);
     }
   }
 }
@@ -1022,7 +1182,7 @@ __device__ inline float uniform(float x) {
 
 // 6 waves per SIMD (80 registers; a few values outside the row loop go to scratch) measured
 // about 1% faster than 5 waves without the cap.
-template <bool BF16>
+template <bool BF16, bool MSEARCH>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_sweep_diag(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ imp, uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
@@ -1063,14 +1223,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   const float gsc = uniform(global_scale(amax[g], opt.gdiv));
-  const bool msearch = opt.nm > 0;
+  constexpr bool msearch = MSEARCH;               // multiplier search: its own instantiation
   float mu0 = 0.0f, mu1 = 0.0f;
+  double g6 = 0.0, ig6 = 0.0;
   if (msearch) {
     lane_multipliers(opt, lane, mu0, mu1);
     mk_all[wave][lane] = -1;
     mk_all[wave][lane + 64] = -1;
+    g6 = 6.0 * (double)gsc;
+    ig6 = 1.0 / g6;
   }
-  const double g6 = 6.0 * (double)gsc, ig6 = 1.0 / g6;
   float a[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1422,12 +1584,15 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
   const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
                    (unsigned)((nb + 63) / 64), (unsigned)n_groups);
 #define LH_SWEEP_PAIR(B, C)                                                                        \
-  if (equalize)                                                                                   \
-    hipLaunchKernelGGL((k_sweep_full<B, C, true>), grid, block, 0, stream, W, cout, cin, amax, H, P, \
-                       code, fp4, loss, rpw, opt);                                                   \
+  if (opt.nm > 0)                                                                                  \
+    hipLaunchKernelGGL((k_sweep_full<B, C, false, true>), grid, block, 0, stream, W, cout, cin, amax, \
+                       H, P, code, fp4, loss, rpw, opt);                                           \
+  else if (equalize)                                                                               \
+    hipLaunchKernelGGL((k_sweep_full<B, C, true, false>), grid, block, 0, stream, W, cout, cin, amax, \
+                       H, P, code, fp4, loss, rpw, opt);                                           \
   else                                                                                             \
-    hipLaunchKernelGGL((k_sweep_full<B, C, false>), grid, block, 0, stream, W, cout, cin, amax, H,  \
-                       P, code, fp4, loss, rpw, opt);                                                \
+    hipLaunchKernelGGL((k_sweep_full<B, C, false, false>), grid, block, 0, stream, W, cout, cin, amax, \
+                       H, P, code, fp4, loss, rpw, opt);                                           \
   hipLaunchKernelGGL((k_sweep_full_exact<B, C>), xgrid, block, 0, stream, W, cout, cin, amax, H, P, \
                      code, fp4, loss, opt)
   if (bf16 && P) {
@@ -1443,6 +1608,26 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
   return hipGetLastError();
 }
 
+hipError_t launch_accumulate_sweep(const void* X, const void* W, bool bf16, int64_t rows, int64_t cin,
+                                   const int64_t* offsets, int64_t n_groups, int64_t cout, const float* amax,
+                                   uint8_t* code, uint8_t* fp4, float* loss, const SweepOpts& opt,
+                                   hipStream_t stream) {
+  const int64_t nb = cin / 16;
+  if (cout == 0) return hipSuccess;
+  const int64_t R = stream::piece_rows(rows, nb);
+  const dim3 grid((unsigned)((nb + 3) / 4), (unsigned)n_groups);
+#define LH_FUSED(B, M)                                                                             \
+  hipLaunchKernelGGL((k_moe_fused<B, M>), grid, dim3(kWaves * 64), 0, stream, X, W, rows, cin, cout,  \
+                     offsets, R, amax, code, fp4, loss, opt)
+  if (bf16) {
+    if (opt.nm > 0) LH_FUSED(true, true); else LH_FUSED(true, false);
+  } else {
+    if (opt.nm > 0) LH_FUSED(false, true); else LH_FUSED(false, false);
+  }
+#undef LH_FUSED
+  return hipGetLastError();
+}
+
 hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t cout,
                              int64_t cin, const float* amax, const float* imp, uint8_t* code,
                              uint8_t* fp4, float* loss, const SweepOpts& opt, hipStream_t stream) {
@@ -1453,13 +1638,16 @@ hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t
   dim3 block(kWaves * 64);
   const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
                    (unsigned)((nb + 63) / 64), (unsigned)n_groups);
+#define LH_DIAG(B, M) \
+  hipLaunchKernelGGL((k_sweep_diag<B, M>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt)
   if (bf16) {
-    hipLaunchKernelGGL((k_sweep_diag<true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
+    if (opt.nm > 0) LH_DIAG(true, true); else LH_DIAG(true, false);
     hipLaunchKernelGGL((k_sweep_diag_exact<true>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
   } else {
-    hipLaunchKernelGGL((k_sweep_diag<false>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
+    if (opt.nm > 0) LH_DIAG(false, true); else LH_DIAG(false, false);
     hipLaunchKernelGGL((k_sweep_diag_exact<false>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);
   }
+#undef LH_DIAG
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
               "lh_activation_fake_quant", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag_ex",
-              "lh_dequantize_ex",
+              "lh_dequantize_ex", "lh_accumulate_sweep",
               "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_dequantize", "lh_absmax", "lh_last_error",
               "lh_version"):
         assert n in names
@@ -80,6 +80,14 @@ def test_validation_errors_without_device():
     nul = lh.SweepOptions(448.0, 3, None)
     c, m = _err(L.lh_scale_sweep_ex(FAKE, 1, 1, 16, 32, FAKE, FAKE, None, ctypes.byref(nul), FAKE, None, None, None))
     assert c == lh.LH_ERR_INVALID_ARGUMENT and "multipliers" in m
+    # fused accumulate-and-sweep: cout limit, offsets for several groups, options checked
+    c, m = _err(L.lh_accumulate_sweep(FAKE, FAKE, 1, 10, 32, FAKE, 2, 9000, FAKE, None, FAKE, None, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "8192" in m
+    c, m = _err(L.lh_accumulate_sweep(FAKE, FAKE, 1, 10, 32, None, 2, 16, FAKE, None, FAKE, None, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "group_offsets" in m
+    bad = lh.SweepOptions(300.0, 0, None)
+    c, m = _err(L.lh_accumulate_sweep(FAKE, FAKE, 1, 10, 32, FAKE, 2, 16, FAKE, ctypes.byref(bad), FAKE, None, None, None))
+    assert c == lh.LH_ERR_INVALID_ARGUMENT and "scale_norm" in m
     # no outputs, NULL input
     assert L.lh_accumulate(FAKE, 1, 10, 32, None, 1, 0.0, None, None, None) == lh.LH_ERR_INVALID_ARGUMENT
     assert L.lh_accumulate(None, 1, 10, 32, None, 1, 0.0, FAKE, None, None) == lh.LH_ERR_INVALID_ARGUMENT

@@ -267,3 +267,23 @@ def test_fullsize_activation_fake_quant_and_fused_accumulation():
         H_ref, P_ref = oracle.accumulate_act_aware(Xn, Xqn, wl.offsets)
         assert_h_close(H2[:, n0:n0 + 4], H_ref)
         assert_p_close(P2[:, n0:n0 + 4], P_ref, H_ref, cross_gram(Xn, Xqn, wl.offsets))
+
+
+def test_fullsize_fused_moe_equals_two_calls(run):
+    """The whole 512-expert layer through lh_accumulate_sweep (Hessians kept on chip): every code,
+    nibble and loss bit-identical to the two-call path the other tests checked against the oracle."""
+    name, wl, out = run
+    if wl.n_groups == 1:
+        pytest.skip("the fused path is for grouped rows")
+    note(f"full-size {name}: fused accumulate-and-sweep of all {wl.n_groups} experts")
+    W = to_dev(wl.W, wl.dtype)
+    X = to_dev(wl.X, wl.dtype)
+    off = torch.from_numpy(wl.offsets).to(DEV)
+    code, fp4, loss = lh.lh_accumulate_sweep(X, W, torch.from_numpy(out["amax"]).to(DEV), off)
+    torch.cuda.synchronize()
+    got = (code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy())
+    del W, X, code, fp4, loss
+    torch.cuda.empty_cache()
+    np.testing.assert_array_equal(got[0], out["code"])
+    np.testing.assert_array_equal(got[1], out["fp4"])
+    np.testing.assert_array_equal(got[2].view(np.int32), out["loss"].view(np.int32))
