@@ -82,6 +82,23 @@ lh_status lh_accumulate(const void* X, lh_dtype x_dtype, int64_t rows, int64_t c
                         float* H, float* imp, void* stream);
 
 /*
+ * lh_accumulate for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments, computation, results
+ * (bit for bit) and errors as lh_accumulate, but the partial sums and arrival counters live in a
+ * fixed array of 64 MiB per device that is part of the library's code object (each device the
+ * library runs on holds it until the process ends), instead of the library's memory pool: the
+ * call allocates nothing and records no event.  Every call on a device shares that device's
+ * array, so calls that overlap on one device (other streams, graph replays in flight at once)
+ * race and give wrong results; order them.  The arrival counters are cleared by a kernel at the
+ * start of each call.  A problem that needs more scratch than the array holds (dense layers need
+ * little; grouped rows need up to 2 * rows / R pieces x cin/64 slices x 4 KiB, R about
+ * rows * cin / 262144 rows, between 64 and 1024) fails with INVALID_ARGUMENT before any launch.
+ */
+lh_status lh_accumulate_noalloc(const void* X, lh_dtype x_dtype, int64_t rows, int64_t cin,
+                                const int64_t* group_offsets, int64_t n_groups, float beta,
+                                float* H, float* imp, void* stream);
+
+/*
  * Activation-aware Hessian and cross matrix (PR #1976, What does this PR do?):
  *   H[g][n] = beta*H[g][n] + X_q^T X_q / T_g,   P[g][n] = beta*P[g][n] + X_q^T (X_q - X) / T_g
  * per 16-channel block, over the rows of group g.  X and Xq are [rows, cin] of the same dtype.

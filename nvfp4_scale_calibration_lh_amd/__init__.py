@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("LH_LIBRARY") or os.path.join(_PKG, "liblh.so")
 LH_OK, LH_ERR_INVALID_ARGUMENT, LH_ERR_UNSUPPORTED, LH_ERR_HIP = 0, 1, 2, 3
 LH_DTYPE_F32, LH_DTYPE_BF16 = 0, 1
 
-EXPORTED = ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_activation_fake_quant",
+EXPORTED = ("lh_accumulate", "lh_accumulate_noalloc", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq", "lh_activation_fake_quant",
             "lh_accumulate_sweep", "lh_dequantize", "lh_dequantize_ex", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag",
             "lh_scale_sweep_diag_ex", "lh_scale_sweep_mse", "lh_absmax", "lh_last_error", "lh_version")
 MAX_MULTIPLIERS = 128
@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
         h = ctypes.CDLL(LIB_PATH)
         vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
         h.lh_accumulate.argtypes = [vp, i32, i64, i64, vp, i64, f32, vp, vp, vp]
+        h.lh_accumulate_noalloc.argtypes = [vp, i32, i64, i64, vp, i64, f32, vp, vp, vp]
         h.lh_accumulate_act_aware.argtypes = [vp, vp, i32, i64, i64, vp, i64, f32, vp, vp, vp]
         h.lh_accumulate_act_aware_fq.argtypes = [vp, i32, i64, i64, vp, i64, vp, f32, vp, vp, vp]
         h.lh_activation_fake_quant.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, vp]
@@ -65,7 +66,7 @@ def lib() -> ctypes.CDLL:
         h.lh_scale_sweep_mse.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
         h.lh_absmax.argtypes = [vp, i32, i64, i64, vp, vp]
         h.lh_dequantize.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
-        for f in ("lh_accumulate", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
+        for f in ("lh_accumulate", "lh_accumulate_noalloc", "lh_accumulate_act_aware", "lh_accumulate_act_aware_fq",
                   "lh_activation_fake_quant", "lh_scale_sweep", "lh_scale_sweep_ex", "lh_scale_sweep_diag_ex",
                   "lh_dequantize_ex", "lh_accumulate_sweep",
                   "lh_scale_sweep_diag", "lh_scale_sweep_mse", "lh_absmax", "lh_dequantize"):
@@ -142,6 +143,25 @@ def lh_accumulate(X: torch.Tensor, H: Optional[torch.Tensor] = None, imp: Option
         _need(imp, "imp", (G, cin), torch.float32)
     _check(lib().lh_accumulate(_ptr(X), _dtype_code(X), rows, cin, _ptr(offsets), G, float(beta),
                                _ptr(H), _ptr(imp), _stream(X.device)))
+    return H, imp
+
+
+def lh_accumulate_noalloc(X: torch.Tensor, H: torch.Tensor = None, imp: Optional[torch.Tensor] = None,
+                          offsets: Optional[torch.Tensor] = None, beta: float = 0.0):
+    """lh_accumulate that allocates nothing (no output allocation here either: H and/or imp are
+    required), its scratch in the library's fixed per-device array; overlapping calls on one
+    device race."""
+    _need(X, "X")
+    rows, cin = X.shape
+    offsets, G = _offsets(offsets, X)
+    if H is None and imp is None:
+        raise ValueError("H and/or imp must be given")
+    if H is not None:
+        _need(H, "H", (G, cin // 16, 16, 16), torch.float32)
+    if imp is not None:
+        _need(imp, "imp", (G, cin), torch.float32)
+    _check(lib().lh_accumulate_noalloc(_ptr(X), _dtype_code(X), rows, cin, _ptr(offsets), G, float(beta),
+                                       _ptr(H), _ptr(imp), _stream(X.device)))
     return H, imp
 
 

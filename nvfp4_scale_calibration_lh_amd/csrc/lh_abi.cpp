@@ -233,6 +233,29 @@ lh_status run_accumulate(const void* X, const void* Xq, const float* x_amax, lh_
   return ok();
 }
 
+// Scratch of the allocation-free accumulation: one fixed array per device, part of the library's
+// code object (so each device that loads the library holds it until the process ends).  Host code
+// never uses the name `scratch` as an address: each device's own copy is looked up once, with
+// that device current, and kept in noalloc_ptr.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of this device's `scratch` (the caller has made `dev` current).
+lh_status noalloc_scratch(int dev, unsigned char** out) {
+  static std::mutex mu;
+  static unsigned char* ptrs[64] = {};
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 0 || dev >= 64) return fail(LH_ERR_UNSUPPORTED, "device %d out of range", dev);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    ptrs[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = ptrs[dev];
+  return LH_OK;
+}
+
 lh_status check_sweep_shapes(int64_t n_groups, int64_t cout, int64_t cin) {
   if (n_groups < 1 || n_groups > 65535) return fail(LH_ERR_INVALID_ARGUMENT, "n_groups must be in [1, 65535] (got %lld)", (long long)n_groups);
   // the sweep grid takes 32 rows per workgroup along its 16-bit y dimension
@@ -281,6 +304,43 @@ lh_status lh_accumulate(const void* X, lh_dtype x_dtype, int64_t rows, int64_t c
   if (!H && !imp) return fail(LH_ERR_INVALID_ARGUMENT, "at least one of H, imp must be given");
   if (!X && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X is NULL");
   return run_accumulate(X, nullptr, nullptr, x_dtype, rows, cin, group_offsets, n_groups, beta, H, nullptr, imp, stream);
+}
+
+lh_status lh_accumulate_noalloc(const void* X, lh_dtype x_dtype, int64_t rows, int64_t cin,
+                                const int64_t* group_offsets, int64_t n_groups, float beta, float* H,
+                                float* imp, void* stream) {
+  if (!dtype_ok(x_dtype)) return fail(LH_ERR_UNSUPPORTED, "unknown dtype %d", (int)x_dtype);
+  lh_status st = check_shapes_x(rows, cin, group_offsets, n_groups);
+  if (st != LH_OK) return st;
+  if (!H && !imp) return fail(LH_ERR_INVALID_ARGUMENT, "at least one of H, imp must be given");
+  if (!X && rows > 0) return fail(LH_ERR_INVALID_ARGUMENT, "X is NULL");
+  const lh::AccScratch need = lh::accumulate_scratch(rows, cin / 16, group_offsets, n_groups, x_dtype == LH_DTYPE_BF16,
+                                                    false, H == nullptr);
+  const size_t work = (std::max<size_t>(need.work_bytes, 16) + 255) / 256 * 256;
+  const size_t counters = std::max<size_t>(need.counters, 1);
+  if (work + counters * sizeof(unsigned) > kNoAllocScratchBytes)
+    return fail(LH_ERR_INVALID_ARGUMENT,
+                "this accumulation needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                "(use lh_accumulate, or fewer rows or channels per call)",
+                work + counters * sizeof(unsigned), kNoAllocScratchBytes);
+  int dev = -1;
+  st = check_pointers({{X, "X"}, {group_offsets, "group_offsets"}, {H, "H"}, {imp, "imp"}}, &dev);
+  if (st != LH_OK) return st;
+  if ((st = check_aligned(X, "X")) != LH_OK) return st;
+  DeviceGuard guard;
+  if ((st = guard.enter(dev)) != LH_OK) return st;
+  unsigned char* base = nullptr;
+  if ((st = noalloc_scratch(dev, &base)) != LH_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned* ctr = reinterpret_cast<unsigned*>(base + work);
+  // the counters must start at zero: every call leaves them zero, but a previous call on this
+  // device may not have completed normally, so they are cleared (by a kernel, not a memset node)
+  hipError_t e = lh::launch_zero_fill(ctr, counters, s);
+  if (e == hipSuccess)
+    e = lh::launch_accumulate(X, nullptr, nullptr, x_dtype == LH_DTYPE_BF16, rows, cin, group_offsets, n_groups, beta,
+                              H, nullptr, imp, base, work, ctr, counters, s);
+  if (e != hipSuccess) return hip_fail(e, "allocation-free accumulate launch");
+  return ok();
 }
 
 lh_status lh_accumulate_act_aware(const void* X, const void* Xq, lh_dtype dtype, int64_t rows,
