@@ -407,10 +407,11 @@ __global__ __launch_bounds__(NW * 64) void k_imp_dense(const void* __restrict__ 
 // Grouped rows.  Every group is cut into pieces of at most R rows (a group without rows is one
 // empty piece).  Pieces are numbered in group order, the pieces of one group consecutive; the
 // schedule runs the R-row pieces first (longest work first), then the others, each part in piece
-// order.  A 1-D grid of ceil(capacity / 4) x slices workgroups, slice fastest (the slices of the
-// same rows run together); wave w of workgroup x owns the piece in schedule slot 4x + w.  Each
-// workgroup derives its pieces itself from a scan of the group offsets in LDS (no planning
-// kernel, no table in memory).  Only groups of several pieces leave partial sums; their pieces
+// order.  A 1-D grid of capacity x ceil(slices / 4) workgroups: the four waves of a workgroup take
+// the same piece in four neighbouring slices (the same rows, so the same work, and 512
+// contiguous bytes of every row), the slices of one piece run together.  Each workgroup derives
+// its piece itself from a scan of the group offsets in LDS (no planning kernel, no table in
+// memory).  Only groups of several pieces leave partial sums; their pieces
 // own the slots, numbered in group order among themselves (fewer than 2 rows / R of them).
 // Partial layout: [slot][slice][m][block][kPart]; counters: [group][slice].
 // ---------------------------------------------------------------------------------------------
@@ -428,7 +429,9 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
   __shared__ int64_t scan_m[kThreads];        // pieces of groups of more than one piece
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, gg = lane >> 4;
-  const int64_t slices = (nb + 3) / 4, slice = blockIdx.x % slices;
+  // workgroup x: the piece in schedule slot x / sgroups, its wave w the slice 4 (x % sgroups) + w
+  const int64_t slices = (nb + 3) / 4, sgroups = (slices + 3) / 4;
+  const int64_t slice = (int64_t)(blockIdx.x % sgroups) * 4 + wave;
 
   // rows of group g, clamped to [0, rows] so that offsets outside the contract never address
   // memory outside X; its pieces: f of exactly R rows and n in all
@@ -476,9 +479,9 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
   const int64_t last = uni(scan[kThreads - 1]);
   const int64_t tot_full = last & 0xFFFFFFFF;
   const int64_t total = tot_full + (last >> 32);
-  const int64_t sidx = (int64_t)(blockIdx.x / slices) * 4 + wave;
+  const int64_t sidx = (int64_t)blockIdx.x / sgroups;
   // more pieces than the capacity only if the offsets break the contract: then nothing is done
-  if (total > cap || uni(scan_m[kThreads - 1]) > mcap || sidx >= total) return;   // whole wave leaves
+  if (total > cap || uni(scan_m[kThreads - 1]) > mcap || sidx >= total || slice >= slices) return;   // whole wave leaves
   // schedule slot -> piece: the thread whose groups hold it (first inclusive count above the
   // rank), then a walk over that thread's groups (wave-uniform)
   const bool full = sidx < tot_full;
@@ -602,7 +605,7 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
   const int64_t cap = rows / R + G;           // >= sum over groups of max(1, ceil(T_g / R))
   const int64_t mcap = multi_piece_cap(rows, R);
   float* ws = (float*)work;
-  hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG, FQ>), dim3((unsigned)(((cap + 3) / 4) * slices)),
+  hipLaunchKernelGGL((k_acc_pieces<BF16, ACT, DIAG, FQ>), dim3((unsigned)(cap * ((slices + 3) / 4))),
                      dim3(kThreads), 0, stream, X, Xq, x_amax, cin, off, G, rows, R, cap, mcap, beta, H, P, imp,
                      ws, counters, nb);
   return hipGetLastError();
