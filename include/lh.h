@@ -61,7 +61,15 @@ typedef enum {
   LH_ERR_HIP = 3               /* a HIP runtime call or launch failed */
 } lh_status;
 
-typedef enum { LH_DTYPE_F32 = 0, LH_DTYPE_BF16 = 1 } lh_dtype;
+/* The two sentinels widen the enum's value range to every 32-bit int: a value other than F32 or
+ * BF16 coming from a caller is then a well-defined lh_dtype in C and C++, and every entry point
+ * rejects it with LH_ERR_UNSUPPORTED.  They are not dtypes. */
+typedef enum {
+  LH_DTYPE_F32 = 0,
+  LH_DTYPE_BF16 = 1,
+  LH_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  LH_DTYPE_RANGE_MAX_ = 2147483647
+} lh_dtype;
 
 /*
  * Per-block local Hessian and importance (PR #788, Overview / Changes: per-block Hessians
