@@ -27,10 +27,20 @@
 //    group offsets; each wave owns one piece, so a group of at most R rows is finished by one wave
 //    with no synchronization.  Pieces of larger groups leave
 //    partial sums and the last of them to finish adds them in piece order.
-//  * Pieces' partial sums cross workgroups through agent-scope relaxed atomic stores and loads (coherent
-//    across the per-XCD L2 caches without whole-cache flushes), ordered by waiting for the stores
-//    before an arrival counter is incremented; the last arrival clears the counter for the next
-//    call.  Summation orders never depend on timing: results are bit-identical run to run.
+//  * Partial sums and arrival counters that cross workgroups are touched only through relaxed
+//    agent-scope atomics (aligned 4 or 8 bytes), so no access is a data race; gfx950 performs each
+//    at the device's coherence point, past the per-XCD L2 caches (stores and loads carry the sc1
+//    scope bit; the counter add is a returning atomic).  The order the last arriver relies on --
+//    every piece's partial stores before its own loads -- is made by the instruction stream: a
+//    wave waits for its stores to complete (s_waitcnt vmcnt(0); in the dense kernels every wave
+//    waits, then a workgroup barrier, then one thread adds) before it adds to the counter, and the
+//    last arriver issues its loads only once the add has returned the count.  That is the
+//    compiler's own agent-scope release/acquire sequence minus the L2 writeback and invalidate,
+//    which serve non-atomic data, and no non-atomic data is shared here.  A CPU test checks the
+//    generated code for the wait.  Declaring the add release or acq_rel puts the writeback on
+//    every arrival and doubles the 512-expert layer's accumulation time, so it is not done.  The
+//    last arrival clears the counter for the next call.  Summation orders never depend on timing:
+//    results are bit-identical run to run.
 //  * When only the importance is wanted, partial sums keep just the 16 diagonal entries.
 #include "lh_internal.hpp"
 #include "acc_stream.hpp"

@@ -287,3 +287,93 @@ def test_fullsize_fused_moe_equals_two_calls(run):
     np.testing.assert_array_equal(got[0], out["code"])
     np.testing.assert_array_equal(got[1], out["fp4"])
     np.testing.assert_array_equal(got[2].view(np.int32), out["loss"].view(np.int32))
+
+
+def test_fullsize_grouped_equals_per_expert(run):
+    """Grouped rows against one call per expert (the expert's rows alone, as a dense layer) on eight
+    whole experts of the 512-expert layer, with the largest and the smallest routed-token counts:
+    the sweep of one expert's weights and Hessian is bit-identical to that expert's part of the
+    grouped sweep; the expert's own accumulation and the grouped one are both within tolerance of
+    the float64 sums of exactly its rows (the summation orders differ, so not bit for bit); and the
+    tolerance is not vacuous: the same check against the rows of the next expert fails."""
+    name, wl, out = run
+    if wl.n_groups == 1:
+        pytest.skip("grouped rows only")
+    groups = _sweep_groups(wl)
+    off = wl.offsets
+    note(f"full-size {name}: per-expert calls for experts {groups.tolist()}")
+    for g in groups:
+        g = int(g)
+        a, b = int(off[g]), int(off[g + 1])
+        Wg = to_dev(wl.W[g], wl.dtype)
+        am = torch.from_numpy(out["amax"][g:g + 1]).to(DEV)
+        Hg = torch.from_numpy(np.ascontiguousarray(out["H"][g:g + 1])).to(DEV)
+        code, fp4, loss = lh.lh_scale_sweep(Wg, am, Hg)
+        Hd = lh.lh_accumulate(to_dev(wl.X[a:b], wl.dtype))[0] if b > a else None
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(code.cpu().numpy()[0], out["code"][g])
+        np.testing.assert_array_equal(fp4.cpu().numpy()[0], out["fp4"][g])
+        np.testing.assert_array_equal(loss.cpu().numpy()[0].view(np.int32), out["loss"][g].view(np.int32))
+        H_ref, _ = oracle.accumulate(wl._f64(wl.X[a:b]), np.array([0, b - a]))
+        assert_h_close(out["H"][g:g + 1], H_ref)
+        if Hd is None:
+            assert not out["H"][g].any(), f"expert {g} has no rows and must have H = 0"
+            continue
+        assert_h_close(Hd.cpu().numpy(), H_ref)
+        nxt = int(np.nonzero(np.diff(off)[g + 1:])[0][0]) + g + 1 if np.diff(off)[g + 1:].any() else None
+        if nxt is not None:
+            c, d = int(off[nxt]), int(off[nxt + 1])
+            H_other, _ = oracle.accumulate(wl._f64(wl.X[c:d]), np.array([0, d - c]))
+            with pytest.raises(AssertionError):
+                assert_h_close(out["H"][g:g + 1], H_other)
+        del Wg, Hg, Hd, code, fp4, loss
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_non_vacuity(run):
+    """The local-Hessian (or importance-weighted) codes differ from the plain weight-MSE search's on
+    a clearly non-zero share of the blocks of the whole layer: the objective decides."""
+    name, wl, out = run
+    note(f"full-size {name}: plain MSE search of the whole layer")
+    W = to_dev(wl.W, wl.dtype)
+    code, _, _ = lh.lh_scale_sweep_mse(W, torch.from_numpy(out["amax"]).to(DEV), want_fp4=False, want_loss=False)
+    torch.cuda.synchronize()
+    frac = float(np.mean(code.cpu().numpy() != out["code"]))
+    del W, code
+    torch.cuda.empty_cache()
+    note(f"full-size {name}: {frac:.3f} of the blocks take a different scale than under plain MSE")
+    assert frac > 0.05, frac
+
+
+def test_fullsize_full_sweep_on_diagonal_hessian(run):
+    """The full-Hessian sweep given H_n = diag(importance of block n) chooses, block for block, what
+    the diagonal sweep chose on the whole WMSE layer: identical codes and FP4 nibbles outside
+    near-ties (each differing block is confirmed a near-tie by the oracle), losses within 1e-5."""
+    name, wl, out = run
+    if wl.mode != "diag":
+        pytest.skip("the diagonal (importance) workload")
+    imp = out["imp"]
+    G, nb = imp.shape[0], wl.n_blocks
+    Hd = np.zeros((G, nb, 16, 16), dtype=np.float32)
+    idx = np.arange(16)
+    Hd[:, :, idx, idx] = imp.reshape(G, nb, 16)
+    note(f"full-size {name}: full sweep on H = diag(importance)")
+    W = to_dev(wl.W, wl.dtype)
+    code, fp4, loss = lh.lh_scale_sweep(W, torch.from_numpy(out["amax"]).to(DEV), torch.from_numpy(Hd).to(DEV))
+    torch.cuda.synchronize()
+    code, fp4, loss = code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy()
+    del W
+    torch.cuda.empty_cache()
+    cout = wl.cout
+    diff = (code != out["code"]) | (fp4.reshape(G, cout, nb, 8) != out["fp4"].reshape(G, cout, nb, 8)).any(-1)
+    note(f"full-size {name}: {int(diff.sum())} of {diff.size} blocks differ; checking them with the oracle")
+    if diff.any():
+        g_, r_, n_ = np.nonzero(diff)
+        w = np.stack([wl._f64(wl.W[g, r, 16 * n:16 * n + 16]) for g, r, n in zip(g_, r_, n_)])
+        gs = oracle.global_scale(out["amax"][g_].astype(np.float64))
+        res = oracle.sweep_blocks_diag(w, gs, imp[g_].reshape(len(g_), nb, 16)[np.arange(len(g_)), n_].astype(np.float64))
+        assert oracle.exempt_mask(res).all(), f"{int((~oracle.exempt_mask(res)).sum())} differing blocks are not near-ties"
+    same = ~diff
+    scale = np.abs(out["loss"].astype(np.float64))
+    lbad = same & (np.abs(loss.astype(np.float64) - out["loss"]) > 1e-5 * scale + 1e-30)
+    assert not lbad.any(), f"{int(lbad.sum())} losses differ by more than 1e-5"

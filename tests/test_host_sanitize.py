@@ -5,6 +5,7 @@ tests/host/abi_checks.cpp.  The kernels are compiled as usual; only the host sid
 import os
 import shutil
 import subprocess
+import sys
 import tempfile
 
 import pytest
@@ -13,8 +14,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "nvfp4_scale_calibration_lh_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 KERNELS = ["absmax.hip", "accumulate.hip", "sweep.hip", "dequant.hip"]
-COMMON = ["-O1", "-g", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature",
-          "-Xclang", "-packed-fp32-ops"]
+sys.path.insert(0, ROOT)
+from nvfp4_scale_calibration_lh_amd.build import FLAGS  # noqa: E402  (the library's own compile flags)
+
+COMMON = ["-O1", "-g"] + [f for f in FLAGS if f not in ("-O3", "-Wall")]
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 
