@@ -19,9 +19,10 @@
 //  * The contraction H_n e is reorganized so the matrix cores see exact small integers:
 //    (H e)_i = s (H q)_i - (H w)_i, where q holds E2M1 grid values times a power of 4 (at most
 //    2 significant bits, exact in bf16).  H_n is split once per column into two bf16 pieces
-//    (H1 + H2 equals H to 2^-18 relative, a residual the error bound below covers), so one
-//    v_mfma_f32_16x16x32_bf16 with K slots [H1 | H2] gives H q for 16 candidates with exact products and fp32
-//    accumulation.  H w (and P w, |P||w| in the coupled form) comes from v_mfma_f32_16x16x4_f32
+//    (H1 + H2 equals H to 2^-18 relative, a residual the error bound below covers), so two
+//    chained v_mfma_f32_16x16x16_bf16 (H2 q onto the accumulator input, then H1 q) give H q for
+//    16 candidates with exact products and fp32 accumulation.  (One 16x16x32 instruction with K
+//    slots [H1 | H2] needs q twice in its B operand, two register copies per tile.)  H w (and P w, |P||w| in the coupled form) comes from v_mfma_f32_16x16x4_f32
 //    once per 16-row tile; -(H w - 2 P w)/s is the accumulator input of the H q MFMA, so its
 //    result times s is H e + 2 P w.  The loss L = e^T (H e + 2 P w) is a 4-term dot per lane
 //    reduced over the 4 lane groups with permlane swaps and scaled by s once; the argmin over lanes uses DPP row rotations and
@@ -70,12 +71,13 @@ constexpr int kWaves = 4;            // waves per workgroup; wave w takes block 
 constexpr int kRowsPerWave = 32;     // rows (blocks of one column) per wave
 constexpr int kExactRows = 16;       // rows per wave of the float64 passes
 // Filter error bound factor.  Full form: per element i the computed s y_i misses (H e + 2b)_i by
-// at most d_i (S_w + S_e) 2^-18 (two-piece split of H), gamma_32 d_i (2 S_w + S_e) (fp32
+// at most d_i (S_w + S_e) 2^-18 (two-piece split of H), gamma_33 d_i (2 S_w + S_e) (fp32
 // accumulation of 32 exact products onto the accumulator input, whose size is at most
-// d_i S_w + 2(|P||w|)_i), 2^-20 d_i S_w (H w on fp32 MFMA) and 2^-23 d_i S_w (the accumulator
-// input's two roundings); weighted by |e_i| and summed, with the dot product's own roundings,
-// that is at most about 2^-16.8 (S_e^2 + S_e S_w + 2|e|^T(|P||w|)) <= 2^-16.8 A (A_k as in the
-// header), so 2^-16 leaves a margin of about 1.75x.
+// d_i S_w + 2(|P||w|)_i, in two chained instructions of 16 products each: gamma_16 for each plus
+// the hand-over, at most gamma_33 of the terms' absolute sum), 2^-20 d_i S_w (H w on fp32 MFMA)
+// and 2^-23 d_i S_w (the accumulator input's two roundings); weighted by |e_i| and summed, with
+// the dot product's own roundings, that is at most about 2^-16.8 (S_e^2 + S_e S_w +
+// 2|e|^T(|P||w|)) <= 2^-16.8 A (A_k as in the header), so 2^-16 leaves a margin of about 1.7x.
 constexpr float kErrC = 0x1p-16f;
 constexpr int kNearUlps = 16;        // midpoint proximity test, in ulps of |w|/(m g)
 
@@ -330,7 +332,8 @@ struct FullLds {
   int mk[128];         // codes proposed by the multipliers, tagged with the row
 };
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // bf16 round-to-nearest-even of a finite float, as bits in the low half.
@@ -472,9 +475,10 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
     pa[t] = fabsf(pv[t]);
     hpmax = fmaxf(hpmax, fmaxf(mx, pa[t]));
   }
-  // one 16x16x32 bf16 MFMA per tile: K slots [H1 | H2] against [q | q]
-  const v4u A1u = {h1[0] | (h1[1] << 16), h1[2] | (h1[3] << 16), h2[0] | (h2[1] << 16), h2[2] | (h2[3] << 16)};
-  const v8bf A1 = __builtin_bit_cast(v8bf, A1u);
+  // two chained 16x16x16 bf16 MFMAs per tile: H2 q onto the accumulator input, then H1 q
+  const v2u A1u = {h1[0] | (h1[1] << 16), h1[2] | (h1[3] << 16)};
+  const v2u A2u = {h2[0] | (h2[1] << 16), h2[2] | (h2[3] << 16)};
+  const v4s A1 = __builtin_bit_cast(v4s, A1u), A2 = __builtin_bit_cast(v4s, A2u);
 
   // ---- candidate scales.  Tile tau holds codes 16*tau + i + 1.  Tile 0 (codes 1..16) uses
   // s0/is0 directly.  For tau >= 1 the lane's codes share one E4M3 mantissa and step the exponent
@@ -658,9 +662,10 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int tau = 4 * q + u;
-            const v4u Bu = {p01, p23, p01, p23};
-            const v8bf B = __builtin_bit_cast(v8bf, Bu);
-            const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, tau == 0 ? cacc0 : cacc1, 0, 0, 0);
+            const v2u Bu = {p01, p23};
+            const v4s B = __builtin_bit_cast(v4s, Bu);
+            const v4f y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                A1, B, __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A2, B, tau == 0 ? cacc0 : cacc1, 0, 0, 0), 0, 0, 0);
             if (tau < 7) tile_err(tau + 1, en, pn01, pn23);         // overlaps the MFMAs
             // bound: uncoupled, this lane's part of S_e = sum_i d_i |e_i| (A follows after the
             // group sum); coupled, (2 S_e,g)^2 + sum_i |e_i| om_i over the lane's 4 elements,
