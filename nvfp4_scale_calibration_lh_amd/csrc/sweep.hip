@@ -226,6 +226,28 @@ __device__ inline void apply_overrides(unsigned long long m, int pbase, int kv, 
   }
 }
 
+// The same overrides applied to the packed FP4 codes of tile tau (elements 4*gg..4*gg+3 of the
+// lane's candidate 16*tau + i + 1, nibble t at bits 4t): a flagged pair's nibble becomes the
+// convert of its exact-side quotient w / s_k (scale 1, the same rounding as that quotient times
+// 4^(tau-1) under the tile's power-of-4 scale).  The quotients themselves are left alone, so the
+// common path and the override path read the same registers.
+__device__ inline unsigned patch_overrides(unsigned long long m, int pbase, int kv, float rv, int tau,
+                                           int i, int gg, unsigned pk) {
+  while (m) {
+    const int b = __builtin_ctzll(m);
+    m &= m - 1;
+    const int k = __builtin_amdgcn_readlane(kv, b);
+    if (k == 0 || ((k - 1) >> 4) != tau) continue;
+    const int el = (b + pbase) / 7;
+    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), b));
+    const unsigned nib = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, v, 1.0f, 0) & 0xFu;
+    const unsigned sh = 4u * (unsigned)(el & 3);
+    const bool me = gg == (el >> 2) && i == ((k - 1) & 15);
+    pk = me ? ((pk & ~(0xFu << sh)) | (nib << sh)) : pk;
+  }
+  return pk;
+}
+
 // Overrides for element el of candidate kmatch (used when emitting the winner's codes).
 __device__ inline float override_for(unsigned long long m, int pbase, int kv, float rv, int kmatch,
                                      int el, float r) {
@@ -605,9 +627,12 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
           if (k != 0) tile_hit |= 1u << ((k - 1) >> 4);
         }
       }
-      float rb[4];                                   // w / s for this lane's tile-1 code
+      float ra[4], rb[4];                            // w / s for this lane's tile-0 and tile-1 codes
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rb[t] = w[t] * is1;
+      for (int t = 0; t < 4; ++t) {
+        ra[t] = w[t] * is0;
+        rb[t] = w[t] * is1;
+      }
       // accumulator inputs -(H w - 2 P w)_i / s of tile 0 and of tiles 1..7 (which share s1)
       v4f cacc0, cacc1;
 #pragma unroll
@@ -626,21 +651,15 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
         constexpr bool OVR = decltype(ovr_tag)::value;
         auto tile_err = [&](int tau, float e[4], unsigned& p01, unsigned& p23) {
           const float sc = tau == 0 ? 1.0f : (float)(1u << (2 * (tau - 1)));   // 4^(tau-1)
-          float r[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) r[t] = tau == 0 ? w[t] * is0 : rb[t];
-          if (OVR && ((tile_hit >> tau) & 1u)) {      // overrides are actual quotients w / s_k
-            const float isc = 1.0f / sc;               // powers of two: exact
-            float o[4] = {r[0] * isc, r[1] * isc, r[2] * isc, r[3] * isc};
-            apply_overrides(m0, 0, kv0, rv0, tau, 0, i, gg, o);
-            apply_overrides(m1, 64, kv1, rv1, tau, 0, i, gg, o);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) r[t] = o[t] * sc;
-          }
+          const float* r = tau == 0 ? ra : rb;
           // bytes 0 and 1 of the pack register are written and read; its other bytes never
           // are, so the register carried from the previous tile serves as the old value
           pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, r[0], r[1], sc, 0);
           pkc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pkc, r[2], r[3], sc, 1);
+          if (OVR && ((tile_hit >> tau) & 1u)) {      // exact decisions replace their nibbles
+            pkc = patch_overrides(m0, 0, kv0, rv0, tau, i, gg, pkc);
+            pkc = patch_overrides(m1, 64, kv1, rv1, tau, i, gg, pkc);
+          }
           const unsigned pk = pkc;
           const v2f q01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc, 0);
           const v2f q23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, sc, 1);
