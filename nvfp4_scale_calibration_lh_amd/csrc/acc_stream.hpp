@@ -162,11 +162,15 @@ __device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool f
   return out;
 }
 
-// One wave's streaming contraction of rows [r0, r1) of a 64-channel slice into four blocks of
-// accumulators, using the wave's own LDS stage.  Chunks are taken with a stride of `step` chunks
-// starting at chunk `first` (counted from r0), so several waves can share a range.  With FQ the
-// activation-aware X_q is not read: it is made from X in registers (act_fake_quant) while the
-// next chunk's loads are in flight.
+// One wave's streaming contraction of 64-channel row slices into four blocks of accumulators,
+// using the wave's own LDS stage.  A chunk is 32 rows starting at row c0 of a range that ends at
+// r1: issue() puts its loads in flight (rows past the range re-read its last row, channels past
+// cin read channel 0; every lane issues the same loads on every path), stage_chunk() writes it to
+// the stage with those rows and channels zeroed,
+// finish_stage() makes the stage visible to the whole wave (with FQ it first makes X_q from the
+// staged X: X_q is not read, it is made in registers while later chunks' loads are in flight),
+// and contract() adds it to the accumulators.  The next chunk's loads are issued between
+// stage_chunk() and contract(), so one chunk is in flight while a chunk is contracted.
 template <bool BF16, bool ACT, bool FQ = false>
 struct Streamer {
   using Gm = Geo<BF16>;
@@ -180,6 +184,7 @@ struct Streamer {
   float gx = 0.0f;              // FQ: the group's gX, 1/(6 gX) in float64, gX in the fast range
   double inv6g = 0.0;
   bool fq_fast = false;
+  v4u pre[kM][Gm::kLoads];      // the chunk in flight
 
   __device__ void set_fake_quant(float x_amax) {
     gx = x_amax / 2688.0f;                       // fp32(amax / (6*448)), correctly rounded
@@ -187,70 +192,70 @@ struct Streamer {
     fq_fast = gx >= 0x1p-100f && gx <= 0x1p100f;
   }
 
-  __device__ void run(int64_t r0, int64_t r1, int first, int step) {
+  __device__ void zero() {
 #pragma unroll
     for (int b = 0; b < 4; ++b) accH[b] = accP[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ int lrow() const { return BF16 ? (lane >> 3) : (lane >> 4); }
+  __device__ int lcol() const { return BF16 ? (lane & 7) * 8 : (lane & 15) * 4; }
+  __device__ bool col_on() const { return ch0 + lcol() < cin; }
+  __device__ static int word(int row, int col) { return BF16 ? (row * kPitchH + col) / 2 : row * kPitchF + col; }
+
+  __device__ void issue(int64_t c0, int64_t r1) {
+    const int esz = BF16 ? 2 : 4;
+    const int64_t col = col_on() ? ch0 + lcol() : 0;
+#pragma unroll
+    for (int q = 0; q < Gm::kLoads; ++q) {
+      const int64_t r = min(c0 + lrow() + q * Gm::kRowsPerLoad, r1 - 1);
+      const int64_t byte = (r * cin + col) * esz;
+#pragma unroll
+      for (int m = FQ ? 1 : 0; m < kM; ++m) {
+        const char* base = (m == 0) ? (ACT ? Xq : X) : X;    // act-aware: matrix 0 = X_q, 1 = X
+        pre[m][q] = __builtin_nontemporal_load((const v4u*)(base + byte));
+      }
+    }
+  }
+
+  // With FQ only X is staged, into the second matrix's place.
+  __device__ void stage_chunk(int64_t c0, int64_t r1) {
+#pragma unroll
+    for (int q = 0; q < Gm::kLoads; ++q) {
+      const int row = lrow() + q * Gm::kRowsPerLoad;
+      const bool on = col_on() && c0 + row < r1;
+#pragma unroll
+      for (int m = FQ ? 1 : 0; m < kM; ++m)
+        *(v4u*)&stage[m * Gm::kWords + word(row, lcol())] = on ? pre[m][q] : v4u{0u, 0u, 0u, 0u};
+    }
+  }
+
+  __device__ void finish_stage() {
+    if constexpr (FQ) {
+      // each lane reads back its own 16 bytes of X to make X_q (an X of zeros stays zero)
+#pragma unroll
+      for (int q = 0; q < Gm::kLoads; ++q) {
+        const int w = word(lrow() + q * Gm::kRowsPerLoad, lcol());
+        const v4u xv = *(const v4u*)&stage[Gm::kWords + w];
+        *(v4u*)&stage[w] = act_fake_quant<BF16>(xv, gx, inv6g, fq_fast);   // every lane: uses its pair/quad
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // Rows [r0, r1) from zero, chunks taken with a stride of `step` chunks starting at chunk `first`
+  // (counted from r0), so several waves can share a range.
+  __device__ void run(int64_t r0, int64_t r1, int first, int step) {
+    zero();
     if (r1 <= r0) return;
     const int nchunks = (int)((r1 - r0 + kChunk - 1) / kChunk);
-    const int lrow = BF16 ? (lane >> 3) : (lane >> 4);
-    const int lcol = BF16 ? (lane & 7) * 8 : (lane & 15) * 4;
-    const bool col_on = ch0 + lcol < cin;
-    const int esz = BF16 ? 2 : 4;
-    v4u pre[kM][Gm::kLoads];
-    // Every lane issues the same loads on every path (rows past the range re-read its last row,
-    // channels past cin read channel 0; both are zeroed when staged).
-    auto issue = [&](int j) {
-#pragma unroll
-      for (int q = 0; q < Gm::kLoads; ++q) {
-        const int64_t r = min(r0 + (int64_t)j * kChunk + lrow + q * Gm::kRowsPerLoad, r1 - 1);
-        const int64_t byte = (r * cin + (col_on ? ch0 + lcol : 0)) * esz;
-#pragma unroll
-        for (int m = FQ ? 1 : 0; m < kM; ++m) {
-          const char* base = (m == 0) ? (ACT ? Xq : X) : X;    // act-aware: matrix 0 = X_q, 1 = X
-          pre[m][q] = __builtin_nontemporal_load((const v4u*)(base + byte));
-        }
-      }
-    };
+    auto at = [&](int j) { return r0 + (int64_t)j * kChunk; };
     int j = first;
-    if (j < nchunks) issue(j);
+    if (j < nchunks) issue(at(j), r1);
     for (; j < nchunks; j += step) {
-      const int64_t c0 = r0 + (int64_t)j * kChunk;
-      if constexpr (FQ) {
-        // X goes to its stage first and the next chunk's loads are issued; each lane then reads
-        // back its own 16 bytes to make X_q (an X of zeros stays zero)
-#pragma unroll
-        for (int q = 0; q < Gm::kLoads; ++q) {
-          const int row = lrow + q * Gm::kRowsPerLoad;
-          const bool on = col_on && c0 + row < r1;
-          const int word = BF16 ? (row * kPitchH + lcol) / 2 : row * kPitchF + lcol;
-          *(v4u*)&stage[Gm::kWords + word] = on ? pre[1][q] : v4u{0u, 0u, 0u, 0u};
-        }
-        if (j + step < nchunks) issue(j + step);
-#pragma unroll
-        for (int q = 0; q < Gm::kLoads; ++q) {
-          const int row = lrow + q * Gm::kRowsPerLoad;
-          const int word = BF16 ? (row * kPitchH + lcol) / 2 : row * kPitchF + lcol;
-          const v4u xv = *(const v4u*)&stage[Gm::kWords + word];
-          *(v4u*)&stage[word] = act_fake_quant<BF16>(xv, gx, inv6g, fq_fast);   // every lane: uses its pair/quad
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        contract();
-        continue;
-      }
-#pragma unroll
-      for (int q = 0; q < Gm::kLoads; ++q) {
-        const int row = lrow + q * Gm::kRowsPerLoad;
-        const bool on = col_on && c0 + row < r1;
-        const int word = BF16 ? (row * kPitchH + lcol) / 2 : row * kPitchF + lcol;
-#pragma unroll
-        for (int m = 0; m < kM; ++m) *(v4u*)&stage[m * Gm::kWords + word] = on ? pre[m][q] : v4u{0u, 0u, 0u, 0u};
-      }
-      if (j + step < nchunks) issue(j + step);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      stage_chunk(at(j), r1);
+      if (j + step < nchunks) issue(at(j + step), r1);
+      finish_stage();
       contract();
     }
   }
@@ -339,6 +344,7 @@ inline int64_t piece_rows(int64_t rows, int64_t nb) {
   R = (R + kChunk - 1) / kChunk * kChunk;
   return R < 64 ? 64 : (R > 1024 ? 1024 : R);
 }
+
 
 }  // namespace stream
 }  // namespace lh

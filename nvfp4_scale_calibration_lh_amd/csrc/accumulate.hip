@@ -194,17 +194,18 @@ __device__ inline v4f load_partial(const float* w, int lane, int i, int gg) {
   return s;
 }
 
-// Sum of n partial blocks w0, w0 + stride, ... in order, eight loads in flight.
-template <bool DIAG>
+// Sum of n partial blocks w0, w0 + stride, ... in order, KF loads in flight (few enough that
+// this tail does not set the kernel's register count).
+template <bool DIAG, int KF = 4>
 __device__ inline v4f sum_partials(const float* w0, int64_t stride, int64_t n, int lane, int i, int gg) {
   v4f s = {0.f, 0.f, 0.f, 0.f};
   int64_t t = 0;
-  for (; t + 8 <= n; t += 8) {
-    v4f p[8];
+  for (; t + KF <= n; t += KF) {
+    v4f p[KF];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) p[u] = load_partial<DIAG>(w0 + (t + u) * stride, lane, i, gg);
+    for (int u = 0; u < KF; ++u) p[u] = load_partial<DIAG>(w0 + (t + u) * stride, lane, i, gg);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += p[u];
+    for (int u = 0; u < KF; ++u) s += p[u];
   }
   for (; t < n; ++t) s += load_partial<DIAG>(w0 + t * stride, lane, i, gg);
   return s;
