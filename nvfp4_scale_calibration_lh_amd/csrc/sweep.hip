@@ -1508,6 +1508,326 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Diagonal sweep over a window of 32 codes (float32 filter; no amax-multiplier search)
+// ------------------------------------------------------------------------------------------
+// Which codes can win.  Let kmax be a code with 6 s_kmax >= amax (the smallest such code or one
+// above it) and let the window be the 32 codes from start = clamp(kmax - 12, 1, 95) to
+// end = start + 31.  Below its amax a block's scale clips: every element keeps an error of at
+// least |w_i| - 6 s_k whatever its FP4 code, so for every k < start
+//   L_k >= LB_lo = sum_i Imp_i (|w_i| - 6 s_{start-1})_+^2.
+// Above the window every scale is at least s_hi = s_{end+1}; an element with |w_i| < s_hi / 2
+// then has a quotient below 1/2 and rounds to 0 or 1/2, so for every k > end
+//   L_k >= LB_hi = sum_{|w_i| < s_hi/2} Imp_i min(|w_i|, s_hi/2 - |w_i|)^2.
+// With U an upper bound of the window's exact minimum, LB_lo > U and LB_hi >= U (the lowest code
+// wins a tie, and codes above the window are higher) make the window's argmin the block's.  The
+// pages' score and candidate set are unchanged: the window only skips codes these bounds rule
+// out.  On the WMSE down_proj layer the argmin lies 11 codes below to 6 above kmax and both
+// bounds decide the block almost always; the others, like blocks whose window starts below
+// code 8 or that keep more than four contenders, are left at code 0 for the float64 kernel.
+//
+// Scoring.  Lane j of an 8-lane row group takes the codes start + j + 8t, t = 0..3, with scales
+// s, 2s, 4s, 8s (exact powers of two for codes >= 8 in fp32's normal range), so one quotient
+// w (1/s) per element serves all four through the FP4 convert's exponent-only scale operand, and
+// a wave scores eight rows at a time.  Each candidate's L' and its error bound are those of
+// k_sweep_diag (the weighted frame, constants kDiagC1..C3), with the line through lam set per
+// row; here 1/s comes from the hardware reciprocal (within one ulp), so a quotient is within
+// 1.5 2^-23 of |w|/s and a wrong-side rounding changes an element's e^2 by at most 84 delta of
+// itself instead of 56: with the 22 delta of the arithmetic that is 106 delta <= C1 = 128 delta.
+// Two to four contenders are scored again in float64 by the whole wave.
+
+// Smallest code k in 1..126 with v_k >= y (126 above 448, 1 at or below 2^-9).
+__device__ inline int e4m3_ceil_code(double y) {
+  if (!(y > 0x1p-9)) return 1;
+  if (y > 448.0) return 126;
+  const int e = ilogb(y);
+  if (e < -6) return (int)ceil(y * 512.0);                 // subnormal values m 2^-9
+  const int f = (int)ceil((ldexp(y, -e) - 1.0) * 8.0);     // 0..8 (8: the next binade's first)
+  return min((e + 7) * 8 + f, 126);
+}
+
+// Minimum over each group of 8 lanes of values >= 0 or +inf (bit patterns ordered like the
+// floats): the two quad permutations, then the half-row mirror.
+__device__ inline unsigned oct_min_u(unsigned v) {
+  v = min(v, (unsigned)dppi<0xB1>((int)v));
+  v = min(v, (unsigned)dppi<0x4E>((int)v));
+  v = min(v, (unsigned)dppi<0x141>((int)v));
+  return v;
+}
+
+// 6 waves per SIMD (at most 80 registers).
+template <bool BF16>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_sweep_diag_win(
+    const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
+    const float* __restrict__ imp, uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
+    float* __restrict__ loss, const SweepOpts opt) {
+  __shared__ __attribute__((aligned(16))) float wt_all[kWaves][kRowsPerWave][16];   // w (+0 for -0)
+  __shared__ __attribute__((aligned(16))) float ut_all[kWaves][kRowsPerWave][16];   // w a
+  __shared__ __attribute__((aligned(16))) float sa_all[kWaves][16];                 // a = sqrt(Imp)
+  __shared__ float im_all[kWaves][16];
+  __shared__ float wr_all[kWaves][kRowsPerWave];      // W of the row (-1: not filtered)
+  __shared__ float lb_all[kWaves][kRowsPerWave];      // LB_lo: bound on the codes below the window
+  __shared__ float lh_all[kWaves][kRowsPerWave];      // LB_hi: bound on the codes above it
+  __shared__ int st_all[kWaves][kRowsPerWave];        // first code of the window (0: no window)
+  __shared__ int win_k[kWaves][kRowsPerWave];         // winner's code per row (0: no winner)
+  __shared__ unsigned long long ctd_all[kWaves][kRowsPerWave];   // 2..4 contenders: bit b = code start + b
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nb = cin / 16;
+  const int64_t n = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t g = blockIdx.z;
+  const int64_t c_begin = (int64_t)blockIdx.y * kRowsPerWave;
+  if (n >= nb || c_begin >= cout) return;
+  const int64_t c_end = min(cout, c_begin + kRowsPerWave);
+  const int nrows = (int)(c_end - c_begin);
+
+  // importance of the block column (all ones when it sums to zero or none is given: plain MSE),
+  // a_j = sqrt(Imp_j)
+  const float* ip = imp ? imp + g * cin + n * 16 : nullptr;
+  double isum = 0.0;
+  if (ip) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) isum += (double)ip[j];
+  }
+  if (lane < 16) {
+    const float v = isum == 0.0 ? 1.0f : ip[lane];
+    im_all[wave][lane] = v;
+    sa_all[wave][lane] = (float)sqrt((double)v);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const float gsc = uniform(global_scale(amax[g], opt.gdiv));
+  float amx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v4f t = *(const v4f*)&sa_all[wave][4 * q];
+    amx = fmaxf(amx, fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
+  }
+  const bool fast = filter_ok(gsc) && 448.0 * 64.0 * (double)gsc * (double)amx <= 0x1p120;
+  float (*wt)[16] = wt_all[wave];
+  float (*ut)[16] = ut_all[wave];
+
+  // The wave's 32 blocks come in with one coalesced load per lane (lane l: row l/2, elements
+  // 8*(l%2)..+7) and wait in LDS as w and w a, with the row's W, its window and its bound.
+  {
+    const int rr = lane >> 1, h = lane & 1;
+    const int64_t c = c_begin + rr;
+    const int64_t e0 = (g * cout + min(c, c_end - 1)) * cin + n * 16 + 8 * h;
+    float v[8];
+    if (BF16) {
+      const v4u u = *(const v4u*)((const unsigned short*)W + e0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(u[q] << 16) + 0.0f;           // + 0 turns -0 into +0
+        v[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u) + 0.0f;
+      }
+    } else {
+      const v4f u0 = *(const v4f*)((const float*)W + e0), u1 = *(const v4f*)((const float*)W + e0 + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v[q] = u0[q] + 0.0f; v[4 + q] = u1[q] + 0.0f; }
+    }
+    const v4f a0 = *(const v4f*)&sa_all[wave][8 * h], a1 = *(const v4f*)&sa_all[wave][8 * h + 4];
+    const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    float uv[8];
+    float wp = 0.0f, am = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uv[q] = v[q] * av[q];
+      wp = fmaf(uv[q], uv[q], wp);
+      am = fmaxf(am, fabsf(v[q]));
+    }
+    *(v4f*)&wt[rr][8 * h] = v4f{v[0], v[1], v[2], v[3]};
+    *(v4f*)&wt[rr][8 * h + 4] = v4f{v[4], v[5], v[6], v[7]};
+    *(v4f*)&ut[rr][8 * h] = v4f{uv[0], uv[1], uv[2], uv[3]};
+    *(v4f*)&ut[rr][8 * h + 4] = v4f{uv[4], uv[5], uv[6], uv[7]};
+    const float wrow = wp + __shfl_xor(wp, 1, 64);
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    // window: kmax one above the smallest code with 6 s >= amax (so that 6 s_kmax >= amax holds
+    // after the fp32 rounding of s_kmax), start 12 codes below it
+    const int kmax = min(126, e4m3_ceil_code((double)am / (6.0 * (double)gsc)) + 1);
+    const int start = min(max(kmax - 12, 1), 95);
+    // LB_lo and LB_hi in fp32, lowered by 2^-18 to bound the exact sums from below (each term
+    // has at most three roundings, the 16-term sum at most 16 more); |w| - 6 s and s_hi/2 - |w|
+    // take one rounding each (fma), so their signs are exact
+    const v4f m0 = *(const v4f*)&im_all[wave][8 * h], m1 = *(const v4f*)&im_all[wave][8 * h + 4];
+    const float mv[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+    const float sl = cand_scale(max(start - 1, 1), gsc), sh = cand_scale(min(start + 32, 126), gsc);
+    float lbp = 0.0f, lhp = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float aw = fabsf(v[q]);
+      const float d = fmaf(-6.0f, sl, aw);
+      if (d > 0.0f) lbp = fmaf(mv[q] * d, d, lbp);
+      const float dh = fminf(aw, fmaf(0.5f, sh, -aw));
+      if (dh > 0.0f) lhp = fmaf(mv[q] * dh, dh, lhp);
+    }
+    lbp += __shfl_xor(lbp, 1, 64);
+    lhp += __shfl_xor(lhp, 1, 64);
+    if (h == 0) {
+      const bool row_ok = fast && wrow >= 0x1p-100f && wrow <= 0x1p+100f && start >= 8;
+      wr_all[wave][rr] = row_ok ? wrow : -1.0f;
+      st_all[wave][rr] = row_ok ? start : 0;
+      lb_all[wave][rr] = start > 1 ? lbp * (1.0f - 0x1p-18f) : __builtin_inff();
+      lh_all[wave][rr] = start + 31 < 126 ? lhp * (1.0f - 0x1p-18f) : __builtin_inff();
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const int grp = lane >> 3, j = lane & 7;
+  for (int pass = 0; pass < (nrows + 7) / 8; ++pass) {
+    const int rr = 8 * pass + grp;
+    const bool row_on = rr < nrows;
+    const int rs = row_on ? rr : 0;
+    const int start = row_on ? st_all[wave][rs] : 0;
+    const float wrow = wr_all[wave][rs];
+    const bool scored = start > 0;                           // the row group's window
+    // the lane's codes start + j + 8 t; rows without a window score codes 95 + j + 8 t (valid
+    // codes, results unused)
+    const int k0 = (scored ? start : 95) + j;
+    const float s0 = cand_scale(k0, gsc), is0 = __builtin_amdgcn_rcpf(s0);   // within one ulp of 1/s
+    float L0 = 0.0f, L1 = 0.0f, L2 = 0.0f, L3 = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      // elements 2p, 2p+1 (w, w a and a read from LDS as needed): byte t of the pack register
+      // holds them for slot t (scale 2^t)
+      const v2f wv = *(const v2f*)&wt[rs][2 * p];
+      const v2f uv = *(const v2f*)&ut[rs][2 * p];
+      const v2f av = *(const v2f*)&sa_all[wave][2 * p];
+      const float x0 = wv[0] * is0, x1 = wv[1] * is0;
+      unsigned pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x0, x1, 1.0f, 0);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, x0, x1, 2.0f, 1);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, x0, x1, 4.0f, 2);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk, x0, x1, 8.0f, 3);
+      const v2f qa = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, 0);
+      const v2f qb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 2.0f, 1);
+      const v2f qc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 4.0f, 2);
+      const v2f qd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 8.0f, 3);
+      const float ta = s0 * av[0], tb = s0 * av[1], ua = -uv[0], ub = -uv[1];
+      const float ea0 = fmaf(qa[0], ta, ua), ea1 = fmaf(qa[1], tb, ub);
+      const float eb0 = fmaf(qb[0], ta, ua), eb1 = fmaf(qb[1], tb, ub);
+      const float ec0 = fmaf(qc[0], ta, ua), ec1 = fmaf(qc[1], tb, ub);
+      const float ed0 = fmaf(qd[0], ta, ua), ed1 = fmaf(qd[1], tb, ub);
+      L0 = fmaf(ea0, ea0, L0);
+      L0 = fmaf(ea1, ea1, L0);
+      L1 = fmaf(eb0, eb0, L1);
+      L1 = fmaf(eb1, eb1, L1);
+      L2 = fmaf(ec0, ec0, L2);
+      L2 = fmaf(ec1, ec1, L2);
+      L3 = fmaf(ed0, ed0, L3);
+      L3 = fmaf(ed1, ed1, L3);
+    }
+    // losses are >= 0 or +inf, ordered like their bit patterns
+    const float m = __uint_as_float(oct_min_u(min(min(__float_as_uint(L0), __float_as_uint(L1)),
+                                                  min(__float_as_uint(L2), __float_as_uint(L3)))));
+    // the row's line: lam ~ sqrt(W/m) within [1, 4096] (any lam > 0 gives a valid bound); the
+    // factors (1 + 2^-18) cover the roundings of alpha and beta, including the reciprocal of lam
+    // (within one ulp), (1 + 2^-16) those of W, of the reciprocal of 1 - alpha folded into A1
+    // and K2, and of the tests
+    const float wr = fmaxf(wrow, 0x1p-100f);
+    const float mm = m > wr * 0x1p-40f ? m : wr * 0x1p-40f;
+    const float lam = fminf(fmaxf(__builtin_amdgcn_rsqf(mm * __builtin_amdgcn_rcpf(wr)), 1.0f), 4096.0f);
+    const float alpha = fmaf(kDiagC2h, lam, kDiagC1) * (1.0f + 0x1p-18f);
+    const float bet = fmaf(kDiagC2h * (1.0f + 0x1p-18f), __builtin_amdgcn_rcpf(lam), kDiagC3);
+    const float ioma = __builtin_amdgcn_rcpf(1.0f - alpha);
+    const float A1 = (1.0f + alpha) * ioma * (1.0f + 0x1p-16f);
+    const float K2 = 2.0f * bet * ioma * (1.0f + 0x1p-16f);
+    // contenders: L' <= ((1 + alpha) m + 2 beta) / (1 - alpha); the exact window minimum is at
+    // most U = (1 + alpha) m + beta; codes below the window are out when LB_lo > U, codes above
+    // it when LB_hi >= U
+    const float rhs = fmaf(A1, m, K2 * wrow);
+    const float U = fmaf((1.0f + alpha) * (1.0f + 0x1p-16f), m, bet * (1.0f + 0x1p-16f) * wrow);
+    const bool lb_ok = lb_all[wave][rs] > U && lh_all[wave][rs] >= U;
+    const unsigned long long M0 = __ballot(scored && !(L0 > rhs)), M1 = __ballot(scored && !(L1 > rhs));
+    const unsigned long long M2 = __ballot(scored && !(L2 > rhs)), M3 = __ballot(scored && !(L3 > rhs));
+    // the row group's contenders: bit b of mk is code start + b (b = 8 t + j)
+    const int sh = 8 * grp;
+    const unsigned long long mk = ((M0 >> sh) & 0xFFull) | (((M1 >> sh) & 0xFFull) << 8) |
+                                  (((M2 >> sh) & 0xFFull) << 16) | (((M3 >> sh) & 0xFFull) << 24);
+    const int cnt = __popcll(mk);
+    const bool ok = scored && lb_ok;
+    const bool rescore = ok && cnt >= 2 && cnt <= 4;
+    if (j == 0 && row_on) {
+      if (!(ok && cnt >= 1 && cnt <= 4)) code[(g * cout + c_begin + rr) * nb + n] = 0;   // float64 pass
+      win_k[wave][rr] = ok && cnt == 1 ? start + (int)__builtin_ctzll(mk) : 0;
+      ctd_all[wave][rr] = rescore ? mk : 0ull;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // Rows with 2..4 contenders: exact float64 losses, one contender per 16 lanes (lane: element)
+  {
+    const unsigned long long todo0 = __ballot(lane < nrows && ctd_all[wave][lane < nrows ? lane : 0] != 0ull);
+    for (unsigned long long todo = todo0; todo; todo &= todo - 1) {
+      const int rq = (int)__builtin_ctzll(todo);
+      const int st = st_all[wave][rq];
+      unsigned long long mr = ctd_all[wave][rq];
+      int kc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kc[r] = mr ? st + (int)__builtin_ctzll(mr) : 0;       // ascending codes, 0 past the last
+        mr &= mr - 1;
+      }
+      const int rg = lane >> 4, el = lane & 15;              // contender rg, element el
+      const int myk = rg == 0 ? kc[0] : (rg == 1 ? kc[1] : (rg == 2 ? kc[2] : kc[3]));
+      int nib;
+      const double e = exact_err(wt[rq][el], cand_scale(myk > 0 ? myk : 1, gsc), &nib);
+      double z = (double)im_all[wave][el] * e * e;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+      double bestD = __builtin_inf();
+      int kwin = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double Lr = __shfl(z, 16 * r, 64);
+        if (kc[r] > 0 && (Lr < bestD || (Lr == bestD && kc[r] < kwin))) { bestD = Lr; kwin = kc[r]; }
+      }
+      if (lane == 0) win_k[wave][rq] = kwin;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // Exact nibbles and loss of every row's winner, eight rows at a time (as in k_sweep_diag).
+  const int sub = lane & 7, el0 = 2 * sub, el1 = el0 + 1;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int rr = 8 * pass + (lane >> 3);
+    const int64_t c = c_begin + rr;
+    const bool row_on = rr < nrows;
+    const int kw = row_on ? win_k[wave][rr] : 0;
+    const float sw = cand_scale(kw > 0 ? kw : 1, gsc);
+    const float wa = wt[rr][el0], wb = wt[rr][el1];
+    const float ima = im_all[wave][el0], imb = im_all[wave][el1];
+    const float is = __builtin_amdgcn_rcpf(sw);
+    const float isp = is * (1.0f + 0x1p-19f), ism = is * (1.0f - 0x1p-19f);
+    unsigned byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, wa * isp, wb * isp, 1.0f, 0);
+    const unsigned blo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, wa * ism, wb * ism, 1.0f, 0);
+    if (byte != blo) {
+      const int ca = e2m1_index_fma(fabsf(wa), sw), cb = e2m1_index_fma(fabsf(wb), sw);
+      byte = (unsigned)(ca | (wa < 0.0f ? 8 : 0)) | ((unsigned)(cb | (wb < 0.0f ? 8 : 0)) << 4);
+    }
+    const v2f qv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);   // signed grid values
+    const float ea = fmaf(qv[0], sw, -wa), eb = fmaf(qv[1], sw, -wb);
+    float part = fmaf(imb * eb, eb, ima * ea * ea);
+    part += __shfl_xor(part, 1, 64);
+    part += __shfl_xor(part, 2, 64);
+    part += __shfl_xor(part, 4, 64);
+    if (kw != 0) {
+      if (fp4) fp4[(g * cout + c) * (cin / 2) + n * 8 + sub] = (uint8_t)byte;
+      if (sub == 0) {
+        code[(g * cout + c) * nb + n] = (uint8_t)kw;
+        if (loss) loss[(g * cout + c) * nb + n] = part;
+      }
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
@@ -1662,8 +1982,11 @@ hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t
   dim3 block(kWaves * 64);
   const dim3 xgrid((unsigned)((cout + kWaves * kExactRows - 1) / (kWaves * kExactRows)),
                    (unsigned)((nb + 63) / 64), (unsigned)n_groups);
-#define LH_DIAG(B, M) \
-  hipLaunchKernelGGL((k_sweep_diag<B, M>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt)
+#define LH_DIAG(B, M)                                                                              \
+  if (M)                                                                                           \
+    hipLaunchKernelGGL((k_sweep_diag<B, true>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt); \
+  else                                                                                             \
+    hipLaunchKernelGGL((k_sweep_diag_win<B>), grid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt)
   if (bf16) {
     if (opt.nm > 0) LH_DIAG(true, true); else LH_DIAG(true, false);
     hipLaunchKernelGGL((k_sweep_diag_exact<true>), xgrid, block, 0, stream, W, cout, cin, amax, imp, code, fp4, loss, opt);

@@ -534,6 +534,33 @@ def test_sweep_diag_importance_and_weight_ranges():
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
 
+def test_sweep_diag_outside_the_window():
+    """Blocks the diagonal sweep's 32-code window cannot settle by its bounds: a dominant element
+    with almost no importance (the argmin lies far below the window, which starts 12 codes below
+    the block's amax code), blocks whose elements all lie within a factor 2 of each other (no
+    element is small enough for the bound on the codes above the window), and, for contrast,
+    ordinary blocks.  The first two kinds go to the float64 pass; every block must get the
+    oracle's argmin, nibbles and loss."""
+    r = np.random.default_rng(41)
+    G, cout, cin = 3, 48, 64
+    W = r.normal(0, 0.02, (G, cout, cin)).astype(np.float32)
+    imp = (np.abs(r.standard_normal((G, cin))) + 0.5).astype(np.float32)
+    W[0, :, ::16] = np.float32(0.5)                      # element 0 of every block dominates ...
+    imp[0, ::16] = np.float32(1e-9)                      # ... and hardly counts
+    W[0, 0, 1] = np.float32(8.0)                         # (the group's amax, well above 0.5)
+    W[1] = (np.sign(r.standard_normal((cout, cin))) * r.uniform(0.6, 1.0, (cout, cin)) * 0.02).astype(np.float32)
+    a = oracle.absmax(W.astype(np.float64)).astype(np.float32)
+    res = oracle.sweep_diag(W.astype(np.float64), a, imp)
+    # the first kind's argmin is below its window (from 12 codes under the amax code) by construction
+    g = oracle.global_scale(a)[0]
+    kmax = np.searchsorted(oracle.e4m3_ladder(), 0.5 / (6 * g)) + 2
+    assert (res["code"][0, 1:] < kmax - 12).mean() > 0.9
+    note(f"diag sweep outside the window G={G} cout={cout} cin={cin}")
+    code, fp4, loss = lh.lh_scale_sweep_diag(torch.from_numpy(W).to(DEV), torch.from_numpy(a).to(DEV),
+                                             torch.from_numpy(imp).to(DEV))
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
+
+
 @pytest.mark.parametrize("coupled", [False, True])
 def test_sweep_full_hessian_and_weight_ranges(coupled):
     """Hessians far from unit scale, where the fp32 filter's intermediate values would overflow or
