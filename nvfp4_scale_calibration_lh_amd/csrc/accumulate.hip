@@ -218,8 +218,8 @@ __device__ inline v4f sum_partials(const float* w0, int64_t stride, int64_t n, i
 // ---------------------------------------------------------------------------------------------
 // Waves per dense workgroup (measured on MI355X): 8 for bf16 H alone, so two workgroups share a
 // compute unit; 16 for bf16 H and P (both forms: X_q read or made in the kernel, which therefore
-// tile alike and sum in the same order) and for importance only; 4 for fp32.
-constexpr int dense_waves(bool bf16, bool imp_only, bool act) { return bf16 ? ((imp_only || act) ? 16 : 8) : 4; }
+// tile alike and sum in the same order); 4 for fp32.
+constexpr int dense_waves(bool bf16, bool act) { return bf16 ? (act ? 16 : 8) : 4; }
 
 template <bool BF16, bool ACT, bool DIAG, int NW, bool FQ>
 __global__ __launch_bounds__(NW * 64) void k_acc_dense(
@@ -294,45 +294,61 @@ __global__ __launch_bounds__(NW * 64) void k_acc_dense(
 // Dense layer, importance alone (no H): every lane squares and adds the channels it loads, in
 // fp32 registers (the square of a bf16 value is exact in fp32), with no staging and no matrix
 // instructions; the lanes that share channels, then the waves, then the tiles are added in a
-// fixed order.  Grid (tiles, slices) and partial layout [slice][tile][64 channels] as above.
+// fixed order.  A workgroup owns kCW channels of a tile of R rows: for bf16 that is 512 bytes
+// of every row, read by 32 lanes (two rows per load instruction), which HBM serves faster than
+// the 128-byte row pieces of the H kernels' 64-channel slices.  Grid (tiles, channel slices);
+// partial layout [slice][tile][kCW channels].
 // ---------------------------------------------------------------------------------------------
+template <bool BF16>
+struct ImpGeo {
+  static constexpr int kVals = BF16 ? 8 : 4;         // channels per lane (one 16-byte load per row)
+  static constexpr int kCW = BF16 ? 256 : 64;        // channels per workgroup
+  static constexpr int kLPR = kCW / kVals;           // lanes per row
+  static constexpr int kRPL = 64 / kLPR;             // rows per load instruction
+  static constexpr int kCR = BF16 ? 8 : 32;          // rows per chunk (bf16: 4 loads; 8 beat 4, 16, 32)
+  static constexpr int kLoads = kCR / kRPL;          // loads per lane per chunk
+};
+// waves per workgroup (measured on MI355X: 4 beat 8 and 16 on the dense bf16 shapes)
+constexpr int imp_waves(bool) { return 4; }
+
 template <bool BF16, int NW>
 __global__ __launch_bounds__(NW * 64) void k_imp_dense(const void* __restrict__ Xv, int64_t rows,
                                                         int64_t cin, int64_t R, float beta,
                                                         float* __restrict__ imp, float* __restrict__ ws,
                                                         unsigned* __restrict__ counters) {
-  using Gm = Geo<BF16>;
-  constexpr int kVals = BF16 ? 8 : 4;            // channels per lane (one 16-byte load per row)
-  __shared__ float comb[NW][kCh];
+  using Ig = ImpGeo<BF16>;
+  constexpr int kVals = Ig::kVals, kCW = Ig::kCW, kL = Ig::kLoads;
+  static_assert(kCW <= NW * 64, "one thread per channel of the slice for the final sums");
+  __shared__ float comb[NW][kCW];
   __shared__ int last_tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tiles = gridDim.x, tile = blockIdx.x, slice = blockIdx.y;
-  const int64_t ch0 = slice * kCh;
+  const int64_t ch0 = slice * kCW;
   const int64_t t0 = tile * R, t1 = min(rows, t0 + R);
-  const int lrow = BF16 ? (lane >> 3) : (lane >> 4);
-  const int lcol = BF16 ? (lane & 7) * 8 : (lane & 15) * 4;
+  const int lrow = lane / Ig::kLPR;
+  const int lcol = (lane % Ig::kLPR) * kVals;
   const bool col_on = ch0 + lcol < cin;
   const char* X = (const char*)Xv;
-  const int nchunks = t1 > t0 ? (int)((t1 - t0 + kChunk - 1) / kChunk) : 0;
+  const int nchunks = t1 > t0 ? (int)((t1 - t0 + Ig::kCR - 1) / Ig::kCR) : 0;
   float acc[kVals];
 #pragma unroll
   for (int e = 0; e < kVals; ++e) acc[e] = 0.0f;
   // Every lane issues the same loads on every path (rows past the range re-read its last row and
   // are not added; channels past cin read channel 0 and land in channels that are not written).
-  auto issue = [&](v4u (&p)[Gm::kLoads], int j) {
+  auto issue = [&](v4u (&p)[kL], int j) {
 #pragma unroll
-    for (int q = 0; q < Gm::kLoads; ++q) {
-      const int64_t r = min(t0 + (int64_t)j * kChunk + lrow + q * Gm::kRowsPerLoad, t1 - 1);
+    for (int q = 0; q < kL; ++q) {
+      const int64_t r = min(t0 + (int64_t)j * Ig::kCR + lrow + q * Ig::kRPL, t1 - 1);
       const int64_t byte = (r * cin + (col_on ? ch0 + lcol : 0)) * (BF16 ? 2 : 4);
       p[q] = __builtin_nontemporal_load((const v4u*)(X + byte));
     }
   };
-  auto add = [&](const v4u (&p)[Gm::kLoads], int j) {
-    const int64_t c0 = t0 + (int64_t)j * kChunk;
-    const bool full = c0 + kChunk <= t1;
+  auto add = [&](const v4u (&p)[kL], int j) {
+    const int64_t c0 = t0 + (int64_t)j * Ig::kCR;
+    const bool full = c0 + Ig::kCR <= t1;
 #pragma unroll
-    for (int q = 0; q < Gm::kLoads; ++q) {
-      const float f = (full || c0 + lrow + q * Gm::kRowsPerLoad < t1) ? 1.0f : 0.0f;
+    for (int q = 0; q < kL; ++q) {
+      const float f = (full || c0 + lrow + q * Ig::kRPL < t1) ? 1.0f : 0.0f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (BF16) {
@@ -354,11 +370,11 @@ __global__ __launch_bounds__(NW * 64) void k_imp_dense(const void* __restrict__ 
   // two register sets: a chunk's loads complete, the next chunk's are issued, then the chunk is
   // added while they are in flight (the empty asm takes the loaded registers, so the wait for
   // them comes before the next issue and never covers it)
-  auto ready = [](const v4u (&p)[Gm::kLoads]) {
+  auto ready = [](const v4u (&p)[kL]) {
 #pragma unroll
-    for (int q = 0; q < Gm::kLoads; ++q) asm volatile("" : : "v"(p[q]));
+    for (int q = 0; q < kL; ++q) asm volatile("" : : "v"(p[q]));
   };
-  v4u pa[Gm::kLoads], pb[Gm::kLoads];
+  v4u pa[kL], pb[kL];
   int j = wave;
   if (j < nchunks) issue(pa, j);
   while (j < nchunks) {
@@ -372,46 +388,46 @@ __global__ __launch_bounds__(NW * 64) void k_imp_dense(const void* __restrict__ 
     add(pb, j);
     j += NW;
   }
-  // lanes with the same channels: bf16 lanes l, l+8, .., l+56; fp32 lanes l, l+16, l+32, l+48
+  // lanes with the same channels: bf16 lanes l and l+32; fp32 lanes l, l+16, l+32, l+48
 #pragma unroll
-  for (int o = BF16 ? 8 : 16; o < 64; o <<= 1)
+  for (int o = Ig::kLPR; o < 64; o <<= 1)
 #pragma unroll
     for (int e = 0; e < kVals; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
   if (lrow == 0)
 #pragma unroll
     for (int e = 0; e < kVals; ++e) comb[wave][lcol + e] = acc[e];
   __syncthreads();
+  const bool owner = tid < kCW;                 // thread tid owns channel ch0 + tid
   float tot = 0.0f;
-  if (wave == 0)
+  if (owner)
 #pragma unroll
-    for (int v = 0; v < NW; ++v) tot += comb[v][lane];          // wave order
-  const int64_t ch = ch0 + lane;
+    for (int v = 0; v < NW; ++v) tot += comb[v][tid];           // wave order
+  const int64_t ch = ch0 + tid;
   if (tiles == 1) {
-    if (wave == 0 && ch < cin) imp[ch] = beta != 0.0f ? beta * imp[ch] + tot : tot;
+    if (owner && ch < cin) imp[ch] = beta != 0.0f ? beta * imp[ch] + tot : tot;
     return;
   }
   // several tiles: each stores its sums; the slice's last tile to finish adds all of them in
   // tile order and writes the outputs
-  float* part = ws + slice * tiles * kCh;
-  if (wave == 0) {
-    st_agent(part + tile * kCh + lane, tot);
-    __builtin_amdgcn_s_waitcnt(0);            // the partial stores have completed
-    if (lane == 0) last_tile = arrive(&counters[slice]) == (unsigned)(tiles - 1);
-  }
+  float* part = ws + slice * tiles * kCW;
+  if (owner) st_agent(part + tile * kCW + tid, tot);
+  __builtin_amdgcn_s_waitcnt(0);              // every wave's partial stores have completed
   __syncthreads();
-  if (!last_tile || wave != 0) return;
+  if (tid == 0) last_tile = arrive(&counters[slice]) == (unsigned)(tiles - 1);
+  __syncthreads();
+  if (!last_tile || !owner) return;
   float s = 0.0f;
   int64_t t = 0;
   for (; t + 8 <= tiles; t += 8) {
     float p[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) p[u] = ld_agent(part + (t + u) * kCh + lane);
+    for (int u = 0; u < 8; ++u) p[u] = ld_agent(part + (t + u) * kCW + tid);
 #pragma unroll
     for (int u = 0; u < 8; ++u) s += p[u];
   }
-  for (; t < tiles; ++t) s += ld_agent(part + t * kCh + lane);
+  for (; t < tiles; ++t) s += ld_agent(part + t * kCW + tid);
   if (ch < cin) imp[ch] = beta != 0.0f ? beta * imp[ch] + s : s;
-  if (lane == 0) clear(&counters[slice]);
+  if (tid == 0) clear(&counters[slice]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -574,16 +590,28 @@ __global__ __launch_bounds__(kThreads) void k_acc_pieces(
   if (lane == 0) clear(&counters[g * slices + slice]);
 }
 
-// Rows per tile of a dense layer: NW waves x 32 rows x c chunks per wave, with the largest c of
-// 1, 2, 4, 8 that still gives 256 workgroups, or 1024 when only the importance is produced
-// (small partials, several workgroups per compute unit).  Measured on MI355X for the dense
-// shapes.
-int64_t dense_tile_rows(int64_t rows, int64_t nb, bool bf16, bool imp_only, bool act) {
+// Rows per tile of a dense layer with H: NW waves x 32 rows x c chunks per wave, with the largest
+// c of 1, 2, 4, 8 that still gives 256 workgroups.  Measured on MI355X for the dense shapes.
+int64_t dense_tile_rows(int64_t rows, int64_t nb, bool bf16, bool act) {
   const int64_t slices = (nb + 3) / 4;
-  const int64_t base = dense_waves(bf16, imp_only, act) * kChunk;
-  const int64_t want = imp_only ? 1024 : 256;
+  const int64_t base = dense_waves(bf16, act) * kChunk;
   int64_t R = base;
-  while (R < 8 * base && ((rows + 2 * R - 1) / (2 * R)) * slices >= want) R *= 2;
+  while (R < 8 * base && ((rows + 2 * R - 1) / (2 * R)) * slices >= 256) R *= 2;
+  return R;
+}
+
+// Importance-only dense layer: channel slices of ImpGeo::kCW channels and tiles of R rows, R
+// doubling from one chunk per wave while at least 384 workgroups remain (measured on MI355X for
+// the dense shapes: fewer, longer tiles leave HBM idle at the ends, more add partial sums).
+int64_t imp_slices(int64_t cin, bool bf16) {
+  const int64_t cw = bf16 ? ImpGeo<true>::kCW : ImpGeo<false>::kCW;
+  return (cin + cw - 1) / cw;
+}
+int64_t imp_tile_rows(int64_t rows, int64_t cin, bool bf16) {
+  const int64_t slices = imp_slices(cin, bf16);
+  const int64_t base = imp_waves(bf16) * (int64_t)(bf16 ? ImpGeo<true>::kCR : ImpGeo<false>::kCR);
+  int64_t R = base;
+  while (R < 64 * base && ((rows + 2 * R - 1) / (2 * R)) * slices >= 384) R *= 2;
   return R;
 }
 
@@ -599,18 +627,22 @@ hipError_t launch_kind(bool dense, int64_t rows, int64_t cin, const int64_t* off
                        float* P, float* imp, void* work, unsigned* counters, hipStream_t stream) {
   const int64_t nb = cin / 16, slices = (nb + 3) / 4;
   if (dense) {
-    constexpr int NW = dense_waves(BF16, DIAG, ACT);
-    const int64_t R = dense_tile_rows(rows, nb, BF16, DIAG, ACT);
-    const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
     if constexpr (DIAG && !ACT) {
-      hipLaunchKernelGGL((k_imp_dense<BF16, NW>), dim3((unsigned)tiles, (unsigned)slices), dim3(NW * 64), 0,
-                         stream, X, rows, cin, R, beta, imp, (float*)work, counters);
+      constexpr int NW = imp_waves(BF16);
+      const int64_t R = imp_tile_rows(rows, cin, BF16);
+      const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
+      hipLaunchKernelGGL((k_imp_dense<BF16, NW>), dim3((unsigned)tiles, (unsigned)imp_slices(cin, BF16)),
+                         dim3(NW * 64), 0, stream, X, rows, cin, R, beta, imp, (float*)work, counters);
+      return hipGetLastError();
+    } else {
+      constexpr int NW = dense_waves(BF16, ACT);
+      const int64_t R = dense_tile_rows(rows, nb, BF16, ACT);
+      const int64_t tiles = max((int64_t)1, (rows + R - 1) / R);
+      hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG, NW, FQ>), dim3((unsigned)tiles, (unsigned)slices),
+                         dim3(NW * 64), 0, stream, X, Xq, x_amax, rows, cin, R, beta, H, P, imp,
+                         (float*)work, counters, nb);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_acc_dense<BF16, ACT, DIAG, NW, FQ>), dim3((unsigned)tiles, (unsigned)slices),
-                       dim3(NW * 64), 0, stream, X, Xq, x_amax, rows, cin, R, beta, H, P, imp,
-                       (float*)work, counters, nb);
-    return hipGetLastError();
   }
   const int64_t R = piece_rows(rows, nb);
   const int64_t cap = rows / R + G;           // >= sum over groups of max(1, ceil(T_g / R))
@@ -658,8 +690,13 @@ AccScratch accumulate_scratch(int64_t rows, int64_t nb, const int64_t* offsets, 
   const int64_t slices = (nb + 3) / 4;
   const size_t part = (size_t)(act_aware ? 2 : 1) * 4 * (imp_only ? 16 : 256) * sizeof(float);
   AccScratch s;
-  if (is_dense(offsets, n_groups)) {
-    const int64_t R = dense_tile_rows(rows, nb, bf16, imp_only, act_aware);
+  if (is_dense(offsets, n_groups) && imp_only && !act_aware) {
+    const int64_t cin = nb * 16, R = imp_tile_rows(rows, cin, bf16);
+    const int64_t tiles = (rows + R - 1) / R, cw = bf16 ? ImpGeo<true>::kCW : ImpGeo<false>::kCW;
+    s.work_bytes = (size_t)imp_slices(cin, bf16) * tiles * cw * sizeof(float);
+    s.counters = (size_t)slices;
+  } else if (is_dense(offsets, n_groups)) {
+    const int64_t R = dense_tile_rows(rows, nb, bf16, act_aware);
     const int64_t tiles = (rows + R - 1) / R;
     s.work_bytes = (size_t)slices * tiles * part;
     s.counters = (size_t)slices;
