@@ -18,6 +18,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short v2us __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 32;          // rows per chunk (one 16x16x32 MFMA per block)
@@ -62,6 +63,27 @@ __device__ inline float e4m3_nearest(double y) {
   return (float)fmin(ldexp(q, e - 3), 448.0);
 }
 
+// The same value from fp32 arithmetic: y = amax * fp32(1/(6 gX)) is within 2^-23 of itself of the
+// exact quotient (two roundings of 2^-24), i.e. within 2 units of y's last place in the E4M3 normal
+// range and 2^-20 of a grid step below 2^-6, so rounding y to the E4M3 grid decides as the exact
+// quotient would unless y lies within 8 units (normal range) or 2^-18 steps (below 2^-6) of a
+// midpoint; those blocks take the float64 path.  Normal range: round the fp32 significand to 3
+// bits, ties to even (the even code); below 2^-6 the grid is the multiples of 2^-9.  For gX in
+// [2^-100, 2^100], so that 1/(6 gX) is a normal fp32 value.
+__device__ inline float e4m3_nearest_f32(float amax, double inv6g) {
+  const float y = amax * (float)inv6g;
+  const unsigned b = __float_as_uint(y);
+  const unsigned low = b & 0xFFFFFu;                                // bits below the 3 kept
+  const float vn = __uint_as_float((b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u);
+  const float t = y * 512.0f;                                       // grid steps below 2^-6
+  const float vs = rintf(t) * 0x1p-9f;
+  const bool normal = y >= 0x1p-6f;
+  const bool near = normal ? low - 0x7FFF8u <= 16u : fabsf(t - floorf(t) - 0.5f) <= 0x1p-18f;
+  if (!(y < 448.0f)) return 448.0f;
+  if (near) return e4m3_nearest((double)amax * inv6g);
+  return normal ? vn : vs;
+}
+
 __device__ inline float e2m1_value(int c) {
   return c <= 4 ? 0.5f * (float)c : (c == 5 ? 3.0f : (c == 6 ? 4.0f : 6.0f));
 }
@@ -86,21 +108,27 @@ __device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool f
   constexpr int n = BF16 ? 8 : 4;
   float xf[n];
   unsigned am = 0;
+  if constexpr (BF16) {
+    // magnitudes as 15-bit integers order like the values: packed 16-bit maxima, then the halves
+    v2us m2 = {0, 0};
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    if (BF16) {
+    for (int p = 0; p < 4; ++p) {
       xf[2 * p] = __uint_as_float(x[p] << 16);
       xf[2 * p + 1] = __uint_as_float(x[p] & 0xFFFF0000u);
-      const unsigned a = x[p] & 0x7FFF7FFFu;
-      am = max(am, max(a << 16, a & 0xFFFF0000u));
-    } else {
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(v2us, x[p] & 0x7FFF7FFFu));
+    }
+    am = (unsigned)max(m2[0], m2[1]) << 16;
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
       xf[p] = __uint_as_float(x[p]);
       am = max(am, x[p] & 0x7FFFFFFFu);
     }
   }
   am = max(am, dpp_u<0xB1>(am));                  // quad_perm [1,0,3,2]: the lane pair
   if (!BF16) am = max(am, dpp_u<0x4E>(am));       // quad_perm [2,3,0,1]: the whole quad
-  const float v = gx > 0.0f ? e4m3_nearest((double)__uint_as_float(am) * inv6g) : 0.0f;
+  const float v = fast ? e4m3_nearest_f32(__uint_as_float(am), inv6g)
+                       : (gx > 0.0f ? e4m3_nearest((double)__uint_as_float(am) * inv6g) : 0.0f);
   const float s = v * gx;                         // fp32(v gX): one rounding of an exact product
   float q[n];
   if (fast) {
@@ -168,7 +196,8 @@ __device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool f
 // cin read channel 0; every lane issues the same loads on every path), stage_chunk() writes it to
 // the stage with those rows and channels zeroed,
 // finish_stage() makes the stage visible to the whole wave (with FQ it first makes X_q from the
-// staged X: X_q is not read, it is made in registers while later chunks' loads are in flight),
+// staged X, kept in registers: X_q is not read, it is made while the next chunk's loads are in
+// flight),
 // and contract() adds it to the accumulators.  The next chunk's loads are issued between
 // stage_chunk() and contract(), so one chunk is in flight while a chunk is contracted.
 template <bool BF16, bool ACT, bool FQ = false>
@@ -185,6 +214,7 @@ struct Streamer {
   double inv6g = 0.0;
   bool fq_fast = false;
   v4u pre[kM][Gm::kLoads];      // the chunk in flight
+  v4u xs[Gm::kLoads];           // FQ: the staged chunk's X, kept for the fake-quant
 
   __device__ void set_fake_quant(float x_amax) {
     gx = x_amax / 2688.0f;                       // fp32(amax / (6*448)), correctly rounded
@@ -225,17 +255,17 @@ struct Streamer {
 #pragma unroll
       for (int m = FQ ? 1 : 0; m < kM; ++m)
         *(v4u*)&stage[m * Gm::kWords + word(row, lcol())] = on ? pre[m][q] : v4u{0u, 0u, 0u, 0u};
+      if constexpr (FQ) xs[q] = on ? pre[1][q] : v4u{0u, 0u, 0u, 0u};
     }
   }
 
   __device__ void finish_stage() {
     if constexpr (FQ) {
-      // each lane reads back its own 16 bytes of X to make X_q (an X of zeros stays zero)
+      // each lane quantizes the 16 bytes of X it staged (an X of zeros stays zero)
 #pragma unroll
       for (int q = 0; q < Gm::kLoads; ++q) {
         const int w = word(lrow() + q * Gm::kRowsPerLoad, lcol());
-        const v4u xv = *(const v4u*)&stage[Gm::kWords + w];
-        *(v4u*)&stage[w] = act_fake_quant<BF16>(xv, gx, inv6g, fq_fast);   // every lane: uses its pair/quad
+        *(v4u*)&stage[w] = act_fake_quant<BF16>(xs[q], gx, inv6g, fq_fast);   // every lane: uses its pair/quad
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -245,6 +245,46 @@ def test_activation_fake_quant_entry_point(name):
 
 
 @pytest.mark.parametrize("bf16", [True, False])
+def test_activation_fake_quant_block_scale_ties(bf16):
+    """Block maxima placed exactly on every E4M3 midpoint of max|x| / (6 gX) (gX = 2^-8, so each
+    one is a short binary fraction, exact in bf16) and one bf16 step either side: the block scale
+    is the tie's even code or the nearer neighbour, as the oracle decides it, in the standalone
+    fake-quant and in the fused accumulation (equal to the two-input kernel fed the oracle's X_q)."""
+    gx = 2.0 ** -8
+    amax = np.float32(2688.0 * gx)                     # fp32(amax / 2688) = gX exactly
+    lad = oracle.e4m3_ladder()
+    mids = np.concatenate([[lad[0] / 2], (lad[:-1] + lad[1:]) / 2])   # 126 midpoints from 2^-10
+    peak = mids * 6.0 * gx
+    step = 2.0 ** (np.floor(np.log2(peak)) - 7)        # one bf16 unit at each peak
+    peaks = np.concatenate([peak, peak + step, peak - step])
+    rng = np.random.default_rng(58)
+    nblk = 4
+    rows = (len(peaks) + nblk - 1) // nblk
+    X = rng.uniform(-0.9, 0.9, size=(rows, nblk * 16))
+    pk = np.resize(peaks, rows * nblk).reshape(rows, nblk)
+    X *= np.repeat(pk, 16, axis=1)
+    X[:, ::16] = pk * np.where(rng.random((rows, nblk)) < 0.5, -1.0, 1.0)   # the block maximum
+    if bf16:
+        bits = synth.bf16_bits_from_f32(X.astype(np.float32))
+        X64 = synth.f32_from_bf16_bits(bits).astype(np.float64)
+        assert np.array_equal(np.abs(X64[:, ::16]), pk), "planted maxima are not exact bf16 values"
+        Xd = to_dev(bits, "bf16")
+    else:
+        X64 = X.astype(np.float32).astype(np.float64)
+        Xd = to_dev(X64.astype(np.float32), "f32")
+    note(f"activation fake-quant block-scale ties bf16={bf16} X[{rows},{nblk * 16}]")
+    off = np.array([0, rows], dtype=np.int64)
+    am = torch.tensor([amax], device=DEV)
+    Xq = lh.lh_activation_fake_quant(Xd, am)
+    ref = oracle.activation_fake_quant(X64, np.array([float(amax)]), off, bf16=bf16)
+    np.testing.assert_array_equal(Xq.float().cpu().numpy().astype(np.float64), ref)
+    H1, P1 = lh.lh_accumulate_act_aware_fq(Xd, am)
+    Xq_store = synth.bf16_bits_from_f32(ref.astype(np.float32)) if bf16 else ref.astype(np.float32)
+    H2, P2 = lh.lh_accumulate_act_aware(Xd, to_dev(Xq_store, "bf16" if bf16 else "f32"))
+    assert torch.equal(H1, H2) and torch.equal(P1, P2)
+
+
+@pytest.mark.parametrize("bf16", [True, False])
 def test_accumulate_act_aware_unrelated_xq(bf16):
     """X_q far from X: a 9-12 binade gap (D with more than 16 significant bits), blocks where
     X_q or X is zero, and X_q larger than X.  H and P within the 1e-5 Cauchy-Schwarz tolerance."""
