@@ -368,7 +368,7 @@ def main():
     roof = {"bound": "alu", "achieved": sweep_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": sweep_tflops / FP32_PEAK_TFLOPS, "traffic": measured_traffic(rec, "k_sweep"),
             "kernel": "sweep", "flops_per_block": flops_blk, "blocks_per_launch": blocks,
-            "avg_launch_ms": ms_sw, "counters": sq_shares(rec, "k_sweep_diag" if wl.mode == "diag" else "k_sweep_full<")}
+            "avg_launch_ms": ms_sw, "counters": sq_shares(rec, "k_sweep_diag_win" if wl.mode == "diag" else "k_sweep_full<")}
 
     out = {
         "metric": METRIC,

@@ -173,6 +173,12 @@ DeviceScratch& device_scratch(int dev) {
   static DeviceScratch table[64];
   return table[dev];
 }
+// The full-Hessian sweep's own scratch (one float per block column: the Hessian's eigenvalue
+// bound), handed on in stream order like the accumulation's.
+DeviceScratch& sweep_scratch(int dev) {
+  static DeviceScratch table[64];
+  return table[dev];
+}
 
 // Grows a buffer in stream order (the old one is freed on `s` after the waits already queued).
 hipError_t grow(void** buf, size_t* have, size_t need, size_t elem, hipMemPool_t pool, hipStream_t s,
@@ -413,9 +419,32 @@ lh_status lh_scale_sweep_ex(const void* W, lh_dtype w_dtype, int64_t n_groups, i
   if (fp4 && (reinterpret_cast<uintptr_t>(fp4) % 2) != 0) return fail(LH_ERR_INVALID_ARGUMENT, "fp4 must be 2-byte aligned");
   DeviceGuard guard;
   if ((st = guard.enter(dev)) != LH_OK) return st;
-  hipError_t e = lh::launch_sweep(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, H, P,
-                                  scale_code, fp4, best_loss, opts, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (cout == 0) return ok();
+  // scratch: one float per block column (the sweep's per-column eigenvalue bound)
+  hipMemPool_t pool;
+  hipError_t e = scratch_pool(dev, &pool);
+  if (e != hipSuccess) return hip_fail(e, "scratch pool");
+  DeviceScratch& sc = sweep_scratch(dev);
+  std::lock_guard<std::mutex> lk(sc.mu);
+  if (!sc.ready) {
+    e = hipEventCreateWithFlags(&sc.ready, hipEventDisableTiming | hipEventDisableSystemFence);
+    if (e != hipSuccess) { sc.ready = nullptr; return hip_fail(e, "hipEventCreateWithFlags"); }
+  } else {
+    e = hipStreamWaitEvent(s, sc.ready, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  e = grow(&sc.work, &sc.work_bytes, std::max<size_t>((size_t)n_groups * (size_t)(cin / 16) * sizeof(float), 16), 1, pool,
+           s, false);
+  if (e != hipSuccess) {
+    (void)hipEventRecord(sc.ready, s);
+    return hip_fail(e, "sweep scratch");
+  }
+  e = lh::launch_sweep(W, w_dtype == LH_DTYPE_BF16, n_groups, cout, cin, global_amax, H, P, scale_code, fp4,
+                       best_loss, opts, static_cast<float*>(sc.work), s);
+  hipError_t e2 = hipEventRecord(sc.ready, s);
   if (e != hipSuccess) return hip_fail(e, "sweep launch");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipEventRecord");
   return ok();
 }
 

@@ -48,9 +48,11 @@ struct SweepOpts {
   float mult[kMaxMultipliers];
 };
 
+// mu: device scratch of n_groups * cin/16 floats (each block column's Hessian eigenvalue bound,
+// written and read by the launch).
 hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout, int64_t cin,
                         const float* amax, const float* H, const float* P, uint8_t* code,
-                        uint8_t* fp4, float* loss, const SweepOpts& opts, hipStream_t stream);
+                        uint8_t* fp4, float* loss, const SweepOpts& opts, float* mu, hipStream_t stream);
 
 hipError_t launch_sweep_diag(const void* W, bool bf16, int64_t n_groups, int64_t cout,
                              int64_t cin, const float* amax, const float* imp, uint8_t* code,

@@ -387,6 +387,87 @@ __device__ inline float wave_max_nonneg(float x) {
   return __uint_as_float((unsigned)__builtin_amdgcn_readfirstlane((int)v));
 }
 
+// Lane group gg's Cholesky test of A = S - m I (S in registers, lane i holding row i; the column
+// being eliminated passes through the 16 floats of LDS at cbuf + 16 gg): true when every pivot is
+// positive.
+__device__ inline bool chol_positive(const float (&srow)[16], float m, int i, int gg, float* cbuf) {
+  float a[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a[k] = k == i ? srow[k] - m : srow[k];
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    cbuf[16 * gg + i] = a[j];                        // column j of the reduced matrix
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float piv = cbuf[16 * gg + j];
+    ok = ok && piv > 0.0f;
+    const float isr = __builtin_amdgcn_rsqf(fmaxf(piv, 0x1p-100f));
+    const float li = a[j] * isr;
+#pragma unroll
+    for (int k = j + 1; k < 16; ++k) a[k] = fmaf(-li, cbuf[16 * gg + k] * isr, a[k]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  return ok;
+}
+
+// A lower bound mu >= 0 of the smallest eigenvalue of S = (H + H^T)/2 for a column's Hessian H
+// (16x16 row-major in LDS), the same value in every lane: every e then has e^T H e = e^T S e >=
+// mu |e|^2.  S is scaled by a power of two to max |S_ij| in [1/2, 1).  If a float32 Cholesky
+// factorization of S - m I completes with positive pivots, R^T R = S - m I + E with
+// |E_ij| <= gamma_17 (|R^T||R|)_ij (the standard backward error of Cholesky, here with unit
+// roundoff 2^-22 for the reciprocal square root and product), and (|R^T||R|)_ij <=
+// sqrt((R^T R)_ii (R^T R)_jj) <= 1.01, so the 2-norm of E is below 16 * 17 * 2^-22 * 1.01 <
+// 2^-13.8; with the roundings of S's entries (2^-20 in norm) the smallest eigenvalue of S is at
+// least m - 2^-13.7.  The four lane groups test four values of m at a time, below d, the smallest
+// diagonal entry (which bounds the smallest eigenvalue from above): d 2^-2, 2^-6, 2^-10, 2^-14,
+// then the three doublings of the largest that passed.  mu is the largest m that passed less
+// 2^-12 (else 0), scaled back.  A column of zero trace is scored as H = I: mu = 1.  Non-finite
+// H gives 0.
+__device__ inline float column_mu(const float* Hs, bool dead, int lane, float* cbuf) {
+  if (dead) return 1.0f;
+  const int i = lane & 15, gg = lane >> 4;
+  float a[16];
+  float mx = 0.0f;
+  bool fin = true;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    a[k] = 0.5f * Hs[i * 16 + k] + 0.5f * Hs[k * 16 + i];
+    fin = fin && fabsf(a[k]) <= 0x1.fffffep127f;     // false for inf and NaN
+    mx = fmaxf(mx, fabsf(a[k]));
+  }
+  if (__ballot(!fin)) return 0.0f;
+  mx = wave_max_nonneg(mx);
+  if (!(mx > 0.0f)) return 0.0f;
+  const int ex = __builtin_amdgcn_frexp_expf(mx);   // mx = f 2^ex, f in [1/2, 1)
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a[k] = __builtin_amdgcn_ldexpf(a[k], -ex);
+  float di = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) di = k == i ? a[k] : di;
+  const float d = wave_min_ordered(di);
+  if (!(d > 0.0f)) return 0.0f;
+  // round 1: m = d 2^-(4 gg + 2)
+  unsigned long long okm = __ballot(chol_positive(a, __builtin_amdgcn_ldexpf(d, -(4 * gg + 2)), i, gg, cbuf));
+  int e1 = 0;                                        // exponent of the largest m that passed
+#pragma unroll
+  for (int q = 3; q >= 0; --q)
+    if ((okm >> (16 * q)) & 1ull) e1 = -(4 * q + 2);
+  if (e1 == 0) return 0.0f;
+  // round 2: m = d 2^(e1 + 1 + gg) for gg < 3 (group 3 repeats the passed value)
+  const int e2 = gg < 3 ? e1 + 1 + gg : e1;
+  okm = __ballot(e2 <= -1 && chol_positive(a, __builtin_amdgcn_ldexpf(d, e2), i, gg, cbuf));
+  int eb = e1;
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+    if ((okm >> (16 * q)) & 1ull) eb = e1 + 1 + q;
+  const float mu = __builtin_amdgcn_ldexpf(d, eb) - 0x1p-12f;
+  return mu > 0.0f ? __builtin_amdgcn_ldexpf(mu, ex) : 0.0f;
+}
+
 // Float64 re-scoring of one block by a whole wave: lane l scores codes l + 1 and l + 65 (those
 // with al0 / al1 set) with exact quantization, and the winner's code, nibbles and loss are written
 // to code_p, fp4_p (the block's 8 bytes, or NULL) and loss_p (or NULL).  Hs, Ps (16x16 row-major)
@@ -461,7 +542,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
                                          int64_t g, int64_t n, int64_t c_begin, int64_t c_end, float gsc,
                                          uint8_t* __restrict__ code, uint8_t* __restrict__ fp4,
                                          float* __restrict__ loss, int rows_per_wave, const SweepOpts& opt,
-                                         unsigned* undec_bits = nullptr) {
+                                         const float* mu_col, unsigned* undec_bits = nullptr) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, gg = lane >> 4;
   const int64_t nb = cin / 16;
@@ -534,6 +615,16 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
   const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)mid1 * (double)gsc)) : 0.0f;
   const float sl0 = gg == 0 ? s0 : s1;             // scale of tile gg (first half of the tiles)
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  // Codes 65..126 are scored first; codes 1..64 only when this bound does not rule them out: for
+  // k <= 64 every element keeps an error |e_i| >= |w_i| - 6 s_k >= |w_i| - 6 s_64 whatever its
+  // FP4 value (at most 6), so with mu <= the smallest eigenvalue of the column's (symmetrized)
+  // Hessian, L_k >= mu sum_i (|w_i| - 6 s_64)_+^2 =: LB (and L_k >= c (mu c - 2|b|) with
+  // c^2 = that sum, b = P w, when mu c >= |b|, in the coupled form).  LB > U (the lowest upper end
+  // among codes 65..126, at least their exact minimum) means no code <= 64 is or ties the argmin.
+  // The multiplier search scores all codes.
+  constexpr bool kWindow = !MSEARCH;
+  const float mu = !(kWindow && fast) ? 0.0f : (mu_col ? *mu_col : column_mu(L.H, dead, lane, &L.g[0][0]));
+  const float s64 = cand_scale(64, gsc);
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
     // ---- 16-row tile: w, H w, P w and |P||w| (fp32 MFMA, K index = element 4*gg + t)
@@ -627,6 +718,31 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
           if (k != 0) tile_hit |= 1u << ((k - 1) >> 4);
         }
       }
+      float lb_row = -__builtin_inff();            // LB of codes 1..64 (see the column set-up)
+      if (kWindow && mu > 0.0f) {
+        float c2p = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float dl = fmaxf(fmaf(-6.0f, s64, fabsf(w[t])), 0.0f);   // one rounding of |w| - 6 s_64
+          c2p = fmaf(dl, dl, c2p);
+        }
+        const float c2 = group_sum(c2p) * (1.0f - 0x1p-18f);   // rounded down (7 roundings < 2^-21)
+        if (coupled) {
+          // |b_i| <= |fp32 (P w)_i| + 2^-20 (|P||w|)_i, and om_i >= 2 (|P||w|)_i
+          float bp = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float bb = fmaf(0x1p-19f, om[t], fabsf(L.b[rr][4 * gg + t]));
+            bp = fmaf(bb, bb, bp);
+          }
+          const float bn = sqrtf(group_sum(bp)) * (1.0f + 0x1p-17f);     // >= |b|
+          const float cd = sqrtf(c2) * (1.0f - 0x1p-20f);                  // <= c
+          const float tm = fmaf(mu, cd, -2.0f * bn);
+          if (mu * cd >= bn * (1.0f + 0x1p-20f) && tm > 0.0f) lb_row = cd * tm * (1.0f - 0x1p-20f);
+        } else {
+          lb_row = mu * c2 * (1.0f - 0x1p-22f);
+        }
+      }
       float ra[4], rb[4];                            // w / s for this lane's tile-0 and tile-1 codes
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -647,8 +763,9 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
       // (H e + 2b)_i = s y_i and L = s sum_i e_i y_i, with s applied once after the sum over the
       // lane groups.  Instantiated twice so the common case has no override code.
       unsigned pkc = 0u;
-      auto score = [&](auto ovr_tag, float Lq[2], float Aq[2]) {
+      auto score_quad = [&](auto ovr_tag, auto quad_tag, float& Lo, float& Ao) {
         constexpr bool OVR = decltype(ovr_tag)::value;
+        constexpr int q = decltype(quad_tag)::value;
         auto tile_err = [&](int tau, float e[4], unsigned& p01, unsigned& p23) {
           const float sc = tau == 0 ? 1.0f : (float)(1u << (2 * (tau - 1)));   // 4^(tau-1)
           const float* r = tau == 0 ? ra : rb;
@@ -674,9 +791,8 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
         };
         float e[4], en[4];
         unsigned p01, p23, pn01 = 0, pn23 = 0;
-        tile_err(0, e, p01, p23);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        tile_err(4 * q, e, p01, p23);
+        {
           float pl[4], pa4[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -685,7 +801,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
             const v4s B = __builtin_bit_cast(v4s, Bu);
             const v4f y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                 A1, B, __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A2, B, tau == 0 ? cacc0 : cacc1, 0, 0, 0), 0, 0, 0);
-            if (tau < 7) tile_err(tau + 1, en, pn01, pn23);         // overlaps the MFMAs
+            if (u < 3) tile_err(tau + 1, en, pn01, pn23);           // overlaps the MFMAs
             // bound: uncoupled, this lane's part of S_e = sum_i d_i |e_i| (A follows after the
             // group sum); coupled, (2 S_e,g)^2 + sum_i |e_i| om_i over the lane's 4 elements,
             // whose sum over the 4 groups is >= S_e^2 + S_e S_w + 2|e|^T(|P||w|) (Cauchy-Schwarz)
@@ -707,24 +823,38 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
             lp = fmaf(e[3], y[3], lp);
             pl[u] = lp;
             pa4[u] = ap;
-            if (tau < 7) {
+            if (u < 3) {
 #pragma unroll
               for (int t = 0; t < 4; ++t) e[t] = en[t];
               p01 = pn01;
               p23 = pn23;
             }
           }
-          Lq[q] = quad_sum(pl) * (q == 0 ? sl0 : s1);   // lane group gg holds tile 4q + gg
-          Aq[q] = quad_sum(pa4);
-          if (!COUPLED) Aq[q] *= fmaf(4.0f, Aq[q], S_w);   // A = S_e (4 S_e + S_w)
+          Lo = quad_sum(pl) * (q == 0 ? sl0 : s1);      // lane group gg holds tile 4q + gg
+          Ao = quad_sum(pa4);
+          if (!COUPLED) Ao *= fmaf(4.0f, Ao, S_w);       // A = S_e (4 S_e + S_w)
         }
       };
+      auto score = [&](auto quad_tag, float& Lo, float& Ao) {
+        if (has_ovr) score_quad(std::true_type{}, quad_tag, Lo, Ao);
+        else score_quad(std::false_type{}, quad_tag, Lo, Ao);
+      };
+      // lane l holds codes l + 1 (tiles 0..3) and l + 65 (tiles 4..7); 127 and 128 do not exist
       float Lq[2], Aq[2];
-      if (has_ovr) score(std::true_type{}, Lq, Aq);
-      else score(std::false_type{}, Lq, Aq);
-
-      // lane l now holds codes l + 1 (tiles 0..3) and l + 65 (tiles 4..7); 127 and 128 do not exist
+      score(std::integral_constant<int, 1>{}, Lq[1], Aq[1]);
       if (lane >= 62) Lq[1] = __builtin_inff();
+      float U1 = 0.0f;
+      bool win = false;
+      if (kWindow) {
+        U1 = wave_min_ordered(fmaf(kErrC, Aq[1], Lq[1]));
+        win = lb_row > U1;
+      }
+      if (win) {
+        Lq[0] = __builtin_inff();
+        Aq[0] = 0.0f;
+      } else {
+        score(std::integral_constant<int, 0>{}, Lq[0], Aq[0]);
+      }
       if (msearch) {                                 // candidates no multiplier proposes drop out
         bool al0, al1;
         mark_allowed(L.ab[rr], g6, ig6, mu0, mu1, (int)(c - c_begin), L.mk, lane + 1, lane + 65, al0, al1);
@@ -735,7 +865,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
       // is >= the exact minimum, so the exact argmin is one of the candidates whose lower end is
       // <= U; when there is only one, it is the argmin.
       const float u0 = fmaf(kErrC, Aq[0], Lq[0]), u1 = fmaf(kErrC, Aq[1], Lq[1]);
-      const float U = wave_min_ordered(u1 < u0 ? u1 : u0);
+      const float U = win ? U1 : wave_min_ordered(u1 < u0 ? u1 : u0);
       const unsigned long long M0 = __ballot(fmaf(-kErrC, Aq[0], Lq[0]) <= U);
       const unsigned long long M1 = __ballot(fmaf(-kErrC, Aq[1], Lq[1]) <= U);
       // |L_k| <= A_k, so |U| >= 2^-100 keeps every bound that matters far above the absolute
@@ -885,13 +1015,14 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
 }
 
 // 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
-// more and drop to 3 waves, which costs about 10%).  rows_per_wave: 32, or 64 when one round holds
-// them all.
+// more and drop to 3 waves, which costs about 10%).  rows_per_wave: 32, 64 when one round holds
+// them all, 128 for launches of more than 64 rounds.
 template <bool BF16, bool COUPLED, bool EQUALIZE, bool MSEARCH>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
     const float* __restrict__ Hg, const float* __restrict__ Pg, uint8_t* __restrict__ code,
-    uint8_t* __restrict__ fp4, float* __restrict__ loss, int rows_per_wave, const SweepOpts opt) {
+    uint8_t* __restrict__ fp4, float* __restrict__ loss, int rows_per_wave, const SweepOpts opt,
+    const float* __restrict__ mu) {
   __shared__ FullLds lds_all[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   FullLds& L = lds_all[wave];
@@ -910,7 +1041,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   }
   sweep_full_column<BF16, COUPLED, EQUALIZE, false, MSEARCH>(L, W, cout, cin, g, n, c_begin, c_end,
                                                     global_scale(amax[g], opt.gdiv), code, fp4, loss,
-                                                    rows_per_wave, opt);
+                                                    rows_per_wave, opt, mu + g * nb + n);
+}
+
+// Each block column's eigenvalue bound (column_mu) once, for all the waves that sweep its rows: a
+// wave per column, H_n through LDS.
+__global__ __launch_bounds__(kWaves * 64) void k_column_mu(const float* __restrict__ Hg, int64_t ncols,
+                                                           float* __restrict__ mu) {
+  __shared__ float hs[kWaves][256];
+  __shared__ float cb[kWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * kWaves + wave;
+  if (col >= ncols) return;                        // whole wave leaves; no workgroup barriers below
+  const float* Hn = Hg + col * 256;
+  for (int q = 0; q < 4; ++q) hs[wave][lane * 4 + q] = Hn[lane * 4 + q];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  double tr = 0.0;                                 // zero trace: scored as H = I (as the sweep)
+  for (int j = 0; j < 16; ++j) tr += (double)hs[wave][j * 17];
+  const float m = column_mu(hs[wave], tr == 0.0, lane, cb[wave]);
+  if (lane == 0) mu[col] = m;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -989,7 +1139,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))
   // float64 (so the filter's registers are not live during the float64 pass, nor the reverse)
   for (int q = lane; q < kFusedMaxCout / 32; q += 64) ub[q] = 0u;
   sweep_full_column<BF16, false, false, true, MSEARCH>(L, W, cout, cin, g, n, 0, cout, gsc, code, fp4, loss,
-                                                       (int)cout, opt, ub);
+                                                       (int)cout, opt, nullptr, ub);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1913,15 +2063,23 @@ __global__ __launch_bounds__(kWaves * 64) void k_sweep_diag_exact(
 
 hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout, int64_t cin,
                         const float* amax, const float* H, const float* P, uint8_t* code,
-                        uint8_t* fp4, float* loss, const SweepOpts& opt, hipStream_t stream) {
+                        uint8_t* fp4, float* loss, const SweepOpts& opt, float* mu, hipStream_t stream) {
   const int64_t nb = cin / 16;
   if (cout == 0) return hipSuccess;
+  if (opt.nm == 0) {                               // the multiplier search scores every code
+    const int64_t ncols = n_groups * nb;
+    hipLaunchKernelGGL(k_column_mu, dim3((unsigned)((ncols + kWaves - 1) / kWaves)), dim3(kWaves * 64), 0, stream,
+                       H, ncols, mu);
+  }
   // a launch of at most four rounds of resident waves (4096 at a time) ends in a tail that the
   // progress-based priority shortens; longer launches keep the arbiter's own order, which mixes
-  // phases better.  A launch of at most two rounds takes 64 rows per wave and runs as one.
+  // phases better.  A launch of at most two rounds takes 64 rows per wave and runs as one; one of
+  // more than 64 rounds takes 128 rows per wave, so each wave's column set-up (the Hessian's
+  // eigenvalue bound above all) serves more rows (512-expert gate_up: 51.6 -> 46.2 ms).
   const int64_t waves32 = (nb + kWaves - 1) / kWaves * kWaves * ((cout + kRowsPerWave - 1) / kRowsPerWave) * n_groups;
   const bool equalize = waves32 <= 16384;
-  const int rpw = (waves32 <= 8192 && cout > kRowsPerWave) ? 2 * kRowsPerWave : kRowsPerWave;
+  const int rpw = waves32 > 262144 ? 4 * kRowsPerWave
+                                   : ((waves32 <= 8192 && cout > kRowsPerWave) ? 2 * kRowsPerWave : kRowsPerWave);
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + rpw - 1) / rpw), (unsigned)n_groups);
   dim3 block(kWaves * 64);
   // float64 pass: a wave per (kExactRows rows, 64 block columns)
@@ -1930,13 +2088,13 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
 #define LH_SWEEP_PAIR(B, C)                                                                        \
   if (opt.nm > 0)                                                                                  \
     hipLaunchKernelGGL((k_sweep_full<B, C, false, true>), grid, block, 0, stream, W, cout, cin, amax, \
-                       H, P, code, fp4, loss, rpw, opt);                                           \
+                       H, P, code, fp4, loss, rpw, opt, mu);                                       \
   else if (equalize)                                                                               \
     hipLaunchKernelGGL((k_sweep_full<B, C, true, false>), grid, block, 0, stream, W, cout, cin, amax, \
-                       H, P, code, fp4, loss, rpw, opt);                                           \
+                       H, P, code, fp4, loss, rpw, opt, mu);                                       \
   else                                                                                             \
     hipLaunchKernelGGL((k_sweep_full<B, C, false, false>), grid, block, 0, stream, W, cout, cin, amax, \
-                       H, P, code, fp4, loss, rpw, opt);                                           \
+                       H, P, code, fp4, loss, rpw, opt, mu);                                       \
   hipLaunchKernelGGL((k_sweep_full_exact<B, C>), xgrid, block, 0, stream, W, cout, cin, amax, H, P, \
                      code, fp4, loss, opt)
   if (bf16 && P) {
