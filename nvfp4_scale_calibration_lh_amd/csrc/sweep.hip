@@ -615,16 +615,17 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
   const float img1 = (fast && p1 < 112) ? (float)(1.0 / ((double)mid1 * (double)gsc)) : 0.0f;
   const float sl0 = gg == 0 ? s0 : s1;             // scale of tile gg (first half of the tiles)
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  // Codes 65..126 are scored first; codes 1..64 only when this bound does not rule them out: for
-  // k <= 64 every element keeps an error |e_i| >= |w_i| - 6 s_k >= |w_i| - 6 s_64 whatever its
-  // FP4 value (at most 6), so with mu <= the smallest eigenvalue of the column's (symmetrized)
-  // Hessian, L_k >= mu sum_i (|w_i| - 6 s_64)_+^2 =: LB (and L_k >= c (mu c - 2|b|) with
-  // c^2 = that sum, b = P w, when mu c >= |b|, in the coupled form).  LB > U (the lowest upper end
-  // among codes 65..126, at least their exact minimum) means no code <= 64 is or ties the argmin.
-  // The multiplier search scores all codes.
+  // Codes 97..126 (tiles 6, 7) are scored first, codes 65..96 (tiles 4, 5) only when the bound
+  // below does not rule them out for K = 96, and codes 1..64 only when it does not for K = 64 once
+  // codes 65..96 are scored: for k <= K every element keeps an error |e_i| >= |w_i| - 6 s_k >=
+  // |w_i| - 6 s_K whatever its FP4 value (at most 6), so with mu <= the smallest eigenvalue of the
+  // column's (symmetrized) Hessian, L_k >= mu sum_i (|w_i| - 6 s_K)_+^2 =: LB_K (and
+  // L_k >= c (mu c - 2|b|) with c^2 = that sum, b = P w, when mu c >= |b|, in the coupled form).
+  // LB_K > U (the lowest upper end among the codes scored, at least their exact minimum) means no
+  // code <= K is or ties the argmin.  The multiplier search scores all codes.
   constexpr bool kWindow = !MSEARCH;
   const float mu = !(kWindow && fast) ? 0.0f : (mu_col ? *mu_col : column_mu(L.H, dead, lane, &L.g[0][0]));
-  const float s64 = cand_scale(64, gsc);
+  const float s64 = cand_scale(64, gsc), s96 = cand_scale(96, gsc);
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
     // ---- 16-row tile: w, H w, P w and |P||w| (fp32 MFMA, K index = element 4*gg + t)
@@ -718,12 +719,13 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
           if (k != 0) tile_hit |= 1u << ((k - 1) >> 4);
         }
       }
-      float lb_row = -__builtin_inff();            // LB of codes 1..64 (see the column set-up)
-      if (kWindow && mu > 0.0f) {
+      // LB_K of codes 1..K (see the column set-up), -inf without a bound; sK = s_K
+      auto lower_bound = [&](float sK) -> float {
+        if (!(kWindow && mu > 0.0f)) return -__builtin_inff();
         float c2p = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float dl = fmaxf(fmaf(-6.0f, s64, fabsf(w[t])), 0.0f);   // one rounding of |w| - 6 s_64
+          const float dl = fmaxf(fmaf(-6.0f, sK, fabsf(w[t])), 0.0f);    // one rounding of |w| - 6 s_K
           c2p = fmaf(dl, dl, c2p);
         }
         const float c2 = group_sum(c2p) * (1.0f - 0x1p-18f);   // rounded down (7 roundings < 2^-21)
@@ -738,11 +740,11 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
           const float bn = sqrtf(group_sum(bp)) * (1.0f + 0x1p-17f);     // >= |b|
           const float cd = sqrtf(c2) * (1.0f - 0x1p-20f);                  // <= c
           const float tm = fmaf(mu, cd, -2.0f * bn);
-          if (mu * cd >= bn * (1.0f + 0x1p-20f) && tm > 0.0f) lb_row = cd * tm * (1.0f - 0x1p-20f);
-        } else {
-          lb_row = mu * c2 * (1.0f - 0x1p-22f);
+          return (mu * cd >= bn * (1.0f + 0x1p-20f) && tm > 0.0f) ? cd * tm * (1.0f - 0x1p-20f)
+                                                                   : -__builtin_inff();
         }
-      }
+        return mu * c2 * (1.0f - 0x1p-22f);
+      };
       float ra[4], rb[4];                            // w / s for this lane's tile-0 and tile-1 codes
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -762,10 +764,15 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
       // MFMA (H in two pieces, products exact, fp32 accumulation onto the accumulator input), so
       // (H e + 2b)_i = s y_i and L = s sum_i e_i y_i, with s applied once after the sum over the
       // lane groups.  Instantiated twice so the common case has no override code.
+      // NT = 4 scores tiles T0..T0+3 and leaves tile T0 + r in lane group r; NT = 2 scores tiles
+      // T0, T0+1 and leaves tile T0 + (r & 1) in lane group r (the quad sum of {T0, T0+1, T0,
+      // T0+1}), so with T0 = 4 q + 2 h the lane groups 2h, 2h+1 hold them in the quad's layout.
       unsigned pkc = 0u;
-      auto score_quad = [&](auto ovr_tag, auto quad_tag, float& Lo, float& Ao) {
+      auto score_quad = [&](auto ovr_tag, auto t0_tag, auto nt_tag, float& Lo, float& Ao) {
         constexpr bool OVR = decltype(ovr_tag)::value;
-        constexpr int q = decltype(quad_tag)::value;
+        constexpr int T0 = decltype(t0_tag)::value;
+        constexpr int NT = decltype(nt_tag)::value;
+        static_assert((NT == 4 && T0 % 4 == 0) || (NT == 2 && T0 % 2 == 0), "tile group");
         auto tile_err = [&](int tau, float e[4], unsigned& p01, unsigned& p23) {
           const float sc = tau == 0 ? 1.0f : (float)(1u << (2 * (tau - 1)));   // 4^(tau-1)
           const float* r = tau == 0 ? ra : rb;
@@ -791,17 +798,17 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
         };
         float e[4], en[4];
         unsigned p01, p23, pn01 = 0, pn23 = 0;
-        tile_err(4 * q, e, p01, p23);
+        tile_err(T0, e, p01, p23);
         {
           float pl[4], pa4[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int tau = 4 * q + u;
+          for (int u = 0; u < NT; ++u) {
+            const int tau = T0 + u;
             const v2u Bu = {p01, p23};
             const v4s B = __builtin_bit_cast(v4s, Bu);
             const v4f y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                 A1, B, __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A2, B, tau == 0 ? cacc0 : cacc1, 0, 0, 0), 0, 0, 0);
-            if (u < 3) tile_err(tau + 1, en, pn01, pn23);           // overlaps the MFMAs
+            if (u < NT - 1) tile_err(tau + 1, en, pn01, pn23);      // overlaps the MFMAs
             // bound: uncoupled, this lane's part of S_e = sum_i d_i |e_i| (A follows after the
             // group sum); coupled, (2 S_e,g)^2 + sum_i |e_i| om_i over the lane's 4 elements,
             // whose sum over the 4 groups is >= S_e^2 + S_e S_w + 2|e|^T(|P||w|) (Cauchy-Schwarz)
@@ -823,37 +830,60 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
             lp = fmaf(e[3], y[3], lp);
             pl[u] = lp;
             pa4[u] = ap;
-            if (u < 3) {
+            if (u < NT - 1) {
 #pragma unroll
               for (int t = 0; t < 4; ++t) e[t] = en[t];
               p01 = pn01;
               p23 = pn23;
             }
           }
-          Lo = quad_sum(pl) * (q == 0 ? sl0 : s1);      // lane group gg holds tile 4q + gg
+          if (NT == 2) {
+            pl[2] = pl[0];
+            pl[3] = pl[1];
+            pa4[2] = pa4[0];
+            pa4[3] = pa4[1];
+          }
+          Lo = quad_sum(pl) * (T0 == 0 ? sl0 : s1);     // tiles >= 1 share the scale s1
           Ao = quad_sum(pa4);
           if (!COUPLED) Ao *= fmaf(4.0f, Ao, S_w);       // A = S_e (4 S_e + S_w)
         }
       };
-      auto score = [&](auto quad_tag, float& Lo, float& Ao) {
-        if (has_ovr) score_quad(std::true_type{}, quad_tag, Lo, Ao);
-        else score_quad(std::false_type{}, quad_tag, Lo, Ao);
+      auto score = [&](auto t0_tag, auto nt_tag, float& Lo, float& Ao) {
+        if (has_ovr) score_quad(std::true_type{}, t0_tag, nt_tag, Lo, Ao);
+        else score_quad(std::false_type{}, t0_tag, nt_tag, Lo, Ao);
       };
+      using I0 = std::integral_constant<int, 0>;
+      using I2 = std::integral_constant<int, 2>;
+      using I4 = std::integral_constant<int, 4>;
+      using I6 = std::integral_constant<int, 6>;
       // lane l holds codes l + 1 (tiles 0..3) and l + 65 (tiles 4..7); 127 and 128 do not exist
       float Lq[2], Aq[2];
-      score(std::integral_constant<int, 1>{}, Lq[1], Aq[1]);
-      if (lane >= 62) Lq[1] = __builtin_inff();
       float U1 = 0.0f;
       bool win = false;
       if (kWindow) {
+        score(I6{}, I2{}, Lq[1], Aq[1]);             // codes 97..126 in lanes 32..61
+        if (lane < 32 || lane >= 62) Lq[1] = __builtin_inff();
         U1 = wave_min_ordered(fmaf(kErrC, Aq[1], Lq[1]));
-        win = lb_row > U1;
+        win = lower_bound(s96) > U1;
+        if (!win) {
+          float L45, A45;                              // codes 65..96 in lanes 0..31 (and again in 32..63)
+          score(I4{}, I2{}, L45, A45);
+          U1 = fminf(U1, wave_min_ordered(fmaf(kErrC, A45, L45)));
+          if (lane < 32) {
+            Lq[1] = L45;
+            Aq[1] = A45;
+          }
+          win = lower_bound(s64) > U1;
+        }
+      } else {
+        score(I4{}, I4{}, Lq[1], Aq[1]);
+        if (lane >= 62) Lq[1] = __builtin_inff();
       }
       if (win) {
         Lq[0] = __builtin_inff();
         Aq[0] = 0.0f;
       } else {
-        score(std::integral_constant<int, 0>{}, Lq[0], Aq[0]);
+        score(I0{}, I4{}, Lq[0], Aq[0]);
       }
       if (msearch) {                                 // candidates no multiplier proposes drop out
         bool al0, al1;

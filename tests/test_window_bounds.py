@@ -8,6 +8,7 @@ code above it at least LB_hi = sum_{|w_i| < s_hi/2} Imp_i min(|w_i|, s_hi/2 - |w
 s_hi = s_{start+32}.  These are statements about the objective the pages define, so the oracle's
 own candidate losses decide them; the kernel relies on them to skip the other codes."""
 import numpy as np
+import pytest
 
 import oracle
 from oracle.lh_oracle import candidate_scales, e4m3_ladder, fake_quant
@@ -97,11 +98,12 @@ def test_window_bounds_decide_most_blocks():
 
 
 # --------------------------------------------------------------------------- full Hessian
-# The full-Hessian sweep scores codes 65..126 first and skips codes 1..64 when
-#   LB = mu * sum_i (|w_i| - 6 s_64)_+^2            (no cross term)
-#   LB = c (mu c - 2 |b|),  c^2 = that sum,  mu c >= |b|   (b = P w, with the cross term)
-# exceeds the lowest loss among codes 65..126, mu a lower bound of the smallest eigenvalue of the
-# symmetric part of H.  The inequalities L_k >= LB for every k <= 64 are checked here on the
+# The full-Hessian sweep scores codes 97..126 first and skips codes 1..K, K = 96 (else 64 once
+# codes 65..96 are scored too), when
+#   LB_K = mu * sum_i (|w_i| - 6 s_K)_+^2             (no cross term)
+#   LB_K = c (mu c - 2 |b|),  c^2 = that sum,  mu c >= |b|   (b = P w, with the cross term)
+# exceeds the lowest loss among the codes scored, mu a lower bound of the smallest eigenvalue of
+# the symmetric part of H.  The inequalities L_k >= LB_K for every k <= K are checked here on the
 # oracle's own losses with mu = the exact smallest eigenvalue (the kernel's mu is smaller).
 
 def hessians(seed, n):
@@ -123,7 +125,8 @@ def hessians(seed, n):
     return np.array(Hs)
 
 
-def test_full_window_bound_holds_below_code_65():
+@pytest.mark.parametrize("K", [64, 96])
+def test_full_window_bound_holds_below_code_K(K):
     r = np.random.default_rng(72)
     n = 600
     W, _ = blocks(73, n)
@@ -131,34 +134,55 @@ def test_full_window_bound_holds_below_code_65():
     P = 0.1 * r.standard_normal((n, 16, 16)) * np.sqrt(np.abs(np.diagonal(H, axis1=1, axis2=2)))[:, :, None]
     amax = np.abs(W).max()
     g = np.full(n, float(oracle.global_scale(np.array([amax]))[0]))
-    s64 = candidate_scales(g[:1])[0, 63]
+    sK = candidate_scales(g[:1])[0, K - 1]
     L0, Q, C = oracle.candidate_losses(W, g, H, None)
     L1, _, _ = oracle.candidate_losses(W, g, H, P)
     S = 0.5 * (H + np.transpose(H, (0, 2, 1)))
     mu = np.linalg.eigvalsh(S)[:, 0]
     dead = np.trace(H, axis1=1, axis2=2) == 0
     mu[dead] = 1.0
-    c2 = (np.maximum(np.abs(W) - 6.0 * s64, 0.0) ** 2).sum(1)
+    c2 = (np.maximum(np.abs(W) - 6.0 * sK, 0.0) ** 2).sum(1)
     psd = mu > 0                        # the kernel uses the bound only with a positive mu
     assert 0.3 < psd.mean() < 1.0       # singular and indefinite Hessians are among the cases
     mu = np.where(psd, mu, 0.0)
     lb0 = mu * c2
-    low = L0[:, :64]
+    low = L0[:, :K]
     assert np.all(low[psd] >= lb0[psd, None] - 1e-12 * np.abs(low[psd])), "mu |e|^2 bound violated"
     b = np.einsum("bij,bj->bi", P, W)
     bn = np.linalg.norm(b, axis=1)
     c = np.sqrt(c2)
     ok = psd & (mu * c >= bn)
     lb1 = c * (mu * c - 2.0 * bn)
-    low1 = L1[:, :64]
+    low1 = L1[:, :K]
     assert np.all(low1[ok] >= lb1[ok, None] - 1e-12 * np.abs(low1[ok])), "coupled bound violated"
-    # not vacuous: for well-conditioned blocks whose argmin is above code 64 the bound rules out
-    # codes <= 64 for most blocks (here about three quarters: many of these blocks sit only a few
-    # times above the clipping level of code 64; on the MoE gate_up layer 96.6% of all rows)
-    U = L0[:, 64:].min(1)
+    # a bound for the larger code set is never above the smaller set's (6 s_K grows with K)
+    if K == 96:
+        s64 = candidate_scales(g[:1])[0, 63]
+        assert np.all(c2 <= (np.maximum(np.abs(W) - 6.0 * s64, 0.0) ** 2).sum(1))
+    # not vacuous: for well-conditioned blocks whose argmin is above code K the bound rules out
+    # codes <= K for most blocks (many of these blocks sit only a few times above the clipping
+    # level of code K)
+    U = L0[:, K:].min(1)
     good = np.array([np.linalg.eigvalsh(h)[0] > 1e-3 * np.abs(h).max() for h in S])
-    good &= L0.argmin(1) >= 64
-    assert good.sum() > 100 and np.mean((lb0 > U)[good]) > 0.6
+    good &= L0.argmin(1) >= K
+    assert good.sum() > 40 and np.mean((lb0 > U)[good]) > 0.5
+    # ... and on blocks of a layer-like tensor (N(0, 0.02) weights whose tensor amax is that of
+    # 3.3M such values, Hessians of 40 to 400 tokens) it rules out codes <= K for nearly all
+    rl = np.random.default_rng(76)
+    m = 400
+    Wl = rl.normal(0, 0.02, (m, 16)).astype(np.float32).astype(np.float64)
+    gl = np.full(m, float(oracle.global_scale(np.array([0.02 * 5.1]))[0]))
+    Hl = []
+    for j in range(m):
+        X = rl.standard_normal((int(rl.choice([40, 100, 400])), 16))
+        Hl.append((X.T @ X / len(X)).astype(np.float32).astype(np.float64))
+    Hl = np.array(Hl)
+    Ll, _, _ = oracle.candidate_losses(Wl, gl, Hl, None)
+    assert np.all(Ll.argmin(1) >= 96)                 # the argmin sits in the two top tiles
+    mul = np.linalg.eigvalsh(Hl)[:, 0]
+    lbl = mul * (np.maximum(np.abs(Wl) - 6.0 * candidate_scales(gl[:1])[0, K - 1], 0.0) ** 2).sum(1)
+    assert np.all(Ll[:, :K] >= lbl[:, None] - 1e-12 * np.abs(Ll[:, :K]))
+    assert np.mean(lbl > Ll[:, K:].min(1)) > 0.9
 
 
 def _chol32_passes(S, m, rng):
