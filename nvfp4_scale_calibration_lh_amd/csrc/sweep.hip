@@ -351,6 +351,8 @@ struct FullLds {
   unsigned short wn[16][4];   // winner's signed nibbles per row and lane group (override rows)
   double ex[4][16];    // float64 refinement: e of up to 4 contenders
   float ab[16];        // block amax per row of the tile (multiplier search)
+  float lb96[16];      // LB_96 and LB_64 per row of the tile (-inf: no bound)
+  float lb64[16];
   int mk[128];         // codes proposed by the multipliers, tagged with the row
 };
 
@@ -663,6 +665,43 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
       }
     }
     if (gg == 0) L.sw[i] = swr;
+    if (kWindow && mu > 0.0f) {
+      // LB_96 and LB_64 of row i (see the column set-up) from the lane's 4 elements of row i
+      float c96p = 0.0f, c64p = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float d96 = fmaxf(fmaf(-6.0f, s96, fabsf(wt[t])), 0.0f);   // one rounding of |w| - 6 s_K
+        const float d64 = fmaxf(fmaf(-6.0f, s64, fabsf(wt[t])), 0.0f);
+        c96p = fmaf(d96, d96, c96p);
+        c64p = fmaf(d64, d64, c64p);
+      }
+      const float c96 = group_sum(c96p) * (1.0f - 0x1p-18f);   // rounded down (7 roundings < 2^-21)
+      const float c64 = group_sum(c64p) * (1.0f - 0x1p-18f);
+      float lb96 = mu * c96 * (1.0f - 0x1p-22f), lb64 = mu * c64 * (1.0f - 0x1p-22f);
+      if (coupled) {
+        // |b_i| <= |fp32 (P w)_i| + 2^-20 (|P||w|)_i, and om_i >= 2 (|P||w|)_i
+        float bp = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float om = fmaf(dm[t], 0.5f * swr, 2.0f * pwt[t]);
+          const float bb = fmaf(0x1p-19f, om, fabsf(bt[t]));
+          bp = fmaf(bb, bb, bp);
+        }
+        const float bn = sqrtf(group_sum(bp)) * (1.0f + 0x1p-17f);     // >= |b|
+        auto lbc = [&](float c2) -> float {
+          const float cd = sqrtf(c2) * (1.0f - 0x1p-20f);               // <= c
+          const float tm = fmaf(mu, cd, -2.0f * bn);
+          return (mu * cd >= bn * (1.0f + 0x1p-20f) && tm > 0.0f) ? cd * tm * (1.0f - 0x1p-20f)
+                                                                   : -__builtin_inff();
+        };
+        lb96 = lbc(c96);
+        lb64 = lbc(c64);
+      }
+      if (gg == 0) {
+        L.lb96[i] = lb96;
+        L.lb64[i] = lb64;
+      }
+    }
     if (msearch) {
       // block amax of row i: the lane's 4 elements, then the 4 lane groups
       unsigned am = max(max(__float_as_uint(fabsf(wt[0])), __float_as_uint(fabsf(wt[1]))),
@@ -719,45 +758,23 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
           if (k != 0) tile_hit |= 1u << ((k - 1) >> 4);
         }
       }
-      // LB_K of codes 1..K (see the column set-up), -inf without a bound; sK = s_K
-      auto lower_bound = [&](float sK) -> float {
-        if (!(kWindow && mu > 0.0f)) return -__builtin_inff();
-        float c2p = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float dl = fmaxf(fmaf(-6.0f, sK, fabsf(w[t])), 0.0f);    // one rounding of |w| - 6 s_K
-          c2p = fmaf(dl, dl, c2p);
-        }
-        const float c2 = group_sum(c2p) * (1.0f - 0x1p-18f);   // rounded down (7 roundings < 2^-21)
-        if (coupled) {
-          // |b_i| <= |fp32 (P w)_i| + 2^-20 (|P||w|)_i, and om_i >= 2 (|P||w|)_i
-          float bp = 0.0f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float bb = fmaf(0x1p-19f, om[t], fabsf(L.b[rr][4 * gg + t]));
-            bp = fmaf(bb, bb, bp);
-          }
-          const float bn = sqrtf(group_sum(bp)) * (1.0f + 0x1p-17f);     // >= |b|
-          const float cd = sqrtf(c2) * (1.0f - 0x1p-20f);                  // <= c
-          const float tm = fmaf(mu, cd, -2.0f * bn);
-          return (mu * cd >= bn * (1.0f + 0x1p-20f) && tm > 0.0f) ? cd * tm * (1.0f - 0x1p-20f)
-                                                                   : -__builtin_inff();
-        }
-        return mu * c2 * (1.0f - 0x1p-22f);
-      };
-      float ra[4], rb[4];                            // w / s for this lane's tile-0 and tile-1 codes
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ra[t] = w[t] * is0;
-        rb[t] = w[t] * is1;
-      }
-      // accumulator inputs -(H w - 2 P w)_i / s of tile 0 and of tiles 1..7 (which share s1)
+      // w / s for this lane's tile-0 and tile-1 codes, and the accumulator inputs -(H w - 2 P w)_i / s
+      // of tile 0 and of tiles 1..7 (which share s1); the tile-0 values are formed only when codes
+      // 1..64 are scored
+      float ra[4], rb[4];
       v4f cacc0, cacc1;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        cacc0[t] = -gq[t] * is0;
+        rb[t] = w[t] * is1;
         cacc1[t] = -gq[t] * is1;
       }
+      auto tile0_inputs = [&]() {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ra[t] = w[t] * is0;
+          cacc0[t] = -gq[t] * is0;
+        }
+      };
 
       // Scoring of tile tau (16 codes): quotients (with exact overrides) -> FP4 round trip
       // q' = q * 4^(tau-1) (exact in bf16), e = fma(q', s, -w), y = H q' - (H w - 2b)/s on bf16
@@ -864,7 +881,8 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
         score(I6{}, I2{}, Lq[1], Aq[1]);             // codes 97..126 in lanes 32..61
         if (lane < 32 || lane >= 62) Lq[1] = __builtin_inff();
         U1 = wave_min_ordered(fmaf(kErrC, Aq[1], Lq[1]));
-        win = lower_bound(s96) > U1;
+        const bool bounded = mu > 0.0f;                // LB_96, LB_64 of the row are in L
+        win = bounded && L.lb96[rr] > U1;
         if (!win) {
           float L45, A45;                              // codes 65..96 in lanes 0..31 (and again in 32..63)
           score(I4{}, I2{}, L45, A45);
@@ -873,7 +891,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
             Lq[1] = L45;
             Aq[1] = A45;
           }
-          win = lower_bound(s64) > U1;
+          win = bounded && L.lb64[rr] > U1;
         }
       } else {
         score(I4{}, I4{}, Lq[1], Aq[1]);
@@ -883,6 +901,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
         Lq[0] = __builtin_inff();
         Aq[0] = 0.0f;
       } else {
+        tile0_inputs();
         score(I0{}, I4{}, Lq[0], Aq[0]);
       }
       if (msearch) {                                 // candidates no multiplier proposes drop out
