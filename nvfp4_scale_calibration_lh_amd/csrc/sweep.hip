@@ -392,7 +392,8 @@ __device__ inline float wave_max_nonneg(float x) {
 // Lane group gg's Cholesky test of A = S - m I (S in registers, lane i holding row i; the column
 // being eliminated passes through the 16 floats of LDS at cbuf + 16 gg): true when every pivot is
 // positive.
-__device__ inline bool chol_positive(const float (&srow)[16], float m, int i, int gg, float* cbuf) {
+__device__ __attribute__((always_inline)) inline bool chol_positive(const float (&srow)[16], float m, int i,
+                                                                     int gg, float* cbuf) {
   float a[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) a[k] = k == i ? srow[k] - m : srow[k];
@@ -428,8 +429,11 @@ __device__ inline bool chol_positive(const float (&srow)[16], float m, int i, in
 // diagonal entry (which bounds the smallest eigenvalue from above): d 2^-2, 2^-6, 2^-10, 2^-14,
 // then the three doublings of the largest that passed.  mu is the largest m that passed less
 // 2^-12 (else 0), scaled back.  A column of zero trace is scored as H = I: mu = 1.  Non-finite
-// H gives 0.
-__device__ inline float column_mu(const float* Hs, bool dead, int lane, float* cbuf) {
+// H gives 0.  Inlined where the caller's LDS arrays are visible, so its LDS accesses are LDS
+// instructions rather than generic ones; column_mu is the out-of-line form for the fused kernel,
+// whose register budget is already full.
+__device__ __attribute__((always_inline)) inline float column_mu_inl(const float* Hs, bool dead, int lane,
+                                                                     float* cbuf) {
   if (dead) return 1.0f;
   const int i = lane & 15, gg = lane >> 4;
   float a[16];
@@ -468,6 +472,9 @@ __device__ inline float column_mu(const float* Hs, bool dead, int lane, float* c
     if ((okm >> (16 * q)) & 1ull) eb = e1 + 1 + q;
   const float mu = __builtin_amdgcn_ldexpf(d, eb) - 0x1p-12f;
   return mu > 0.0f ? __builtin_amdgcn_ldexpf(mu, ex) : 0.0f;
+}
+__device__ __attribute__((noinline)) float column_mu(const float* Hs, bool dead, int lane, float* cbuf) {
+  return column_mu_inl(Hs, dead, lane, cbuf);
 }
 
 // Float64 re-scoring of one block by a whole wave: lane l scores codes l + 1 and l + 65 (those
@@ -626,7 +633,12 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
   // LB_K > U (the lowest upper end among the codes scored, at least their exact minimum) means no
   // code <= K is or ties the argmin.  The multiplier search scores all codes.
   constexpr bool kWindow = !MSEARCH;
-  const float mu = !(kWindow && fast) ? 0.0f : (mu_col ? *mu_col : column_mu(L.H, dead, lane, &L.g[0][0]));
+  // (the plain sweep always receives mu_col from k_column_mu; the fused kernel forms it here)
+  float mu = 0.0f;
+  if (kWindow && fast) {
+    if constexpr (RECORD) mu = column_mu(L.H, dead, lane, &L.g[0][0]);
+    else mu = *mu_col;
+  }
   const float s64 = cand_scale(64, gsc), s96 = cand_scale(96, gsc);
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
@@ -1108,7 +1120,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_column_mu(const float* __restri
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   double tr = 0.0;                                 // zero trace: scored as H = I (as the sweep)
   for (int j = 0; j < 16; ++j) tr += (double)hs[wave][j * 17];
-  const float m = column_mu(hs[wave], tr == 0.0, lane, cb[wave]);
+  const float m = column_mu_inl(hs[wave], tr == 0.0, lane, cb[wave]);
   if (lane == 0) mu[col] = m;
 }
 
