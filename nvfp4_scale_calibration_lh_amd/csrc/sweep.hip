@@ -430,9 +430,8 @@ __device__ __attribute__((always_inline)) inline bool chol_positive(const float 
 // then the three doublings of the largest that passed.  mu is the largest m that passed less
 // 2^-12 (else 0), scaled back.  A column of zero trace is scored as H = I: mu = 1.  Non-finite
 // H gives 0.  Inlined where the caller's LDS arrays are visible, so its LDS accesses are LDS
-// instructions rather than generic ones; column_mu is the out-of-line form for the fused kernel,
-// whose register budget is already full.
-__device__ __attribute__((always_inline)) inline float column_mu_inl(const float* Hs, bool dead, int lane,
+// instructions rather than generic ones.
+__device__ __attribute__((always_inline)) inline float column_mu(const float* Hs, bool dead, int lane,
                                                                      float* cbuf) {
   if (dead) return 1.0f;
   const int i = lane & 15, gg = lane >> 4;
@@ -472,9 +471,6 @@ __device__ __attribute__((always_inline)) inline float column_mu_inl(const float
     if ((okm >> (16 * q)) & 1ull) eb = e1 + 1 + q;
   const float mu = __builtin_amdgcn_ldexpf(d, eb) - 0x1p-12f;
   return mu > 0.0f ? __builtin_amdgcn_ldexpf(mu, ex) : 0.0f;
-}
-__device__ __attribute__((noinline)) float column_mu(const float* Hs, bool dead, int lane, float* cbuf) {
-  return column_mu_inl(Hs, dead, lane, cbuf);
 }
 
 // Float64 re-scoring of one block by a whole wave: lane l scores codes l + 1 and l + 65 (those
@@ -1120,7 +1116,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_column_mu(const float* __restri
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   double tr = 0.0;                                 // zero trace: scored as H = I (as the sweep)
   for (int j = 0; j < 16; ++j) tr += (double)hs[wave][j * 17];
-  const float m = column_mu_inl(hs[wave], tr == 0.0, lane, cb[wave]);
+  const float m = column_mu(hs[wave], tr == 0.0, lane, cb[wave]);
   if (lane == 0) mu[col] = m;
 }
 
