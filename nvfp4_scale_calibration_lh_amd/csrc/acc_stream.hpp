@@ -103,8 +103,11 @@ __device__ inline int e2m1_index_f64(double r) {
 // Fake-quantizes the 16 bytes a lane holds of one row: 8 bf16 (half a block; the other half is in
 // lane ^ 1) or 4 fp32 (a quarter; the block is the lane's quad).  gx = gX, inv6g = 1/(6 gX) in
 // float64, fast = gX in [2^-100, 2^100] (all scales and quotients normal).
+// *d_exact is set to false when the block's scale may have saturated far below its amax
+// (max|x| / (6 gX) > 672 or NaN): otherwise every x_q - x is exact in the input format (see
+// finish_stage).
 template <bool BF16>
-__device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool fast) {
+__device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool fast, bool* d_exact = nullptr) {
   constexpr int n = BF16 ? 8 : 4;
   float xf[n];
   unsigned am = 0;
@@ -130,6 +133,7 @@ __device__ inline v4u act_fake_quant(const v4u x, float gx, double inv6g, bool f
   const float v = fast ? e4m3_nearest_f32(__uint_as_float(am), inv6g)
                        : (gx > 0.0f ? e4m3_nearest((double)__uint_as_float(am) * inv6g) : 0.0f);
   const float s = v * gx;                         // fp32(v gX): one rounding of an exact product
+  if (d_exact) *d_exact = s == 0.0f || (double)__uint_as_float(am) * inv6g <= 672.0;
   float q[n];
   if (fast) {
     // Nearest grid values of x * (1/s) pushed up and down by 2^-19 bracket the exact quotient
@@ -215,6 +219,7 @@ struct Streamer {
   bool fq_fast = false;
   v4u pre[kM][Gm::kLoads];      // the chunk in flight
   v4u xs[Gm::kLoads];           // FQ: the staged chunk's X, kept for the fake-quant
+  bool d_exact = false;         // FQ: the stage holds D = X_q - X (exact) in place of X
 
   __device__ void set_fake_quant(float x_amax) {
     gx = x_amax / 2688.0f;                       // fp32(amax / (6*448)), correctly rounded
@@ -246,26 +251,59 @@ struct Streamer {
     }
   }
 
-  // With FQ only X is staged, into the second matrix's place.
+  // With FQ, X is kept in registers and finish_stage writes the stage.
   __device__ void stage_chunk(int64_t c0, int64_t r1) {
 #pragma unroll
     for (int q = 0; q < Gm::kLoads; ++q) {
       const int row = lrow() + q * Gm::kRowsPerLoad;
       const bool on = col_on() && c0 + row < r1;
+      if constexpr (FQ) {
+        xs[q] = on ? pre[1][q] : v4u{0u, 0u, 0u, 0u};
+      } else {
 #pragma unroll
-      for (int m = FQ ? 1 : 0; m < kM; ++m)
-        *(v4u*)&stage[m * Gm::kWords + word(row, lcol())] = on ? pre[m][q] : v4u{0u, 0u, 0u, 0u};
-      if constexpr (FQ) xs[q] = on ? pre[1][q] : v4u{0u, 0u, 0u, 0u};
+        for (int m = 0; m < kM; ++m)
+          *(v4u*)&stage[m * Gm::kWords + word(row, lcol())] = on ? pre[m][q] : v4u{0u, 0u, 0u, 0u};
+      }
     }
   }
 
   __device__ void finish_stage() {
     if constexpr (FQ) {
-      // each lane quantizes the 16 bytes of X it staged (an X of zeros stays zero)
+      // Each lane quantizes the 16 bytes of X it holds (an X of zeros stays zero) and stages X_q
+      // and D = X_q - X.  Every x_q is 0 or has the sign of x and lies within a factor of 2 of it:
+      // the E2M1 cell of |x|/s keeps grid / |x|/s in [2/3, 2], the value 0.5 s rounded to the input
+      // format cannot pass 2|x| (a value of that format above it), and a scale v gX that did not
+      // saturate far below the block's amax (max|x| / (6 gX) <= 672, so max|x| <= 9 s even for the
+      // smallest subnormal v) keeps saturated elements within 2/3 of 6 s.  By Sterbenz's lemma D is
+      // then exact in the input format, one bf16 piece, and the cross matrix takes one MFMA on it.
+      // When some block of the chunk may have saturated further, X is staged instead and the
+      // contraction splits D as for a stored X_q.
+      bool ok = true;
 #pragma unroll
       for (int q = 0; q < Gm::kLoads; ++q) {
         const int w = word(lrow() + q * Gm::kRowsPerLoad, lcol());
-        *(v4u*)&stage[w] = act_fake_quant<BF16>(xs[q], gx, inv6g, fq_fast);   // every lane: uses its pair/quad
+        bool okq;
+        const v4u xq = act_fake_quant<BF16>(xs[q], gx, inv6g, fq_fast, &okq);   // every lane: uses its pair/quad
+        ok = ok && okq;
+        *(v4u*)&stage[w] = xq;
+        v4u d;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if constexpr (BF16) {
+            const float d0 = bf16_lo(xq[p]) - bf16_lo(xs[q][p]);    // exact, a bf16 value
+            const float d1 = bf16_hi(xq[p]) - bf16_hi(xs[q][p]);
+            d[p] = (__float_as_uint(d0) >> 16) | (__float_as_uint(d1) & 0xFFFF0000u);
+          } else {
+            d[p] = __float_as_uint(__uint_as_float(xq[p]) - __uint_as_float(xs[q][p]));
+          }
+        }
+        *(v4u*)&stage[Gm::kWords + w] = d;
+      }
+      d_exact = !__builtin_amdgcn_ballot_w64(!ok);
+      if (!d_exact) {
+#pragma unroll
+        for (int q = 0; q < Gm::kLoads; ++q)
+          *(v4u*)&stage[Gm::kWords + word(lrow() + q * Gm::kRowsPerLoad, lcol())] = xs[q];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -306,7 +344,19 @@ struct Streamer {
         }
         const v8bf A = __builtin_bit_cast(v8bf, aq);
         accH[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, accH[b], 0, 0, 0);
-        if (ACT) {
+        if (FQ && d_exact) {
+          // D = X_q - X staged as one exact bf16 piece (finish_stage): the same value the split
+          // below gives (its remainders are zero), one MFMA
+          const unsigned short* td = (const unsigned short*)(stage + Gm::kWords);
+          v4u dq;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const unsigned d0 = td[(8 * gg + 2 * u) * kPitchH + 16 * b + i];
+            const unsigned d1 = td[(8 * gg + 2 * u + 1) * kPitchH + 16 * b + i];
+            dq[u] = d0 | (d1 << 16);
+          }
+          accP[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(v8bf, dq), accP[b], 0, 0, 0);
+        } else if (ACT) {
           // d = fp32(xq - x) (relative error <= 2^-24, exact whenever the two are within 2^15 of
           // each other) is split exactly into bf16 pieces: hi = its top 8 significant bits, lo =
           // the next 8 bits of the remainder, rest = the at most 8 bits left.  rest is zero when d
@@ -357,7 +407,8 @@ struct Streamer {
           accH[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(q, q, accH[b], 0, 0, 0);
           if (ACT) {
             const float x = ((const float*)(stage + (kM - 1) * Gm::kWords))[(4 * s + gg) * kPitchF + 16 * b + i];
-            accP[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(q, q - x, accP[b], 0, 0, 0);
+            // FQ with an exact D staged: x is already q - x
+            accP[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(q, (FQ && d_exact) ? x : q - x, accP[b], 0, 0, 0);
           }
         }
       }
