@@ -35,9 +35,10 @@
  * Numerics
  *   - Accumulation reads bf16 or fp32 values exactly, multiplies them exactly (bf16) or in fp32
  *     (fp32 inputs), and sums in fp32 in a fixed order: results are bit-reproducible run to run.
- *   - The sweep returns the scale code and FP4 codes of the exact argmin of the float64 objective:
- *     a float32 pass scores every candidate with a rigorous error bound and any block whose
- *     winner is not certain is re-scored in float64 with exact quantization.
+ *   - The sweep returns the scale code and FP4 codes of the exact argmin of the float64 objective
+ *     over all 126 candidates: a float32 pass scores each candidate that a proven lower bound does
+ *     not rule out, with a rigorous error bound, and any block whose winner is not certain is
+ *     re-scored in float64 with exact quantization.
  *
  * Citations are to the pages this library follows: "Add activation-aware local Hessian scale
  * calibration" (PR #1976), "add local hessian calibration" (PR #788), "Add WMSE weight scale

@@ -12,8 +12,9 @@
 //
 // MI355X design
 //  * Full form: one wave per block column n (H_n is loaded once and kept in registers) walking 32
-//    rows c; per block, 8 tiles of 16 candidates cover the 126 codes.  Lane l owns candidate
-//    l%16 of a tile and elements 4*(l/16)..+3.  The lane quantizes its 4 elements in fp32
+//    rows c; per block, 8 tiles of 16 candidates cover the 126 codes, the top two tiles first and
+//    the others only where a lower bound from the column's smallest eigenvalue does not rule them
+//    out (see sweep_full_column).  Lane l owns candidate l%16 of a tile and elements 4*(l/16)..+3.  The lane quantizes its 4 elements in fp32
 //    (r = w * (1/s), the gfx950 FP4 convert, which rounds to nearest-even on the E2M1 grid and
 //    saturates at 6, and the convert back), and forms e = fma(q, s, -w).
 //  * The contraction H_n e is reorganized so the matrix cores see exact small integers:
