@@ -418,9 +418,8 @@ __device__ __attribute__((always_inline)) inline bool chol_positive(const float 
   return ok;
 }
 
-// A lower bound mu >= 0 of the smallest eigenvalue of S = (H + H^T)/2 for a column's Hessian H
-// (16x16 row-major in LDS), the same value in every lane: every e then has e^T H e = e^T S e >=
-// mu |e|^2.  S is scaled by a power of two to max |S_ij| in [1/2, 1).  If a float32 Cholesky
+// A lower bound mu of the smallest eigenvalue of S = (H + H^T)/2 for a column's Hessian H (16x16
+// row-major in LDS), the same value in every lane: every e then has e^T H e = e^T S e >= mu |e|^2.  S is scaled by a power of two to max |S_ij| in [1/2, 1).  If a float32 Cholesky
 // factorization of S - m I completes with positive pivots, R^T R = S - m I + E with
 // |E_ij| <= gamma_17 (|R^T||R|)_ij (the standard backward error of Cholesky, here with unit
 // roundoff 2^-22 for the reciprocal square root and product), and (|R^T||R|)_ij <=
@@ -428,9 +427,12 @@ __device__ __attribute__((always_inline)) inline bool chol_positive(const float 
 // 2^-13.8; with the roundings of S's entries (2^-20 in norm) the smallest eigenvalue of S is at
 // least m - 2^-13.7.  The four lane groups test four values of m at a time, below d, the smallest
 // diagonal entry (which bounds the smallest eigenvalue from above): d 2^-2, 2^-6, 2^-10, 2^-14,
-// then the three doublings of the largest that passed.  mu is the largest m that passed less
-// 2^-12 (else 0), scaled back.  A column of zero trace is scored as H = I: mu = 1.  Non-finite
-// H gives 0.  Inlined where the caller's LDS arrays are visible, so its LDS accesses are LDS
+// then the three doublings of the largest that passed.  When none passes (or d <= 0: a singular
+// or nearly singular S), they test the negative shifts m = -2^-14, -2^-12, -2^-10, -2^-8, for which
+// the same argument holds (the diagonal of S - m I stays below 1.004).  mu is the largest m that
+// passed less 2^-12, scaled back: S - mu I is positive semidefinite, and mu can be <= 0.  No
+// passing m, or non-finite H, gives -inf (no bound).  A column of zero trace is scored as H = I:
+// mu = 1.  Inlined where the caller's LDS arrays are visible, so its LDS accesses are LDS
 // instructions rather than generic ones.
 __device__ __attribute__((always_inline)) inline float column_mu(const float* Hs, bool dead, int lane,
                                                                      float* cbuf) {
@@ -445,9 +447,9 @@ __device__ __attribute__((always_inline)) inline float column_mu(const float* Hs
     fin = fin && fabsf(a[k]) <= 0x1.fffffep127f;     // false for inf and NaN
     mx = fmaxf(mx, fabsf(a[k]));
   }
-  if (__ballot(!fin)) return 0.0f;
+  if (__ballot(!fin)) return -__builtin_inff();
   mx = wave_max_nonneg(mx);
-  if (!(mx > 0.0f)) return 0.0f;
+  if (!(mx > 0.0f)) return -__builtin_inff();
   const int ex = __builtin_amdgcn_frexp_expf(mx);   // mx = f 2^ex, f in [1/2, 1)
 #pragma unroll
   for (int k = 0; k < 16; ++k) a[k] = __builtin_amdgcn_ldexpf(a[k], -ex);
@@ -455,14 +457,22 @@ __device__ __attribute__((always_inline)) inline float column_mu(const float* Hs
 #pragma unroll
   for (int k = 0; k < 16; ++k) di = k == i ? a[k] : di;
   const float d = wave_min_ordered(di);
-  if (!(d > 0.0f)) return 0.0f;
-  // round 1: m = d 2^-(4 gg + 2)
-  unsigned long long okm = __ballot(chol_positive(a, __builtin_amdgcn_ldexpf(d, -(4 * gg + 2)), i, gg, cbuf));
   int e1 = 0;                                        // exponent of the largest m that passed
+  unsigned long long okm = 0ull;
+  if (d > 0.0f) {
+    // round 1: m = d 2^-(4 gg + 2)
+    okm = __ballot(chol_positive(a, __builtin_amdgcn_ldexpf(d, -(4 * gg + 2)), i, gg, cbuf));
 #pragma unroll
-  for (int q = 3; q >= 0; --q)
-    if ((okm >> (16 * q)) & 1ull) e1 = -(4 * q + 2);
-  if (e1 == 0) return 0.0f;
+    for (int q = 3; q >= 0; --q)
+      if ((okm >> (16 * q)) & 1ull) e1 = -(4 * q + 2);
+  }
+  if (e1 == 0) {
+    // negative shifts m = -2^(2 gg - 14); the least negative that passes
+    okm = __ballot(chol_positive(a, -__builtin_amdgcn_ldexpf(1.0f, 2 * gg - 14), i, gg, cbuf));
+    if (okm == 0ull) return -__builtin_inff();
+    const int q = (int)__builtin_ctzll(okm) >> 4;
+    return __builtin_amdgcn_ldexpf(-__builtin_amdgcn_ldexpf(1.0f, 2 * q - 14) - 0x1p-12f, ex);
+  }
   // round 2: m = d 2^(e1 + 1 + gg) for gg < 3 (group 3 repeats the passed value)
   const int e2 = gg < 3 ? e1 + 1 + gg : e1;
   okm = __ballot(e2 <= -1 && chol_positive(a, __builtin_amdgcn_ldexpf(d, e2), i, gg, cbuf));
@@ -470,8 +480,7 @@ __device__ __attribute__((always_inline)) inline float column_mu(const float* Hs
 #pragma unroll
   for (int q = 0; q < 3; ++q)
     if ((okm >> (16 * q)) & 1ull) eb = e1 + 1 + q;
-  const float mu = __builtin_amdgcn_ldexpf(d, eb) - 0x1p-12f;
-  return mu > 0.0f ? __builtin_amdgcn_ldexpf(mu, ex) : 0.0f;
+  return __builtin_amdgcn_ldexpf(__builtin_amdgcn_ldexpf(d, eb) - 0x1p-12f, ex);
 }
 
 // Float64 re-scoring of one block by a whole wave: lane l scores codes l + 1 and l + 65 (those
@@ -631,12 +640,26 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
   // code <= K is or ties the argmin.  The multiplier search scores all codes.
   constexpr bool kWindow = !MSEARCH;
   // (the plain sweep always receives mu_col from k_column_mu; the fused kernel forms it here)
-  float mu = 0.0f;
+  float mu = -__builtin_inff();                   // no bound
   if (kWindow && fast) {
     if constexpr (RECORD) mu = column_mu(L.H, dead, lane, &L.g[0][0]);
     else mu = *mu_col;
   }
   const float s64 = cand_scale(64, gsc), s96 = cand_scale(96, gsc);
+  // In the uncoupled form (the COUPLED kernels keep the bound above) a second bound needs only mu > -inf (S - mu I positive semidefinite):
+  // for k <= K the block's FP4 values q (e = q - w) have |q_i| <= tau = 6 s_K, so in the seminorm
+  // of S - mu I the triangle inequality and |q^T A q| <= tau^2 sum |A_ij| give
+  //   L_k >= (sqrt(w^T H w - mu |w|^2) - tau sqrt(sum |H_ij| + 16 |mu|))_+^2 + mu_term,
+  // mu_term = mu sum_i (|w_i| - tau)_+^2 (mu >= 0) or mu (|w| + 4 tau)^2 (mu < 0), which decides
+  // most rows of near-singular Hessians (experts with few routed tokens).  habs >= sum |H_ij|.
+  const bool tri_ok = kWindow && !COUPLED && mu > -__builtin_inff();
+  float habs = 0.0f;
+  if (tri_ok) {
+    float hp = fabsf(a[0]) + fabsf(a[1]) + fabsf(a[2]) + fabsf(a[3]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) hp += __shfl_xor(hp, o, 64);
+    habs = group_sum(hp) * (1.0f + 0x1p-17f);     // 64 terms: rounded up
+  }
 
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 16) {
     // ---- 16-row tile: w, H w, P w and |P||w| (fp32 MFMA, K index = element 4*gg + t)
@@ -674,37 +697,77 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
       }
     }
     if (gg == 0) L.sw[i] = swr;
-    if (kWindow && mu > 0.0f) {
-      // LB_96 and LB_64 of row i (see the column set-up) from the lane's 4 elements of row i
-      float c96p = 0.0f, c64p = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float d96 = fmaxf(fmaf(-6.0f, s96, fabsf(wt[t])), 0.0f);   // one rounding of |w| - 6 s_K
-        const float d64 = fmaxf(fmaf(-6.0f, s64, fabsf(wt[t])), 0.0f);
-        c96p = fmaf(d96, d96, c96p);
-        c64p = fmaf(d64, d64, c64p);
-      }
-      const float c96 = group_sum(c96p) * (1.0f - 0x1p-18f);   // rounded down (7 roundings < 2^-21)
-      const float c64 = group_sum(c64p) * (1.0f - 0x1p-18f);
-      float lb96 = mu * c96 * (1.0f - 0x1p-22f), lb64 = mu * c64 * (1.0f - 0x1p-22f);
-      if (coupled) {
-        // |b_i| <= |fp32 (P w)_i| + 2^-20 (|P||w|)_i, and om_i >= 2 (|P||w|)_i
-        float bp = 0.0f;
+    if (kWindow) {
+      // LB_96 and LB_64 of row i (see the column set-up) from the lane's 4 elements of row i;
+      // -inf where there is no bound
+      float lb96 = -__builtin_inff(), lb64 = -__builtin_inff();
+      if (mu > -__builtin_inff()) {
+        float c96p = 0.0f, c64p = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float om = fmaf(dm[t], 0.5f * swr, 2.0f * pwt[t]);
-          const float bb = fmaf(0x1p-19f, om, fabsf(bt[t]));
-          bp = fmaf(bb, bb, bp);
+          const float d96 = fmaxf(fmaf(-6.0f, s96, fabsf(wt[t])), 0.0f);   // one rounding of |w| - 6 s_K
+          const float d64 = fmaxf(fmaf(-6.0f, s64, fabsf(wt[t])), 0.0f);
+          c96p = fmaf(d96, d96, c96p);
+          c64p = fmaf(d64, d64, c64p);
         }
-        const float bn = sqrtf(group_sum(bp)) * (1.0f + 0x1p-17f);     // >= |b|
-        auto lbc = [&](float c2) -> float {
-          const float cd = sqrtf(c2) * (1.0f - 0x1p-20f);               // <= c
-          const float tm = fmaf(mu, cd, -2.0f * bn);
-          return (mu * cd >= bn * (1.0f + 0x1p-20f) && tm > 0.0f) ? cd * tm * (1.0f - 0x1p-20f)
-                                                                   : -__builtin_inff();
-        };
-        lb96 = lbc(c96);
-        lb64 = lbc(c64);
+        const float c96 = group_sum(c96p) * (1.0f - 0x1p-18f);   // rounded down (7 roundings < 2^-21)
+        const float c64 = group_sum(c64p) * (1.0f - 0x1p-18f);
+        if (mu > 0.0f) {
+          lb96 = mu * c96 * (1.0f - 0x1p-22f);
+          lb64 = mu * c64 * (1.0f - 0x1p-22f);
+        }
+        if (coupled && mu > 0.0f) {
+          // |b_i| <= |fp32 (P w)_i| + 2^-20 (|P||w|)_i, and om_i >= 2 (|P||w|)_i
+          float bp = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float om = fmaf(dm[t], 0.5f * swr, 2.0f * pwt[t]);
+            const float bb = fmaf(0x1p-19f, om, fabsf(bt[t]));
+            bp = fmaf(bb, bb, bp);
+          }
+          const float bn = sqrtf(group_sum(bp)) * (1.0f + 0x1p-17f);     // >= |b|
+          auto lbc = [&](float c2) -> float {
+            const float cd = sqrtf(c2) * (1.0f - 0x1p-20f);               // <= c
+            const float tm = fmaf(mu, cd, -2.0f * bn);
+            return (mu * cd >= bn * (1.0f + 0x1p-20f) && tm > 0.0f) ? cd * tm * (1.0f - 0x1p-20f)
+                                                                     : -__builtin_inff();
+          };
+          lb96 = lbc(c96);
+          lb64 = lbc(c64);
+        }
+        if (tri_ok) {
+          // w^T H w from the fp32 H w of the tile: |w^T H w - sum w_i (H w)_i| <= 2^-18 S_w^2
+          // (2^-20 S_w^2 from H w, the 16-term sum's roundings below 2^-21 S_w^2)
+          float whp = 0.0f, wwp = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            whp = fmaf(wt[t], hw[t], whp);
+            wwp = fmaf(wt[t], wt[t], wwp);
+          }
+          const float whw = group_sum(whp) - 0x1p-18f * swr * swr;        // <= w^T H w (rounding aside)
+          const float ww = group_sum(wwp);                                 // |w|^2 within 2^-21
+          // whw - mu |w|^2, rounded down: mu |w|^2 taken 2^-20 larger (mu > 0) or smaller (mu < 0)
+          const float pw = (whw - mu * ww * (mu > 0.0f ? 1.0f + 0x1p-20f : 1.0f - 0x1p-20f)) *
+                           (1.0f - 0x1p-20f) - 0x1p-22f * fabsf(whw);
+          const float hq = sqrtf(habs + 16.0f * fabsf(mu)) * (1.0f + 0x1p-20f);
+          auto lbt = [&](float sK, float c2) -> float {
+            const float tau = 6.0f * sK * (1.0f + 0x1p-22f);                // >= 6 s_K
+            const float tq = tau * hq * (1.0f + 0x1p-22f);
+            const float rt = sqrtf(fmaxf(pw, 0.0f)) * (1.0f - 0x1p-20f);
+            const float tv = (rt - tq) - 0x1p-22f * rt;                     // rounded down
+            const float t2 = tv > 0.0f ? tv * tv * (1.0f - 0x1p-21f) : 0.0f;
+            float mt;                                                       // mu_term, rounded down
+            if (mu >= 0.0f) {
+              mt = mu * c2 * (1.0f - 0x1p-22f);
+            } else {
+              const float en = (sqrtf(ww) * (1.0f + 0x1p-20f) + 4.0f * tau) * (1.0f + 0x1p-22f);
+              mt = mu * en * en * (1.0f + 0x1p-20f);
+            }
+            return (t2 + mt) - 0x1p-22f * (t2 + fabsf(mt));
+          };
+          lb96 = fmaxf(lb96, lbt(s96, c96));
+          lb64 = fmaxf(lb64, lbt(s64, c64));
+        }
       }
       if (gg == 0) {
         L.lb96[i] = lb96;
@@ -890,8 +953,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
         score(I6{}, I2{}, Lq[1], Aq[1]);             // codes 97..126 in lanes 32..61
         if (lane < 32 || lane >= 62) Lq[1] = __builtin_inff();
         U1 = wave_min_ordered(fmaf(kErrC, Aq[1], Lq[1]));
-        const bool bounded = mu > 0.0f;                // LB_96, LB_64 of the row are in L
-        win = bounded && L.lb96[rr] > U1;
+        win = L.lb96[rr] > U1;                         // LB_96, LB_64 of the row are in L
         if (!win) {
           float L45, A45;                              // codes 65..96 in lanes 0..31 (and again in 32..63)
           score(I4{}, I2{}, L45, A45);
@@ -900,7 +962,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
             Lq[1] = L45;
             Aq[1] = A45;
           }
-          win = bounded && L.lb64[rr] > U1;
+          win = L.lb64[rr] > U1;
         }
       } else {
         score(I4{}, I4{}, Lq[1], Aq[1]);

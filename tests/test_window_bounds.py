@@ -227,3 +227,83 @@ def test_cholesky_certificate_margin():
                 passed += 1
                 assert lam >= m - 2.0 ** -12, (lam, m)
     assert tried > 1000 and passed > 300
+
+
+def test_cholesky_certificate_negative_shifts():
+    """The negative shifts m = -2^-14 .. -2^-8 that the certificate tries when no positive one
+    passes: a float32 factorization of S - m I with positive pivots still certifies
+    lambda_min(S) >= m - 2^-12, on singular (fewer than 16 rows), near-singular and indefinite S,
+    and the shifts pass for singular X^T X (the case they are there for)."""
+    r = np.random.default_rng(81)
+    tried = passed = passed_singular = singular = 0
+    for j in range(300):
+        T = int(r.choice([4, 10, 13, 15, 16, 17]))
+        X = r.standard_normal((T, 16))
+        S = X.T @ X
+        if j % 5 == 4:
+            S = S - 2.0 ** -9 * np.abs(S).max() * np.eye(16)     # slightly indefinite
+        S = S / (np.abs(S).max() * 1.0001)
+        S = S.astype(np.float32).astype(np.float64)
+        lam = np.linalg.eigvalsh(S)[0]
+        singular += T < 16 and j % 5 != 4
+        for e in (-14, -12, -10, -8):
+            m = -2.0 ** e
+            tried += 1
+            if _chol32_passes(S, m, r):
+                passed += 1
+                passed_singular += T < 16 and j % 5 != 4 and e == -12
+                assert lam >= m - 2.0 ** -12, (lam, m)
+    assert tried == 1200 and passed > 300 and passed_singular > 0.9 * singular
+
+
+# The full-Hessian sweep also uses, in its uncoupled form, a bound that needs no positive smallest
+# eigenvalue.  With mu <= lambda_min(S) (any sign, S the symmetric part of H), S - mu I is positive
+# semidefinite; for k <= K the quantized block q (e = q - w) has |q_i| <= tau = 6 s_K, so in the
+# seminorm of S - mu I the triangle inequality and |x^T A x| <= max|x_i|^2 sum |A_ij| give
+#   L_k = e^T S e >= (sqrt(w^T H w - mu |w|^2) - tau sqrt(sum |H_ij| + 16 |mu|))_+^2 + mu_term,
+# mu_term = mu sum_i (|w_i| - tau)_+^2 for mu >= 0 and mu (|w| + 4 tau)^2 for mu < 0.
+
+def _triangle_bound(W, H, mu, tau):
+    whw = np.einsum("bi,bij,bj->b", W, H, W)
+    ww = (W * W).sum(1)
+    A = np.abs(H).sum((1, 2)) + 16.0 * np.abs(mu)
+    t = np.maximum(np.sqrt(np.maximum(whw - mu * ww, 0.0)) - tau * np.sqrt(A), 0.0)
+    mu_term = np.where(mu >= 0, mu * (np.maximum(np.abs(W) - tau, 0.0) ** 2).sum(1),
+                       mu * (np.sqrt(ww) + 4.0 * tau) ** 2)
+    return t * t + mu_term
+
+
+@pytest.mark.parametrize("K", [64, 96])
+def test_triangle_bound_holds_below_code_K(K):
+    r = np.random.default_rng(77)
+    n = 600
+    W, _ = blocks(78, n)
+    H = hessians(79, n)                             # singular, indefinite and regular
+    amax = np.abs(W).max()
+    g = np.full(n, float(oracle.global_scale(np.array([amax]))[0]))
+    tau = 6.0 * candidate_scales(g[:1])[0, K - 1]
+    L, _, _ = oracle.candidate_losses(W, g, H, None)
+    S = 0.5 * (H + np.transpose(H, (0, 2, 1)))
+    lam = np.linalg.eigvalsh(S)[:, 0]
+    live = np.trace(H, axis1=1, axis2=2) != 0
+    for shift in (0.0, 1e-3):                       # the exact lambda_min and a smaller mu
+        mu = lam - shift * np.abs(S).max((1, 2))
+        lb = _triangle_bound(W, H, mu, tau)
+        low = L[:, :K]
+        assert np.all(low[live] >= lb[live, None] - 1e-12 * np.abs(low[live])), "triangle bound violated"
+    # not vacuous where the eigenvalue bound is: Hessians of 10 to 16 tokens (singular or nearly)
+    # on layer-like blocks, whose argmin is in the two top tiles
+    rl = np.random.default_rng(80)
+    m = 400
+    Wl = rl.normal(0, 0.02, (m, 16)).astype(np.float32).astype(np.float64)
+    gl = np.full(m, float(oracle.global_scale(np.array([0.02 * 5.1]))[0]))
+    Hl = np.array([(X.T @ X / len(X)).astype(np.float32).astype(np.float64)
+                   for X in (rl.standard_normal((int(rl.choice([10, 13, 16])), 16)) for _ in range(m))])
+    Ll, _, _ = oracle.candidate_losses(Wl, gl, Hl, None)
+    taul = 6.0 * candidate_scales(gl[:1])[0, K - 1]
+    lam_l = np.linalg.eigvalsh(Hl)[:, 0]
+    lbl = _triangle_bound(Wl, Hl, lam_l - 2.0 ** -10 * np.abs(Hl).max((1, 2)), taul)
+    assert np.all(Ll[:, :K] >= lbl[:, None] - 1e-12 * np.abs(Ll[:, :K]))
+    eig_lb = np.maximum(lam_l, 0.0) * (np.maximum(np.abs(Wl) - taul, 0.0) ** 2).sum(1)
+    U = Ll[:, K:].min(1)
+    assert np.mean(eig_lb > U) < 0.3 and np.mean(lbl > U) > 0.5
