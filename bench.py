@@ -44,9 +44,10 @@ FLOPS_DIAG = 126 * (32 + 48)
 # for most blocks that a range of codes cannot hold the argmin and do not score those codes, so
 # the algorithmic rate can exceed the fp32 peak; `counters` gives the share of VALU issue slots
 # the kernel actually used.
-WORK_NOTE_FULL = ("achieved counts all 126 candidates per block; codes 1-64 are skipped for blocks "
-                  "where the column's certified smallest Hessian eigenvalue rules them out, so achieved "
-                  "can exceed peak; counters.valu_issue_frac is the issue share actually used")
+WORK_NOTE_FULL = ("achieved counts all 126 candidates per block; codes 1-96 are skipped for blocks "
+                  "where a proven lower bound (the column's certified smallest Hessian eigenvalue, or "
+                  "the triangle inequality in its seminorm) rules them out, so achieved can exceed "
+                  "peak; counters.valu_issue_frac is the issue share actually used")
 WORK_NOTE_DIAG = ("achieved counts all 126 candidates per block; only a 32-code window proven to hold "
                   "the argmin is scored, so achieved can exceed peak; counters.valu_issue_frac is the "
                   "issue share actually used")
