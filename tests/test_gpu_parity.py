@@ -634,6 +634,49 @@ def test_sweep_full_hessian_and_weight_ranges(coupled):
     assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), loss.cpu().numpy(), res)
 
 
+def test_sweep_full_near_singular_and_indefinite_hessians():
+    """Hessians of 2 to 20 tokens (singular below 16), slightly and strongly indefinite ones,
+    non-symmetric ones and outlier channels, on layer-like weights: the eigenvalue certificate
+    takes negative shifts here and the sweep skips low codes by the triangle-inequality bound where
+    that certificate allows; every block must still get the oracle's argmin, FP4 codes and loss."""
+    r = np.random.default_rng(36)
+    G, cout, cin = 8, 96, 128
+    nb = cin // 16
+    W = r.normal(0, 0.02, (G, cout, cin)).astype(np.float32)
+    H = np.empty((G, nb, 16, 16))
+    for g in range(G):
+        for n in range(nb):
+            T = int(r.choice([2, 8, 13, 15, 16, 20]))
+            X = r.standard_normal((T, 16))
+            if (g + n) % 5 == 1:
+                X[:, r.integers(16)] *= 20.0
+            h = X.T @ X / T
+            if g == 5:
+                h -= 2.0 ** -11 * np.abs(h).max() * np.eye(16)      # slightly indefinite
+            if g == 6:
+                h -= 0.05 * np.abs(h).max() * np.eye(16)            # indefinite beyond any shift
+            if g == 7:
+                h += 1e-3 * np.abs(h).max() * r.standard_normal((16, 16))   # not symmetric
+            H[g, n] = h
+    H = H.astype(np.float32)
+    a = oracle.absmax(W.astype(np.float64)).astype(np.float32)
+    note(f"full sweep near-singular and indefinite Hessians G={G} cout={cout} cin={cin}")
+    code, fp4, loss = lh.lh_scale_sweep(torch.from_numpy(W).to(DEV), torch.from_numpy(a).to(DEV),
+                                        torch.from_numpy(H).to(DEV), None)
+    res = oracle.sweep(W.astype(np.float64), a, H, None)
+    # codes and FP4 codes exactly; the loss, an fp32 evaluation of e^T H e, within 1e-5 of the
+    # scale its roundings follow, sum_ij |e_i||H_ij||e_j|, which for singular and indefinite H can
+    # be far above e^T H e itself (the Q + |C| scale of reading 16 presumes a positive definite H)
+    assert_sweep_match(code.cpu().numpy(), fp4.cpu().numpy(), None, res)
+    W64 = W.astype(np.float64).reshape(G, cout, nb, 16)
+    cs = oracle.candidate_scales(oracle.global_scale(a.astype(np.float64)))          # [G, 126]
+    sk = cs[np.arange(G)[:, None], res["code"].reshape(G, -1).astype(np.int64) - 1]        # [G, cout*nb]
+    _, _, e = oracle.fake_quant(W64, sk.reshape(G, cout, nb, 1))
+    scale = np.einsum("gcni,gnij,gcnj->gcn", np.abs(e), np.abs(H.astype(np.float64)), np.abs(e))
+    dl = np.abs(loss.cpu().numpy().astype(np.float64) - res["loss"])
+    assert np.all(dl <= 1e-5 * scale + 1e-30), f"max |dL|/scale {np.max(dl / (scale + 1e-300)):.3g}"
+
+
 def test_sweep_deterministic():
     wl = synth.make("c2", cout=100, cin=64, rows=300)
     note("sweep determinism")
