@@ -1136,7 +1136,7 @@ __device__ inline void sweep_full_column(FullLds& L, const void* __restrict__ W,
 
 // 4 waves per SIMD: the register budget is capped at 128 (the coupled form would otherwise take
 // more and drop to 3 waves, which costs about 10%).  rows_per_wave: 32, 64 when one round holds
-// them all, 128 for launches of more than 64 rounds.
+// them all, 256 for launches of more than 64 rounds.
 template <bool BF16, bool COUPLED, bool EQUALIZE, bool MSEARCH>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_sweep_full(
     const void* __restrict__ W, int64_t cout, int64_t cin, const float* __restrict__ amax,
@@ -2194,11 +2194,12 @@ hipError_t launch_sweep(const void* W, bool bf16, int64_t n_groups, int64_t cout
   // a launch of at most four rounds of resident waves (4096 at a time) ends in a tail that the
   // progress-based priority shortens; longer launches keep the arbiter's own order, which mixes
   // phases better.  A launch of at most two rounds takes 64 rows per wave and runs as one; one of
-  // more than 64 rounds takes 128 rows per wave, so each wave's column set-up (the Hessian's
-  // eigenvalue bound above all) serves more rows (512-expert gate_up: 51.6 -> 46.2 ms).
+  // more than 64 rounds takes 256 rows per wave, so each wave's column set-up serves more rows
+  // (512-expert gate_up: 32 -> 128 rows 51.6 -> 46.2 ms when the set-up held the eigenvalue bound,
+  // 128 -> 256 rows 38.17 -> 37.70 ms; 320 and 640 rows measured the same as 256).
   const int64_t waves32 = (nb + kWaves - 1) / kWaves * kWaves * ((cout + kRowsPerWave - 1) / kRowsPerWave) * n_groups;
   const bool equalize = waves32 <= 16384;
-  const int rpw = waves32 > 262144 ? 4 * kRowsPerWave
+  const int rpw = waves32 > 262144 ? 8 * kRowsPerWave
                                    : ((waves32 <= 8192 && cout > kRowsPerWave) ? 2 * kRowsPerWave : kRowsPerWave);
   dim3 grid((unsigned)((nb + kWaves - 1) / kWaves), (unsigned)((cout + rpw - 1) / rpw), (unsigned)n_groups);
   dim3 block(kWaves * 64);
